@@ -1,0 +1,233 @@
+"""Python binding of libuw (include/uw.h): argument marshalling only.
+
+Every step of the method runs in libuw.so (host encoder in C++, everything else in HIP
+kernels for gfx950). PyTorch tensors supply device memory and streams; a "d_" argument
+may be a torch tensor on the GPU or a raw device address (int). Host arrays are NumPy.
+
+Importing this package loads libuw.so and raises ImportError if it has not been built
+(`python -m decode_gemm_amd.build`); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "UwError", "Header", "Plan", "lib", "encode", "inspect", "validate_header", "decode_full",
+    "decode_exponent", "transcode_palette", "recon_gemm", "run_pipeline", "autotune", "swiglu",
+    "workspace_bytes", "variant_count", "variant_name", "variant_supports", "version",
+    "W_BF16", "W_EXP", "W_IDX", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT",
+    "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuw.so")
+
+STATUS = {0: "UW_OK", 1: "UW_EINVAL", 2: "UW_ESHAPE", 3: "UW_EFORMAT", 4: "UW_ERANGE", 5: "UW_ENOSPACE",
+          6: "UW_EHIP", 7: "UW_EUNSUPPORTED", 8: "UW_EINTERNAL"}
+OK, EINVAL, ESHAPE, EFORMAT, ERANGE, ENOSPACE, EHIP, EUNSUPPORTED, EINTERNAL = range(9)
+W_BF16, W_EXP, W_IDX = 0, 1, 2
+PIPE_FULL, PIPE_EXP, PIPE_TRANSCODE, PIPE_DIRECT = 0, 1, 2, 3
+PIPELINE_NAMES = {0: "full", 1: "exp", 2: "transcode", 3: "direct"}
+DERR_BADCODE, DERR_CHUNKLEN = 1, 2
+
+
+class UwError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Header(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("chunk", ctypes.c_uint32), ("lmax", ctypes.c_uint32), ("n_pal", ctypes.c_uint32),
+        ("n_chunks", ctypes.c_uint32), ("palette", ctypes.c_uint8 * 16), ("code_len", ctypes.c_uint8 * 16),
+        ("n_raw", ctypes.c_int64), ("total_bits", ctypes.c_uint64), ("off_sm", ctypes.c_uint64),
+        ("off_bitmap", ctypes.c_uint64), ("off_rowbase", ctypes.c_uint64), ("off_raw", ctypes.c_uint64),
+        ("off_chunk", ctypes.c_uint64), ("off_stream", ctypes.c_uint64), ("bytes_stream", ctypes.c_uint64),
+        ("total_bytes", ctypes.c_uint64), ("bitmap_words", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 25),
+    ]
+
+
+class EncodeOpts(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_uint32), ("lmax", ctypes.c_uint32)]
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("d_x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("h", ctypes.POINTER(Header)),
+        ("d_blob", ctypes.c_void_p), ("src", ctypes.c_int32), ("d_wplane", ctypes.c_void_p),
+        ("d_y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("variant", ctypes.c_int32),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32), ("t_ms", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Plan(pipeline={PIPELINE_NAMES.get(self.pipeline, self.pipeline)}, variant={self.variant}, t_ms={self.t_ms:.4f})"
+
+
+class TuneArgs(ctypes.Structure):
+    _fields_ = [
+        ("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_idx", ctypes.c_void_p),
+        ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p), ("d_ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("reps", ctypes.c_int32), ("warmup", ctypes.c_int32), ("pipeline_mask", ctypes.c_uint32),
+        ("variant_mask", ctypes.c_int32), ("d_scrub", ctypes.c_void_p), ("scrub_bytes", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libuw.so not built at {LIB_PATH}; run `python -m decode_gemm_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    H = ctypes.POINTER(Header)
+    sigs = {
+        "uw_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "uw_last_error": ([], ctypes.c_char_p),
+        "uw_version": ([], ctypes.c_int),
+        "uw_encode": ([P, i64, i64, ctypes.POINTER(EncodeOpts), P, ctypes.POINTER(sz)], ctypes.c_int),
+        "uw_inspect": ([P, sz, H], ctypes.c_int),
+        "uw_validate_header": ([H, sz], ctypes.c_int),
+        "uw_decode_full": ([H, P, P, P, P], ctypes.c_int),
+        "uw_decode_exponent": ([H, P, P, P, P], ctypes.c_int),
+        "uw_transcode_palette": ([H, P, P, P, P], ctypes.c_int),
+        "uw_recon_gemm": ([ctypes.POINTER(GemmArgs), P], ctypes.c_int),
+        "uw_variant_count": ([], ctypes.c_int),
+        "uw_variant_name": ([ctypes.c_int], ctypes.c_char_p),
+        "uw_variant_supports": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
+        "uw_workspace_bytes": ([H, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "uw_run_pipeline": ([i32, i32, H, P, P, i64, P, i64, P, i64, P, sz, P, P], ctypes.c_int),
+        "uw_autotune": ([ctypes.POINTER(TuneArgs), ctypes.POINTER(i64), ctypes.c_int, P, ctypes.POINTER(Plan)],
+                        ctypes.c_int),
+        "uw_swiglu": ([P, P, i64, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != OK:
+        raise UwError(status, lib.uw_last_error().decode())
+
+
+def _ptr(t):
+    """Device address of a torch tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def version() -> int:
+    return lib.uw_version()
+
+
+# ---------------------------------------------------------------- host
+def encode(w: np.ndarray, chunk: int = 0, lmax: int = 0) -> np.ndarray:
+    """uw_encode: W [N][K] bf16 bit patterns (uint16, host) -> blob (uint8, host)."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N][K]")
+    N, K = w.shape
+    opts = EncodeOpts(chunk, lmax)
+    need = ctypes.c_size_t(0)
+    st = lib.uw_encode(w.ctypes.data, N, K, ctypes.byref(opts), None, ctypes.byref(need))
+    if st != ENOSPACE:
+        _check(st)
+    blob = np.empty(need.value, np.uint8)
+    _check(lib.uw_encode(w.ctypes.data, N, K, ctypes.byref(opts), blob.ctypes.data, ctypes.byref(need)))
+    return blob
+
+
+def inspect(blob: np.ndarray) -> Header:
+    """uw_inspect: validate a host blob and return its header."""
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    h = Header()
+    _check(lib.uw_inspect(b.ctypes.data, b.size, ctypes.byref(h)))
+    return h
+
+
+def validate_header(h: Header, blob_bytes: int) -> None:
+    _check(lib.uw_validate_header(ctypes.byref(h), blob_bytes))
+
+
+def workspace_bytes(h: Header, pipeline: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.uw_workspace_bytes(ctypes.byref(h), pipeline, ctypes.byref(out)))
+    return out.value
+
+
+def variant_count() -> int:
+    return lib.uw_variant_count()
+
+
+def variant_name(v: int) -> str:
+    return lib.uw_variant_name(v).decode()
+
+
+def variant_supports(v: int, N: int, K: int, M: int, src: int) -> bool:
+    return bool(lib.uw_variant_supports(v, N, K, M, src))
+
+
+# ---------------------------------------------------------------- device
+def decode_full(h: Header, d_blob, d_w, d_err=None, stream=None) -> None:
+    _check(lib.uw_decode_full(ctypes.byref(h), _ptr(d_blob), _ptr(d_w), _ptr(d_err), _stream(stream)))
+
+
+def decode_exponent(h: Header, d_blob, d_exp, d_err=None, stream=None) -> None:
+    _check(lib.uw_decode_exponent(ctypes.byref(h), _ptr(d_blob), _ptr(d_exp), _ptr(d_err), _stream(stream)))
+
+
+def transcode_palette(h: Header, d_blob, d_idx, d_err=None, stream=None) -> None:
+    _check(lib.uw_transcode_palette(ctypes.byref(h), _ptr(d_blob), _ptr(d_idx), _ptr(d_err), _stream(stream)))
+
+
+def recon_gemm(h: Header, d_blob, src: int, d_wplane, d_x, d_y, M: int, ldx: int | None = None,
+               ldy: int | None = None, variant: int = -1, stream=None) -> None:
+    a = GemmArgs(M, _ptr(d_x), h.K if ldx is None else ldx, ctypes.pointer(h), _ptr(d_blob), src, _ptr(d_wplane),
+                 _ptr(d_y), h.N if ldy is None else ldy, variant)
+    _check(lib.uw_recon_gemm(ctypes.byref(a), _stream(stream)))
+
+
+def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_idx=None, d_ws=None, ws_bytes: int = 0,
+                 variant: int = -1, d_err=None, ldx: int | None = None, ldy: int | None = None, stream=None) -> None:
+    _check(lib.uw_run_pipeline(pipeline, variant, ctypes.byref(h), _ptr(d_blob), _ptr(d_idx), M, _ptr(d_x),
+                               h.K if ldx is None else ldx, _ptr(d_y), h.N if ldy is None else ldy, _ptr(d_ws),
+                               ws_bytes, _ptr(d_err), _stream(stream)))
+
+
+def autotune(h: Header, d_blob, d_x, d_y, Ms, d_idx=None, d_ws=None, ws_bytes: int = 0, reps: int = 0,
+             warmup: int = 0, pipeline_mask: int = 0, variant_mask: int = 0, d_scrub=None, scrub_bytes: int = 0,
+             stream=None) -> list:
+    a = TuneArgs(ctypes.pointer(h), _ptr(d_blob), _ptr(d_idx), _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes, reps,
+                 warmup, pipeline_mask, variant_mask, _ptr(d_scrub), scrub_bytes)
+    ms = (ctypes.c_int64 * len(Ms))(*Ms)
+    out = (Plan * len(Ms))()
+    _check(lib.uw_autotune(ctypes.byref(a), ms, len(Ms), _stream(stream), out))
+    return list(out)
+
+
+def swiglu(d_g, d_u, d_h, n: int, stream=None) -> None:
+    _check(lib.uw_swiglu(_ptr(d_g), _ptr(d_u), n, _ptr(d_h), _stream(stream)))

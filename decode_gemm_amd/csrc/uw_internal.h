@@ -1,0 +1,50 @@
+// Internal declarations shared by the translation units of libuw.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "uw.h"
+
+namespace uw {
+
+// Thread-local error text behind uw_last_error().
+void clear_error();
+uw_status fail(uw_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Canonical-code tables derived from a header's code lengths: for every length l,
+// count[l] codes starting at first_code[l]; their symbols are sorted[first_index[l] ..].
+struct CanonTables {
+    uint32_t first_code[16];
+    uint32_t count[16];
+    uint32_t first_index[16];
+    uint8_t sorted[16];
+    uint32_t n_used;
+};
+void canon_tables(const uw_header* h, CanonTables* t);
+
+// Header-level checks shared by uw_inspect / uw_validate_header.
+uw_status check_header(const uw_header* h, size_t blob_bytes);
+
+// Expected section layout for given sizes (the same formula the encoder writes).
+struct Layout {
+    uint64_t off_sm, off_bitmap, off_rowbase, off_raw, off_chunk, off_stream, bytes_stream, total;
+};
+Layout layout_for(int64_t N, int64_t K, int64_t n_raw, int64_t n_chunks, uint64_t total_bits);
+
+constexpr uint32_t kMagic = 0x31545755u;  // "UWT1"
+constexpr uint32_t kDefaultChunk = 256;
+constexpr uint32_t kDefaultLmax = 12;
+constexpr uint64_t kSectionAlign = 256;
+constexpr uint64_t kStreamSlack = 64;
+
+// Device-side launchers (uw_decode.hip, uw_gemm.hip).
+enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2 };
+uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err,
+                        void* stream);
+uw_status launch_gemm(const uw_gemm_args* a, void* stream);
+int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
+
+bool aligned(const void* p, size_t a);
+
+}  // namespace uw

@@ -1,0 +1,211 @@
+// Pipeline execution, the measured autotuner and the SwiGLU glue.
+//
+// Pipelines ("Four ways to use compressed weights" in the Unweight blog post): full
+// decode + plain GEMM, exponent-only decode + reconstructive GEMM, runtime palette
+// transcode + reconstructive GEMM, and direct palette (index plane prepared once at
+// load). No pipeline wins everywhere ("Why no single pipeline wins"), so the choice per
+// matrix and batch size is made by timing every candidate on the target GPU and keeping
+// the fastest, which is what the post's autotuner does instead of heuristics.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "uw_internal.h"
+
+namespace uw {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__global__ void fill_kernel(u32x4* p, size_t n16, uint32_t v)
+{
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = u32x4{v, v, v, v};
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN -> quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// h = bf16(silu(g) * u); eight elements per thread, 16-byte loads and stores.
+__global__ void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u, uint16_t* __restrict__ h,
+                              int64_t n)
+{
+    const int64_t i8 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+    if (i8 + 8 <= n) {
+        const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + i8), g1 = *reinterpret_cast<const floatx4*>(g + i8 + 4);
+        const floatx4 u0 = *reinterpret_cast<const floatx4*>(u + i8), u1 = *reinterpret_cast<const floatx4*>(u + i8 + 4);
+        uint32_t o[8];
+        for (int t = 0; t < 4; t++) {
+            o[t] = f32_to_bf16_rne(silu_mul(g0[t], u0[t]));
+            o[4 + t] = f32_to_bf16_rne(silu_mul(g1[t], u1[t]));
+        }
+        u32x4 v = {o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
+        *reinterpret_cast<u32x4*>(h + i8) = v;
+    } else {
+        for (int64_t i = i8; i < n; i++) h[i] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(g[i], u[i])));
+    }
+}
+
+uw_status scrub(void* d, size_t bytes, uint32_t value, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    if (!n16) return UW_OK;
+    hipLaunchKernelGGL(fill_kernel, dim3(2048), dim3(256), 0, s, static_cast<u32x4*>(d), n16, value);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? UW_OK : fail(UW_EHIP, "scrub launch failed: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+}  // namespace uw
+
+using namespace uw;
+
+extern "C" {
+
+uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob, const uint8_t* d_idx,
+                          int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y, int64_t ldy, void* d_ws,
+                          size_t ws_bytes, uint32_t* d_err, void* stream)
+{
+    clear_error();
+    if (!h) return fail(UW_EINVAL, "NULL header");
+    size_t need = 0;
+    uw_status st = uw_workspace_bytes(h, pipeline, &need);
+    if (st != UW_OK) return st;
+    if (need > 0 && (!d_ws || ws_bytes < need)) return fail(UW_ENOSPACE, "pipeline %d needs %zu workspace bytes", pipeline, need);
+    uw_gemm_args g;
+    std::memset(&g, 0, sizeof g);
+    g.M = M;
+    g.d_x = d_x;
+    g.ldx = ldx;
+    g.h = h;
+    g.d_blob = d_blob;
+    g.d_y = d_y;
+    g.ldy = ldy;
+    g.variant = variant;
+    switch (pipeline) {
+    case UW_PIPE_FULL:
+        if ((st = uw_decode_full(h, d_blob, static_cast<uint16_t*>(d_ws), d_err, stream)) != UW_OK) return st;
+        g.src = UW_W_BF16;
+        g.d_wplane = d_ws;
+        break;
+    case UW_PIPE_EXP:
+        if ((st = uw_decode_exponent(h, d_blob, static_cast<uint8_t*>(d_ws), d_err, stream)) != UW_OK) return st;
+        g.src = UW_W_EXP;
+        g.d_wplane = d_ws;
+        break;
+    case UW_PIPE_TRANSCODE:
+        if ((st = uw_transcode_palette(h, d_blob, static_cast<uint8_t*>(d_ws), d_err, stream)) != UW_OK) return st;
+        g.src = UW_W_IDX;
+        g.d_wplane = d_ws;
+        break;
+    case UW_PIPE_DIRECT:
+        if (!d_idx) return fail(UW_EINVAL, "direct palette needs the index plane");
+        g.src = UW_W_IDX;
+        g.d_wplane = d_idx;
+        break;
+    default: return fail(UW_EINVAL, "unknown pipeline %d", pipeline);
+    }
+    return uw_recon_gemm(&g, stream);
+}
+
+uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* stream, uw_plan* out)
+{
+    try {
+        clear_error();
+        if (!a || !a->h || !Ms || !out || nM < 0) return fail(UW_EINVAL, "NULL argument");
+        const uw_header* h = a->h;
+        const int reps = a->reps > 0 ? a->reps : 20;
+        const int warmup = a->warmup > 0 ? a->warmup : 3;
+        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0xFu;
+        const uint32_t vmask = a->variant_mask ? static_cast<uint32_t>(a->variant_mask) : 0xFFFFFFFFu;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipEvent_t e0, e1;
+        if (hipEventCreate(&e0) != hipSuccess) return fail(UW_EHIP, "hipEventCreate failed");
+        if (hipEventCreate(&e1) != hipSuccess) {
+            (void)hipEventDestroy(e0);
+            return fail(UW_EHIP, "hipEventCreate failed");
+        }
+        uw_status result = UW_OK;
+        for (int mi = 0; mi < nM && result == UW_OK; mi++) {
+            const int64_t M = Ms[mi];
+            uw_plan best;
+            best.pipeline = -1;
+            best.variant = -1;
+            best.t_ms = 3.0e38f;
+            best.reserved = 0;
+            for (int p = 0; p < 4 && result == UW_OK; p++) {
+                if (!(pmask >> p & 1u)) continue;
+                if (p == UW_PIPE_DIRECT && !a->d_idx) continue;
+                size_t need = 0;
+                uw_workspace_bytes(h, p, &need);
+                if (need > a->ws_bytes) continue;
+                const int32_t src = p == UW_PIPE_FULL ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP : UW_W_IDX;
+                for (int v = 0; v < uw_variant_count() && result == UW_OK; v++) {
+                    if (!(vmask >> v & 1u) || !uw_variant_supports(v, h->N, h->K, M, src)) continue;
+                    std::vector<float> t;
+                    for (int r = 0; r < warmup + reps; r++) {
+                        if (a->d_scrub && r >= warmup) {
+                            if ((result = scrub(a->d_scrub, a->scrub_bytes, static_cast<uint32_t>(r), s)) != UW_OK) break;
+                        }
+                        if (r >= warmup && hipEventRecord(e0, s) != hipSuccess) { result = fail(UW_EHIP, "event record failed"); break; }
+                        uw_status st = uw_run_pipeline(p, v, h, a->d_blob, a->d_idx, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
+                                                       a->ws_bytes, nullptr, stream);
+                        if (st != UW_OK) { result = st; break; }
+                        if (r >= warmup) {
+                            if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
+                                result = fail(UW_EHIP, "event synchronize failed");
+                                break;
+                            }
+                            float ms = 0.f;
+                            (void)hipEventElapsedTime(&ms, e0, e1);
+                            t.push_back(ms);
+                        }
+                    }
+                    if (result != UW_OK || t.empty()) break;
+                    std::sort(t.begin(), t.end());
+                    const float med = t[t.size() / 2];
+                    if (med < best.t_ms) {
+                        best.pipeline = p;
+                        best.variant = v;
+                        best.t_ms = med;
+                    }
+                }
+            }
+            if (result == UW_OK && best.pipeline < 0) result = fail(UW_EUNSUPPORTED, "no candidate fits M=%lld", (long long)M);
+            out[mi] = best;
+        }
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        return result;
+    } catch (...) {
+        return fail(UW_EINTERNAL, "unexpected exception in uw_autotune");
+    }
+}
+
+uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h, void* stream)
+{
+    clear_error();
+    if (n < 0) return fail(UW_ESHAPE, "n < 0");
+    if (n == 0) return UW_OK;
+    if (!d_g || !d_u || !d_h) return fail(UW_EINVAL, "NULL device pointer");
+    if (!aligned(d_g, 16) || !aligned(d_u, 16) || !aligned(d_h, 16)) return fail(UW_EINVAL, "pointers must be 16-byte aligned");
+    const int64_t threads = (n + 7) / 8;
+    const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
+    hipLaunchKernelGGL(swiglu_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), d_g, d_u, d_h, n);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? UW_OK : fail(UW_EHIP, "swiglu launch failed: %s", hipGetErrorString(e));
+}
+
+}  // extern "C"

@@ -1,0 +1,258 @@
+/*
+ * uw.h -- C ABI of libuw: lossless bf16 weight compression by exponent coding, with
+ * GPU decoders and a reconstructive GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one Cloudflare describes in "Unweight: how we compressed an LLM
+ * 22% without sacrificing quality":
+ *   - a bf16 weight is sign (1 bit), exponent (8 bits), mantissa (7 bits); sign and
+ *     mantissa are kept verbatim ("How weights compress");
+ *   - the exponent byte is replaced by an index into the 16 most common exponents of
+ *     the matrix and Huffman-coded; a 64-weight row holding any exponent outside
+ *     those 16 is stored as-is ("Exponents are predictable");
+ *   - four execution pipelines consume it: full decode + plain GEMM, exponent-only
+ *     decode, runtime palette transcode, and direct palette prepared at load ("Four
+ *     ways to use compressed weights");
+ *   - three of them use a reconstructive matmul that rebuilds bf16 tiles on chip and
+ *     feeds them to the matrix units, so the rebuilt weights never reach HBM ("How the
+ *     reconstructive matmul works");
+ *   - an autotuner picks the pipeline per matrix and batch size by measurement ("Why
+ *     no single pipeline wins").
+ *
+ * Conventions for every entry point:
+ *   - Weights W are [N][K] row-major bf16 bit patterns (PyTorch Linear layout: N = out
+ *     features, K = in features). K must be a multiple of 64. X is [M][K] bf16 row-major
+ *     with leading dimension ldx; Y = X * W^T is [M][N] fp32 with leading dimension ldy.
+ *   - "d_" pointers are device (HBM) pointers; all others are host pointers.
+ *   - The caller owns every buffer. The library never allocates or frees device memory
+ *     and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Device
+ *     calls are asynchronous on that stream; their return value reports argument
+ *     validation and launch errors only.
+ *   - No C++ exception crosses this boundary. On failure a status code is returned and
+ *     a thread-local message is available from uw_last_error().
+ *   - All functions are re-entrant. The only global state is a once-per-process flag per
+ *     kernel recording that its LDS-size attribute has been raised.
+ */
+#ifndef UW_H
+#define UW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UW_VERSION 1
+
+/* Status codes. */
+typedef enum {
+    UW_OK = 0,
+    UW_EINVAL = 1,       /* bad argument: NULL / misaligned pointer, bad option, bad ld */
+    UW_ESHAPE = 2,       /* bad shape: N < 1, K < 1, K % 64 != 0, M < 0 */
+    UW_EFORMAT = 3,      /* blob fails validation (magic, version, sizes, offsets) */
+    UW_ERANGE = 4,       /* value out of the format's range (stream bits >= 2^32, ...) */
+    UW_ENOSPACE = 5,     /* output / workspace buffer too small; required size returned */
+    UW_EHIP = 6,         /* a HIP runtime call or kernel launch failed */
+    UW_EUNSUPPORTED = 7, /* combination not supported by this build */
+    UW_EINTERNAL = 8     /* unexpected internal failure */
+} uw_status;
+
+/* Static string naming a status code. Never NULL. */
+const char* uw_status_string(int status);
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* uw_last_error(void);
+/* UW_VERSION of the built library. */
+int uw_version(void);
+
+/*
+ * Blob header: the first 256 bytes of every blob, byte for byte (little-endian).
+ * Blob layout (format version 1): header, then these sections, each starting at a
+ * multiple of 256 bytes:
+ *   sm       [N*K]   u8   sign<<7 | mantissa of every weight, row-major
+ *   bitmap   [N*bitmap_words] u32  bit (j%32) of word (n*bitmap_words + j/32) set iff the
+ *                         64-weight group W[n][64j .. 64j+63] is raw
+ *   row_base [N+1]   u32  number of raw groups in rows before n
+ *   raw      [n_raw][64] u8  verbatim exponent bytes of every raw group, (n, j) order
+ *   chunk    [n_chunks+1] u32  chunk c covers flattened elements [c*chunk, (c+1)*chunk);
+ *                         entry c = stream bits of all symbols before chunk c
+ *   stream   [bytes_stream] u8  canonical Huffman codes of the palette index of every
+ *                         element of a non-raw group, row-major order, MSB first; stream
+ *                         bit b is bit 31-(b%32) of little-endian u32 word b/32; zero
+ *                         padded, with at least 64 bytes of zero slack after the last bit
+ * Palette: the min(16, #distinct) most frequent exponent bytes of the matrix, by count
+ * descending then value ascending; palette index = rank. code_len[i] = code length of
+ * index i (0 = index unused in the stream). Codes are canonical (RFC 1951 3.2.2 rule).
+ */
+typedef struct uw_header {
+    uint32_t magic;   /* 0x31545755, the bytes "UWT1" */
+    uint32_t version; /* 1 */
+    int64_t N, K;
+    uint32_t chunk;    /* elements per chunk, a multiple of 64 */
+    uint32_t lmax;     /* longest allowed code, 1..15 */
+    uint32_t n_pal;    /* palette entries, 0..16 */
+    uint32_t n_chunks; /* ceil(N*K / chunk) */
+    uint8_t palette[16];
+    uint8_t code_len[16];
+    int64_t n_raw;       /* raw 64-weight groups */
+    uint64_t total_bits; /* stream bits, < 2^32 */
+    uint64_t off_sm, off_bitmap, off_rowbase, off_raw, off_chunk, off_stream;
+    uint64_t bytes_stream; /* stream section bytes including padding and slack */
+    uint64_t total_bytes;  /* whole blob */
+    uint32_t bitmap_words; /* ceil(K / 2048) */
+    uint32_t reserved[25]; /* zero */
+} uw_header;
+
+typedef struct {
+    uint32_t chunk; /* elements per chunk, multiple of 64; 0 = default (256) */
+    uint32_t lmax;  /* 1..15; 0 = default (12) */
+} uw_encode_opts;
+
+/*
+ * uw_encode (host). Compress W (host, [N][K] bf16 bits) into a self-describing blob
+ * ("How weights compress", "Exponents are predictable"). Two-call size query: if blob
+ * is NULL or *blob_bytes is smaller than required, returns UW_ENOSPACE and sets
+ * *blob_bytes to the required size; on success *blob_bytes = bytes written. opts may be
+ * NULL (defaults). Errors: UW_ESHAPE (N < 1, K < 1, K % 64), UW_EINVAL (NULL w or
+ * blob_bytes, chunk not a multiple of 64, lmax outside 1..15 or too small for the number
+ * of used palette indices), UW_ERANGE (stream would need >= 2^32 bits, or more than 2^32
+ * raw groups).
+ */
+uw_status uw_encode(const uint16_t* w_bf16, int64_t N, int64_t K, const uw_encode_opts* opts, void* blob,
+                    size_t* blob_bytes);
+
+/* uw_inspect (host). Validate a blob held in host memory (header fields, section
+ * offsets and sizes, chunk offsets monotone and ending at total_bits, row_base
+ * consistent with the bitmap) and copy its header to *out. UW_EFORMAT on any
+ * inconsistency, UW_EINVAL on NULL arguments. */
+uw_status uw_inspect(const void* blob, size_t blob_bytes, uw_header* out);
+
+/* uw_validate_header (host). The header-only subset of uw_inspect, for a blob already
+ * on the device: checks the header's own fields, its section offsets and
+ * total_bytes <= blob_bytes. */
+uw_status uw_validate_header(const uw_header* h, size_t blob_bytes);
+
+/*
+ * Device decoders ("Four ways to use compressed weights"; the Huffman decoder and
+ * palette transcoder of "Sharing the GPU between decode and compute").
+ *   h       host copy of the blob's header (from uw_inspect / uw_validate_header)
+ *   d_blob  the blob, copied verbatim to device memory, 256-byte aligned
+ *   d_err   optional device u32: kernels OR in UW_DERR_* bits on corrupt input; the
+ *           caller clears it. NULL = no reporting (output is then undefined on corrupt
+ *           input, but every access stays inside the blob).
+ * Outputs (device, 16-byte aligned, caller-owned):
+ *   uw_decode_full:       d_w   [N][K] bf16 bits (2 bytes / weight), bit-exact W
+ *   uw_decode_exponent:   d_exp [N][K] u8 exponent bytes, raw groups included (1 B/w)
+ *   uw_transcode_palette: d_idx [N*K/2] u8, element i in the low nibble of byte i/2 when
+ *                         i is even, the high nibble when odd; raw groups hold 0 (0.5 B/w)
+ */
+#define UW_DERR_BADCODE 1u    /* a bit pattern that is no code of the table */
+#define UW_DERR_CHUNKLEN 2u   /* a chunk's symbols did not end at the next chunk offset */
+uw_status uw_decode_full(const uw_header* h, const void* d_blob, uint16_t* d_w, uint32_t* d_err, void* stream);
+uw_status uw_decode_exponent(const uw_header* h, const void* d_blob, uint8_t* d_exp, uint32_t* d_err, void* stream);
+uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* d_idx, uint32_t* d_err,
+                               void* stream);
+
+/*
+ * uw_recon_gemm (device). Y = X * W^T with W taken from one of three planes ("How the
+ * reconstructive matmul works"): the bf16 weights themselves (plain GEMM of the
+ * full-decode pipeline), the exponent plane plus the blob's sign/mantissa plane, or the
+ * 4-bit palette-index plane plus the sign/mantissa plane, the palette and the raw
+ * groups. Weights are rebuilt in registers / LDS and fed to bf16 MFMA; they are never
+ * written to memory. Accumulation is fp32; Y is overwritten (not accumulated into).
+ */
+typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2 } uw_wsrc;
+
+typedef struct {
+    int64_t M;             /* rows of X and Y; 0 is a no-op */
+    const uint16_t* d_x;   /* X bf16 [M][ldx], 16-byte aligned */
+    int64_t ldx;           /* >= K, multiple of 8 */
+    const uw_header* h;    /* N, K, palette */
+    const void* d_blob;    /* device blob (sm plane, raw tables); unused for UW_W_BF16 */
+    int32_t src;           /* uw_wsrc */
+    const void* d_wplane;  /* bf16 W [N][K] | exponent plane [N][K] | index plane [N*K/2] */
+    float* d_y;            /* Y fp32 [M][ldy], 16-byte aligned */
+    int64_t ldy;           /* >= N */
+    int32_t variant;       /* kernel variant id, -1 = default for (N, K, M) */
+} uw_gemm_args;
+
+uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream);
+
+/* Kernel variants of uw_recon_gemm (tile shape per CU and pipelining depth, "How the
+ * reconstructive matmul works": wider tiles for large batches, deeper buffers for small
+ * ones). uw_variant_count() variants exist; uw_variant_name() describes one;
+ * uw_variant_supports() says whether a variant accepts (N, K, M, src). */
+int uw_variant_count(void);
+const char* uw_variant_name(int variant);
+int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
+
+/*
+ * Pipelines ("Four ways to use compressed weights"):
+ *   UW_PIPE_FULL      uw_decode_full into workspace, then plain bf16 GEMM
+ *   UW_PIPE_EXP       uw_decode_exponent into workspace, then reconstructive GEMM
+ *   UW_PIPE_TRANSCODE uw_transcode_palette into workspace, then reconstructive GEMM
+ *   UW_PIPE_DIRECT    reconstructive GEMM on an index plane prepared once at load
+ */
+typedef enum { UW_PIPE_FULL = 0, UW_PIPE_EXP = 1, UW_PIPE_TRANSCODE = 2, UW_PIPE_DIRECT = 3 } uw_pipeline;
+
+/* A per-(matrix, M) execution plan: which pipeline and which GEMM variant ("Why no
+ * single pipeline wins": the per-model profile). t_ms = measured median time. */
+typedef struct {
+    int32_t pipeline;
+    int32_t variant;
+    float t_ms;
+    int32_t reserved;
+} uw_plan;
+
+/* Workspace bytes a pipeline needs for a matrix (the preprocessing slot: 2, 1, 0.5 or 0
+ * bytes per weight for full / exp / transcode / direct). */
+uw_status uw_workspace_bytes(const uw_header* h, int32_t pipeline, size_t* out);
+
+/* Run one pipeline end to end on `stream`: decode into d_ws if the pipeline needs it,
+ * then the GEMM. d_idx = the persistent palette-index plane (UW_PIPE_DIRECT only). */
+uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob,
+                          const uint8_t* d_idx, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
+                          int64_t ldy, void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream);
+
+/*
+ * uw_autotune (device, synchronous). For each M in Ms, time every supported (pipeline,
+ * variant) pair on the caller's buffers with HIP events (warmup untimed launches, then
+ * the median of reps timed ones) and return the fastest in out[i] ("Why no single
+ * pipeline wins", "Sharing the GPU between decode and compute": measured, not
+ * heuristic). d_idx may be NULL, in which case UW_PIPE_DIRECT is not a candidate.
+ * d_x must hold max(Ms) rows of K bf16, d_y max(Ms) rows of N fp32, and d_ws at least
+ * the largest uw_workspace_bytes of the candidate pipelines (smaller workspaces drop
+ * the pipelines that do not fit). Blocks until the measurements finish.
+ */
+typedef struct {
+    const uw_header* h;
+    const void* d_blob;
+    const uint8_t* d_idx; /* persistent palette-index plane or NULL */
+    const uint16_t* d_x;  /* [max M][K] bf16 */
+    float* d_y;           /* [max M][N] fp32 */
+    void* d_ws;
+    size_t ws_bytes;
+    int32_t reps;   /* timed launches per candidate, >= 1 (0 = 20) */
+    int32_t warmup; /* untimed launches per candidate (0 = 3) */
+    uint32_t pipeline_mask; /* bit p set = pipeline p is a candidate (0 = all) */
+    int32_t variant_mask;   /* bit v set = GEMM variant v is a candidate (0 = all) */
+    void* d_scrub;          /* optional device buffer overwritten before every timed
+                               launch (outside the timed region) so that candidates are
+                               timed with cold caches; NULL = no scrubbing */
+    size_t scrub_bytes;     /* multiple of 16 */
+} uw_tune_args;
+
+uw_status uw_autotune(const uw_tune_args* args, const int64_t* Ms, int nM, void* stream, uw_plan* out);
+
+/*
+ * uw_swiglu (device). The activation between the MLP projections of a SwiGLU layer:
+ * h[i] = bf16(silu(g[i]) * u[i]), silu(z) = z / (1 + e^-z), fp32 math, rounded to
+ * nearest-even bf16. g, u fp32 [n], h bf16 [n], all 16-byte aligned.
+ */
+uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UW_H */

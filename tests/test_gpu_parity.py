@@ -1,0 +1,364 @@
+"""GPU parity: every kernel of libuw against the CPU oracle, through the C ABI.
+
+Decoded planes must be bit-exact (the method is lossless); GEMM outputs must lie
+within 1e-3 * sum_k |x_k w_k| of the fp64 oracle elementwise. Small cases span several
+tiles and ragged tails; the full-size workloads (gate 14336x4096, down 4096x14336,
+70B-shaped 28672x8192 / 8192x28672) compare decoded planes in full and a seeded sample
+of GEMM outputs, in the launch configurations the bench uses.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import check_gemm, dev, empty_f32, empty_u8, empty_u16, host, log, torch_cuda, zeros_u32
+
+pytestmark = pytest.mark.gpu
+
+uw = None
+
+
+def setup_module():
+    global uw
+    torch_cuda()
+    import decode_gemm_amd
+
+    uw = decode_gemm_amd
+    oracle.build(force=False)
+
+
+def _sync():
+    torch_cuda().cuda.synchronize()
+
+
+class Mat:
+    """A weight matrix uploaded with its library blob, plus oracle reference planes."""
+
+    def __init__(self, w, chunk=0, lmax=0, blob=None):
+        self.w = np.ascontiguousarray(w, dtype=np.uint16)
+        self.N, self.K = self.w.shape
+        self.blob = uw.encode(self.w, chunk=chunk, lmax=lmax) if blob is None else blob
+        self.h = uw.inspect(self.blob)
+        self.d_blob = dev(self.blob)
+        self._ref = None
+
+    def ref(self):
+        if self._ref is None:
+            self._ref = oracle.decode(self.blob, want=("exp", "idx"))
+        return self._ref
+
+    def decode(self, mode):
+        n = self.N * self.K
+        err = zeros_u32()
+        if mode == "full":
+            out = empty_u16(n)
+            uw.decode_full(self.h, self.d_blob, out, err)
+        elif mode == "exp":
+            out = empty_u8(n)
+            uw.decode_exponent(self.h, self.d_blob, out, err)
+        else:
+            out = empty_u8(n // 2)
+            uw.transcode_palette(self.h, self.d_blob, out, err)
+        _sync()
+        return out, int(host(err)[0])
+
+
+def _check_decoders(m: Mat, what: str):
+    log(f"  decode {what} N={m.N} K={m.K} chunk={m.h.chunk} lmax={m.h.lmax} raw={m.h.n_raw}")
+    out, err = m.decode("full")
+    assert err == 0, f"{what}: error flags {err}"
+    assert (host(out, np.uint16).reshape(m.N, m.K) == m.w).all(), f"{what}: full decode differs"
+    ref = m.ref()
+    out, err = m.decode("exp")
+    assert err == 0 and (host(out).reshape(m.N, m.K) == ref["exp"]).all(), f"{what}: exponent plane differs"
+    out, err = m.decode("idx")
+    assert err == 0 and (host(out) == ref["idx"]).all(), f"{what}: index plane differs"
+
+
+def test_decoders_tiny_library_and_oracle_blobs():
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    for chunk, lmax in ((64, 12), (256, 12), (1024, 12), (192, 7), (512, 14), (128, 4)):
+        _check_decoders(Mat(w, chunk, lmax), f"lib chunk={chunk} lmax={lmax}")
+        _check_decoders(Mat(w, blob=oracle.encode(w, chunk=chunk, lmax=lmax)), f"oracle chunk={chunk} lmax={lmax}")
+
+
+def test_decoders_edge_matrices():
+    rng = np.random.default_rng(31)
+    _check_decoders(Mat(np.full((3, 192), 0x3C01, np.uint16), 128), "single symbol")
+    e = rng.integers(100, 116, size=(5, 128)).astype(np.uint16)
+    e[:, 5] = 200 + np.arange(5)
+    e[:, 70] = 210 + np.arange(5)
+    w = ((e << 7) | rng.integers(0, 256, size=e.shape).astype(np.uint16) & 0x807F).astype(np.uint16)
+    m = Mat(w, 64)
+    assert m.h.total_bits == 0
+    _check_decoders(m, "all raw")
+    w = synth.f32_to_bf16_bits(rng.standard_normal((37, 320), dtype=np.float32) * 0.02)
+    w.reshape(-1)[rng.choice(w.size, 80, replace=False)] = np.array(
+        [0, 0x8000, 1, 0x807F, 0x7F80, 0xFF80, 0x7FC1, 0xFFFF], np.uint16)[np.arange(80) % 8]
+    _check_decoders(Mat(w, 1024), "specials, ragged last chunk")
+    _check_decoders(Mat(w, 64 * 7), "chunk 448")
+    e = rng.integers(110, 126, size=(6, 4096)).astype(np.uint16)
+    e[1, 64 * 33 + 3] = 230
+    e[3, 64 * 63] = 231
+    e[5, 64 * 31 + 63] = 232
+    w = ((e << 7) | rng.integers(0, 128, size=e.shape).astype(np.uint16)).astype(np.uint16)
+    _check_decoders(Mat(w, 256), "raw groups in the second bitmap word")
+    # one wave's worth of chunks and more: several workgroups, partial last wave
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    w2 = np.concatenate([w, w[:100]], axis=0)
+    _check_decoders(Mat(w2, 64), "612 rows, 2448 chunks")
+
+
+def test_decoder_reports_corruption():
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    m = Mat(w, 256)
+    bad = m.blob.copy()
+    oc = m.h.off_chunk + 4 * 5
+    v = int(np.frombuffer(bad[oc : oc + 4].tobytes(), "<u4")[0])
+    bad[oc : oc + 4] = np.frombuffer(np.uint32(v + 3).tobytes(), np.uint8)  # chunk 5 starts 3 bits late
+    mb = Mat(w, blob=bad)
+    _, err = mb.decode("idx")
+    assert err & uw.DERR_CHUNKLEN
+    # one used symbol has the code '0': a '1' bit in its stream is no code
+    ws = np.full((2, 128), 0x3C01, np.uint16)
+    ms = Mat(ws, 128)
+    bad = ms.blob.copy()
+    bad[ms.h.off_stream + 3] |= 0x80  # bit 0 of the first word (MSB) set
+    _, err = Mat(ws, blob=bad).decode("exp")
+    assert err & uw.DERR_BADCODE
+
+
+# ---------------------------------------------------------------- GEMM
+def _planes(m: Mat):
+    """Device planes for each GEMM source, produced by the GPU decoders."""
+    full, _ = m.decode("full")
+    exp, _ = m.decode("exp")
+    idx, _ = m.decode("idx")
+    return {uw.W_BF16: full, uw.W_EXP: exp, uw.W_IDX: idx}
+
+
+def _run_gemm(m, planes, src, x, variant):
+    M = x.shape[0]
+    d_x = dev(x)
+    y = empty_f32(M, m.N)
+    y.fill_(float("nan"))
+    uw.recon_gemm(m.h, m.d_blob, src, planes[src], d_x, y, M, variant=variant)
+    _sync()
+    return host(y)
+
+
+def _variants_for(m, M, src):
+    return [v for v in range(uw.variant_count()) if uw.variant_supports(v, m.N, m.K, M, src)]
+
+
+def test_gemm_one_hot_rows_give_weights_exactly():
+    """X rows one-hot at k: Y[m][n] = W[n][k] exactly, through every loader and variant
+    (pins the rebuild of sign, exponent, mantissa and the raw overlay)."""
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    m = Mat(w, 256)
+    planes = _planes(m)
+    wf = synth.bf16_bits_to_f32(w)
+    ks = np.array([0, 1, 15, 16, 63, 64, 100, 127, 128, 200, 255] * 6)[:66]
+    for M in (1, 16, 66):
+        x = np.zeros((M, m.K), np.uint16)
+        for r in range(M):
+            x[r, ks[r % len(ks)]] = 0x3F80
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX):
+            for v in _variants_for(m, M, src):
+                log(f"  one-hot M={M} src={src} variant={v}")
+                y = _run_gemm(m, planes, src, x, v)
+                ref = np.stack([wf[:, ks[r % len(ks)]] for r in range(M)])
+                assert np.array_equal(y, ref), f"one-hot M={M} src={src} variant={v}"
+
+
+def test_gemm_small_integers_exact():
+    rng = np.random.default_rng(41)
+    N, K = 200, 320
+    wi = rng.integers(-8, 9, size=(N, K))
+    w = synth.f32_to_bf16_bits(wi.astype(np.float32))
+    m = Mat(w, 128)
+    planes = _planes(m)
+    for M in (3, 40, 130):
+        xi = rng.integers(-8, 9, size=(M, K))
+        x = synth.f32_to_bf16_bits(xi.astype(np.float32))
+        ref = (xi @ wi.T).astype(np.float32)
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX):
+            for v in _variants_for(m, M, src):
+                log(f"  integers M={M} src={src} variant={v}")
+                assert np.array_equal(_run_gemm(m, planes, src, x, v), ref), f"M={M} src={src} v={v}"
+
+
+@pytest.mark.parametrize("N,K", [(512, 256), (200, 192), (333, 4160)])
+def test_gemm_parity_ragged(N, K):
+    cfg = synth.Config("rag", 7, (("w", N, K),), 0.02, "normal", 0.001, 0.0, 12, (1,))
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w, 256)
+    assert m.h.n_raw > 0
+    planes = _planes(m)
+    for M in (1, 4, 16, 17, 33, 64, 65, 129, 300):
+        x = synth.gen_x(cfg, M, K)
+        y_ref, a_ref = oracle.gemm(x, w)
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX):
+            for v in _variants_for(m, M, src):
+                log(f"  ragged N={N} K={K} M={M} src={src} variant={v}")
+                check_gemm(_run_gemm(m, planes, src, x, v), y_ref, a_ref, f"N={N} K={K} M={M} src={src} v={v}")
+
+
+def test_pipelines_tiny():
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w)
+    idx, _ = m.decode("idx")
+    ws = empty_u8(uw.workspace_bytes(m.h, uw.PIPE_FULL))
+    for M in (4, 1, 64, 200):
+        x = synth.gen_x(cfg, M, m.K)
+        y_ref, a_ref = oracle.gemm(x, w)
+        for p in range(4):
+            log(f"  pipeline {p} M={M}")
+            y = empty_f32(M, m.N)
+            err = zeros_u32()
+            uw.run_pipeline(p, m.h, m.d_blob, dev(x), y, M, d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), d_err=err)
+            _sync()
+            assert int(host(err)[0]) == 0
+            check_gemm(host(y), y_ref, a_ref, f"pipeline {p} M={M}")
+
+
+def test_run_pipeline_error_paths():
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    m = Mat(w)
+    x = dev(synth.gen_x(synth.CONFIGS["tiny"], 4, m.K))
+    y = empty_f32(4, m.N)
+    with pytest.raises(uw.UwError) as e:
+        uw.run_pipeline(uw.PIPE_FULL, m.h, m.d_blob, x, y, 4, d_ws=empty_u8(16), ws_bytes=16)
+    assert e.value.status == uw.ENOSPACE
+    with pytest.raises(uw.UwError) as e:
+        uw.run_pipeline(uw.PIPE_DIRECT, m.h, m.d_blob, x, y, 4)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 4, ldx=m.K - 8)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 4, variant=99)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 100, variant=0)
+    assert e.value.status == uw.EUNSUPPORTED
+    uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 0)  # M = 0: no-op
+
+
+# ---------------------------------------------------------------- full sizes
+def _full_size_case(cfg, proj, Ms, n_samples=4096):
+    w = synth.gen_weight(cfg, proj)
+    log(f"  {cfg.name}/{proj}: encoding {w.shape}")
+    m = Mat(w)
+    _check_decoders(m, f"{cfg.name}/{proj}")
+    planes = _planes(m)
+    m._ref = None
+    rng = np.random.default_rng(12345)
+    for M in Ms:
+        x = synth.gen_x(cfg, M, m.K)
+        mi = rng.integers(0, M, n_samples)
+        ni = rng.integers(0, m.N, n_samples)
+        y_ref, a_ref = oracle.gemm_pairs(x, w, mi, ni)
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX):
+            v = -1  # the default variant, as launched by the pipelines and the bench
+            log(f"  {cfg.name}/{proj} M={M} src={src}")
+            y = _run_gemm(m, planes, src, x, v)
+            check_gemm(y[mi, ni], y_ref, a_ref, f"{cfg.name}/{proj} M={M} src={src}")
+            assert np.isfinite(y).all()
+
+
+def test_full_size_gate():
+    _full_size_case(synth.CONFIGS["gate"], "gate", (1, 16, 64))
+
+
+def test_full_size_down():
+    _full_size_case(synth.CONFIGS["down"], "down", (256, 1024, 4096))
+
+
+def test_full_size_70b():
+    cfg = synth.CONFIGS["70b"]
+    _full_size_case(cfg, "gate", (1, 64, 512, 2048))
+    _full_size_case(cfg, "down", (1, 64, 512, 2048), n_samples=2048)
+
+
+# ---------------------------------------------------------------- glue, autotune
+def test_swiglu_against_oracle():
+    torch = torch_cuda()
+    rng = np.random.default_rng(51)
+    for n in (8, 13, 4096 * 3 + 5):
+        g = (rng.standard_normal(n) * 4).astype(np.float32)
+        u = (rng.standard_normal(n) * 4).astype(np.float32)
+        g[:3] = [0.0, -0.0, 30.0]
+        h = torch.empty(n + 8, dtype=torch.int16, device="cuda")
+        uw.swiglu(dev(g), dev(u), h, n)
+        _sync()
+        got = host(h, np.uint16)[:n].astype(np.int32)
+        ref = oracle.swiglu(g, u).astype(np.int32)
+        # within one bf16 ulp of the correctly rounded fp64 value (same sign)
+        assert (np.abs(got - ref) <= 1).all()
+
+
+def test_autotune_picks_the_fastest_and_the_choice_is_correct():
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w)
+    idx, _ = m.decode("idx")
+    Ms = [1, 64, 256]
+    x = synth.gen_x(cfg, max(Ms), m.K)
+    d_x = dev(x)
+    y = empty_f32(max(Ms), m.N)
+    ws = empty_u8(uw.workspace_bytes(m.h, uw.PIPE_FULL))
+    plans = uw.autotune(m.h, m.d_blob, d_x, y, Ms, d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), reps=15, warmup=3)
+    log(f"  plans {plans}")
+    for M, plan in zip(Ms, plans):
+        assert 0 <= plan.pipeline <= 3 and plan.t_ms > 0
+        per = []
+        for p in range(4):
+            per.append(uw.autotune(m.h, m.d_blob, d_x, y, [M], d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), reps=15,
+                                   warmup=3, pipeline_mask=1 << p)[0].t_ms)
+        assert plan.t_ms <= min(per) * 1.25 + 0.002, (M, plan, per)
+        # the chosen plan computes the right result
+        yy = empty_f32(M, m.N)
+        uw.run_pipeline(plan.pipeline, m.h, m.d_blob, dev(x[:M]), yy, M, d_idx=idx, d_ws=ws, ws_bytes=ws.numel(),
+                        variant=plan.variant)
+        _sync()
+        y_ref, a_ref = oracle.gemm(x[:M], w)
+        check_gemm(host(yy), y_ref, a_ref, f"autotuned M={M}")
+
+
+def test_stack_layers_teacher_forced():
+    """Two layers of the 8B-shaped SwiGLU MLP stack: gate and up from the same X, the
+    SwiGLU glue, then down on the glue output, each step checked against the oracle on
+    the GPU's own inputs (teacher forcing)."""
+    cfg = synth.CONFIGS["stack"]
+    sig = synth.gen_stack_sigmas(cfg)
+    M = 4
+    x = synth.gen_x(cfg, M, 4096)
+    rng = np.random.default_rng(61)
+    torch = torch_cuda()
+    for layer in range(2):
+        mats = {p: Mat(synth.gen_weight(cfg, p, layer, sigma=float(sig[layer]))) for p in ("gate", "up", "down")}
+        idx = {p: mats[p].decode("idx")[0] for p in mats}
+        ys = {}
+        for p in ("gate", "up"):
+            y = empty_f32(M, 14336)
+            uw.run_pipeline(uw.PIPE_DIRECT, mats[p].h, mats[p].d_blob, dev(x), y, M, d_idx=idx[p])
+            ys[p] = y
+        hbuf = torch.empty(M * 14336, dtype=torch.int16, device="cuda")
+        uw.swiglu(ys["gate"], ys["up"], hbuf, M * 14336)
+        yd = empty_f32(M, 4096)
+        uw.run_pipeline(uw.PIPE_DIRECT, mats["down"].h, mats["down"].d_blob, hbuf, yd, M, d_idx=idx["down"])
+        _sync()
+        mi = rng.integers(0, M, 1024)
+        for p in ("gate", "up"):
+            ni = rng.integers(0, 14336, 1024)
+            yr, ar = oracle.gemm_pairs(x, mats[p].w, mi, ni)
+            check_gemm(host(ys[p])[mi, ni], yr, ar, f"layer {layer} {p}")
+        g, u = host(ys["gate"]), host(ys["up"])
+        href = oracle.swiglu(g, u).reshape(M, 14336)
+        hg = host(hbuf, np.uint16).reshape(M, 14336)
+        assert (np.abs(hg.astype(np.int32) - href.astype(np.int32)) <= 1).all()
+        ni = rng.integers(0, 4096, 1024)
+        yr, ar = oracle.gemm_pairs(hg, mats["down"].w, mi, ni)
+        check_gemm(host(yd)[mi, ni], yr, ar, f"layer {layer} down")

@@ -1,0 +1,194 @@
+"""CPU tests of libuw's host side: exports, header layout, encoder vs the oracle,
+validation and error paths. No device call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_gemm_amd as uw
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def setup_module():
+    oracle.build(force=False)
+
+
+def test_library_exports_every_declared_symbol():
+    src = open(os.path.join(ROOT, "include", "uw.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(uw_[a-z_]+)\s*\(", src))
+    assert len(names) >= 17
+    lib = ctypes.CDLL(uw.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert uw.version() == 1
+
+
+def test_header_struct_is_256_bytes_and_matches_blob():
+    assert ctypes.sizeof(uw.Header) == 256
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    blob = uw.encode(w, chunk=512)
+    h = uw.inspect(blob)
+    assert bytes(h) == blob[:256].tobytes()
+    oh = oracle.header(blob)
+    for k in ("N", "K", "chunk", "lmax", "n_pal", "n_chunks", "n_raw", "total_bits", "off_sm", "off_stream", "total_bytes"):
+        assert getattr(h, k) == oh[k], k
+
+
+def _cross(w, chunk, lmax):
+    """Library blob -> oracle decoder; oracle blob -> library validation; equal costs."""
+    lb = uw.encode(w, chunk=chunk, lmax=lmax)
+    ob = oracle.encode(w, chunk=chunk, lmax=lmax)
+    lh, oh = uw.inspect(lb), uw.inspect(ob)
+    d = oracle.decode(lb)
+    assert (d["w"] == w).all()
+    # both code-length constructions are optimal: same stream length
+    assert lh.total_bits == oh.total_bits
+    assert list(lh.palette) == list(oh.palette) and lh.n_pal == oh.n_pal
+    assert lh.n_raw == oh.n_raw and lh.total_bytes == oh.total_bytes
+    # every section other than the Huffman lengths-dependent ones is identical
+    for a, b in (("off_sm", "off_chunk"),):
+        assert (lb[getattr(lh, a) : getattr(lh, b)] == ob[getattr(oh, a) : getattr(oh, b)]).all()
+    if list(lh.code_len) == list(oh.code_len):
+        assert (lb == ob).all()
+    return lb
+
+
+@pytest.mark.parametrize("chunk,lmax", [(64, 12), (256, 12), (1024, 12), (192, 7), (256, 15), (128, 4)])
+def test_encoder_matches_oracle_tiny(chunk, lmax):
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    _cross(w, chunk, lmax)
+
+
+def test_encoder_matches_oracle_edge_matrices():
+    rng = np.random.default_rng(21)
+    # all-equal: one symbol
+    _cross(np.full((3, 192), 0x3C01, np.uint16), 128, 12)
+    # all raw: 5 rare exponents per group
+    e = rng.integers(100, 116, size=(5, 128)).astype(np.uint16)
+    e[:, 5] = 200 + np.arange(5)
+    e[:, 70] = 210 + np.arange(5)
+    w = ((e << 7) | rng.integers(0, 128, size=e.shape).astype(np.uint16)).astype(np.uint16)
+    b = _cross(w, 64, 12)
+    assert uw.inspect(b).total_bits == 0
+    # special values and a ragged last chunk
+    w = synth.f32_to_bf16_bits(rng.standard_normal((9, 320), dtype=np.float32) * 0.02)
+    w.reshape(-1)[rng.choice(w.size, 50, replace=False)] = np.array([0, 0x8000, 1, 0x7F80, 0xFF80, 0x7FC1, 0xFFFF], np.uint16)[np.arange(50) % 7]
+    _cross(w, 1024, 12)
+    # K = 4096 (two bitmap words per row) with raw groups in the second word
+    e = rng.integers(110, 126, size=(4, 4096)).astype(np.uint16)
+    e[1, 64 * 33 + 3] = 230
+    e[3, 64 * 63] = 231
+    w = ((e << 7) | rng.integers(0, 128, size=e.shape).astype(np.uint16)).astype(np.uint16)
+    _cross(w, 256, 12)
+
+
+@pytest.mark.slow
+def test_encoder_matches_oracle_gate_shape():
+    w = synth.gen_weight(synth.CONFIGS["gate"], "gate")
+    lb = uw.encode(w)
+    ob = oracle.encode(w, chunk=256)
+    lh, oh = uw.inspect(lb), uw.inspect(ob)
+    assert lh.total_bits == oh.total_bits and lh.n_raw == oh.n_raw
+    assert (oracle.decode(lb, want=("w",))["w"] == w).all()
+    # compressed size in line with the exponent law: about 1.34 bytes per weight
+    assert 1.30 < lh.total_bytes / w.size < 1.37
+
+
+def test_encode_error_paths():
+    w = np.zeros((4, 128), np.uint16)
+    with pytest.raises(uw.UwError) as e:
+        uw.encode(np.zeros((4, 100), np.uint16))
+    assert e.value.status == uw.ESHAPE
+    with pytest.raises(uw.UwError) as e:
+        uw.encode(w, chunk=100)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.encode(w, lmax=16)
+    assert e.value.status == uw.EINVAL
+    # 16 used palette indices cannot be coded with lmax = 3
+    rng = np.random.default_rng(0)
+    w16 = ((rng.integers(100, 116, size=(2, 256)).astype(np.uint16)) << 7).astype(np.uint16)
+    with pytest.raises(uw.UwError) as e:
+        uw.encode(w16, lmax=3)
+    assert e.value.status == uw.EINVAL
+    need = ctypes.c_size_t(0)
+    st = uw.lib.uw_encode(None, 4, 128, None, None, ctypes.byref(need))
+    assert st == uw.EINVAL
+    st = uw.lib.uw_encode(w.ctypes.data, 4, 128, None, None, ctypes.byref(need))
+    assert st == uw.ENOSPACE and need.value > 256
+    small = np.zeros(16, np.uint8)
+    need2 = ctypes.c_size_t(16)
+    assert uw.lib.uw_encode(w.ctypes.data, 4, 128, None, small.ctypes.data, ctypes.byref(need2)) == uw.ENOSPACE
+    assert need2.value == need.value
+    assert uw.lib.uw_last_error().decode() != ""
+    assert uw.lib.uw_status_string(uw.EFORMAT).decode().startswith("UW_EFORMAT")
+    assert uw.lib.uw_status_string(99).decode() == "unknown uw_status"
+
+
+def _u32(blob, off, value):
+    b = blob.copy()
+    b[off : off + 4] = np.frombuffer(np.uint32(value).tobytes(), np.uint8)
+    return b
+
+
+def test_inspect_rejects_corrupt_blobs():
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    blob = uw.encode(w, chunk=256)
+    h = uw.inspect(blob)
+
+    def bad(b, status=uw.EFORMAT):
+        with pytest.raises(uw.UwError) as e:
+            uw.inspect(b)
+        assert e.value.status == status
+
+    bad(_u32(blob, 0, 0x12345678))                       # magic
+    bad(_u32(blob, 4, 2))                                # version
+    bad(blob[: h.total_bytes - 1])                        # truncated
+    bad(blob[:100])                                       # shorter than a header
+    bad(_u32(blob, 28, 16))                              # lmax out of range
+    b = blob.copy(); b[56] = 1; b[57] = 1; b[58] = 1; bad(b)  # Kraft inequality violated
+    b = blob.copy(); b[41] = b[40]; bad(b)                # duplicate palette entry
+    oc = h.off_chunk
+    bad(_u32(blob, oc + 4 * 3, int(np.frombuffer(blob[oc + 4 * 4 : oc + 4 * 5].tobytes(), "<u4")[0]) + 1))  # non-monotone
+    bad(_u32(blob, oc, 1))                                # first offset not 0
+    orb = h.off_rowbase
+    bad(_u32(blob, orb + 4 * 10, 10**6))                  # row_base inconsistent with the bitmap
+    b = blob.copy(); b[h.off_bitmap + 3] |= 0x80; bad(b)   # bitmap bit beyond the row's 4 groups
+    bad(_u32(blob, 88, h.off_sm + 16))                    # section offsets off the layout
+    with pytest.raises(uw.UwError) as e:
+        uw.lib_inspect_null = uw.lib.uw_inspect(None, 0, None)
+        uw._check(uw.lib_inspect_null)
+    assert e.value.status == uw.EINVAL
+
+
+def test_oracle_blobs_pass_library_validation():
+    for name in ("tiny",):
+        w = synth.gen_weight(synth.CONFIGS[name], "w")
+        for chunk in (64, 320, 1024):
+            uw.inspect(oracle.encode(w, chunk=chunk))
+
+
+def test_workspace_bytes_follow_the_pipelines():
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    h = uw.inspect(uw.encode(w))
+    n = w.size
+    # preprocessing output per weight: 2 (full), 1 (exponent-only), 0.5 (transcode), 0 (direct)
+    assert [uw.workspace_bytes(h, p) for p in range(4)] == [2 * n, n, n // 2, 0]
+    with pytest.raises(uw.UwError):
+        uw.workspace_bytes(h, 7)
+
+
+def test_variants_table():
+    n = uw.variant_count()
+    assert n >= 3
+    names = [uw.variant_name(v) for v in range(n)]
+    assert all(names) and uw.variant_name(n) == ""
+    assert any(uw.variant_supports(v, 4096, 4096, 1, uw.W_IDX) for v in range(n))
+    assert any(uw.variant_supports(v, 4096, 4096, 4096, uw.W_IDX) for v in range(n))
+    assert not uw.variant_supports(0, 4096, 100, 1, uw.W_IDX)
