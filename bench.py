@@ -1,0 +1,288 @@
+"""Benchmark: decode + GEMM throughput of the exponent-compressed gate projection on one
+MI355X, as uncompressed-equivalent weight GB/s (2 * N * K bytes per forward / time).
+
+Workload (the small-batch, decode-bound case): a Llama-3.1-8B gate_proj-shaped matrix,
+W 14336 x 4096 bf16 ~ N(0, 0.02) with 0.01% of entries pushed by 2^+-10, synthetic and
+seeded; X M x 4096 bf16 ~ N(0, 1). One step = one forward of the matrix for each batch
+size M in {1, 16, 64}, each through the pipeline the autotuner picked for that M
+(full decode + GEMM, exponent-only, palette transcode or direct palette), with the
+weights' compressed planes rotated over enough copies that the 256 MB Infinity Cache
+cannot serve them. Inputs are resident in HBM when the timed region starts.
+
+The JSON line also carries:
+  roofline      the dominant kernel's algorithmic HBM bytes per launch / its mean
+                duration (HIP events on its stream, inside the timed region) vs 8 TB/s
+  cpu_baseline  the CPU oracle (bit-serial decode + fp64 GEMM) timed on one host core
+                on one full step of the same workload
+  detail        per-M plans and the time of each of the four pipelines
+  large_m       TFLOP/s of the down_proj-shaped (4096 x 14336) GEMM at M = 4096
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=6, help="rotated copies of the compressed weights")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-detail", action="store_true", help="skip per-pipeline detail and the large-M line")
+    p.add_argument("--copy-probe", action="store_true", help="also launch a plain 256 MiB copy kernel (counter scale)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(h, M, pipeline):
+    """HBM bytes a pipeline must move per forward: its resident compressed input, X and Y,
+    plus the preprocessing plane it writes and reads back (none for direct palette)."""
+    N, K = h.N, h.K
+    side = 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw  # raw-group tables
+    xy = 2 * M * K + 4 * M * N
+    if pipeline == 3:  # direct palette: sm plane + index plane + raw tables
+        return N * K + N * K // 2 + side + xy
+    huff = N * K + side + 4 * (h.n_chunks + 1) + h.bytes_stream  # Huffman-format blob
+    plane = {0: 2 * N * K, 1: N * K, 2: N * K // 2}[pipeline]
+    gemm_in = {0: 2 * N * K, 1: 2 * N * K + side, 2: N * K + N * K // 2 + side}[pipeline]
+    return huff + plane + gemm_in + xy
+
+
+def gemm_bytes(h, M, src):
+    """HBM bytes of the GEMM kernel alone (its own inputs and output)."""
+    N, K = h.N, h.K
+    side = 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw
+    w = {0: 2 * N * K, 1: 2 * N * K, 2: N * K + N * K // 2 + side}[src]
+    return w + 2 * M * K + 4 * M * N
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in DESIGN.md but not run",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    import decode_gemm_amd as uw
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = synth.CONFIGS["gate"]
+    Ms = list(cfg.Ms)
+    t0 = time.time()
+    w = synth.gen_weight(cfg, "gate")
+    blob = uw.encode(w)
+    h = uw.inspect(blob)
+    N, K = h.N, h.K
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] gate {N}x{K}: blob {blob.size / 1e6:.1f} MB ({blob.size / (N * K):.3f} B/w), raw groups {h.n_raw}, "
+        f"prep {time.time() - t0:.1f}s")
+
+    # R copies of the blob and of its load-time palette-index plane (direct palette)
+    R = args.copies
+    d_blob = torch.from_numpy(blob).to(dev)
+    blobs, idxs = [], []
+    for r in range(R):
+        b = d_blob.clone()
+        i = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+        uw.transcode_palette(h, b, i)
+        blobs.append(b)
+        idxs.append(i)
+    del d_blob
+    xs = {M: torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev) for M in Ms}
+    ys = {M: torch.empty(M, N, dtype=torch.float32, device=dev) for M in Ms}
+    ws_bytes = uw.workspace_bytes(h, uw.PIPE_FULL)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    # autotune every M (cold-cache timing: the scrub buffer is overwritten before each rep)
+    plans = {}
+    for M in Ms:
+        plans[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_idx=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
+                               warmup=2, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
+    log("[bench] plans: " + ", ".join(f"M={M}: {plans[M]!r} ({uw.variant_name(plans[M].variant)})" for M in Ms))
+
+    seq = [0]
+
+    def step(events=None):
+        for M in Ms:
+            c = seq[0] % R
+            seq[0] += 1
+            p = plans[M]
+            if events is not None:
+                events[M][0].record(stream)
+            uw.run_pipeline(p.pipeline, h, blobs[c], xs[M], ys[M], M, d_idx=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
+                            variant=p.variant, stream=stream)
+            if events is not None:
+                events[M][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = {M: [] for M in Ms}
+    pairs = []
+    ev0.record(stream)
+    for _ in range(args.steps):
+        e = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+        step(e)
+        pairs.append(e)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    for e in pairs:
+        for M in Ms:
+            per[M].append(e[M][0].elapsed_time(e[M][1]))
+    ms_per_step = total_ms / args.steps
+    uncompressed = 2.0 * N * K * len(Ms)
+    value = uncompressed / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the pipeline launch with the largest share of the step; when the
+    # pipeline is direct palette this is exactly one GEMM kernel launch
+    mean_ms = {M: float(np.mean(per[M])) for M in Ms}
+    Mdom = max(Ms, key=lambda M: mean_ms[M])
+    pdom = plans[Mdom]
+    alg = algorithmic_bytes(h, Mdom, pdom.pipeline)
+    achieved = alg / (mean_ms[Mdom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"{uw.PIPELINE_NAMES[pdom.pipeline]} pipeline, {uw.variant_name(pdom.variant)}, M={Mdom}",
+                "bytes_per_launch": int(alg), "mean_launch_us": round(mean_ms[Mdom] * 1e3, 2)}
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s uncompressed-equivalent; per-M us: "
+        + ", ".join(f"{M}: {mean_ms[M] * 1e3:.1f}" for M in Ms))
+
+    detail = {"plans": {str(M): {"pipeline": uw.PIPELINE_NAMES[plans[M].pipeline], "variant": uw.variant_name(plans[M].variant),
+                                 "us": round(mean_ms[M] * 1e3, 2),
+                                 "hbm_frac_compressed": round(algorithmic_bytes(h, M, plans[M].pipeline) / (mean_ms[M] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                        for M in Ms},
+              "blob_bytes_per_weight": round(blob.size / (N * K), 4),
+              "palette_bytes_per_weight": round((N * K * 1.5 + 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw) / (N * K), 4)}
+    large_m = None
+    if not args.no_detail:
+        # every pipeline at every M (best variant each), cold weights via rotation
+        pip = {}
+        for M in Ms:
+            for p in range(4):
+                pl = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_idx=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=5,
+                                 warmup=1, pipeline_mask=1 << p, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
+                ts = []
+                for r in range(3 * R):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    c = r % R
+                    a.record(stream)
+                    uw.run_pipeline(p, h, blobs[c], xs[M], ys[M], M, d_idx=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
+                                    variant=pl.variant, stream=stream)
+                    b.record(stream)
+                    ts.append((a, b))
+                torch.cuda.synchronize()
+                us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+                pip[f"M={M} {uw.PIPELINE_NAMES[p]}"] = {
+                    "variant": uw.variant_name(pl.variant), "us": round(us, 2),
+                    "uncompressed_GBs": round(2 * N * K / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac_compressed": round(algorithmic_bytes(h, M, p) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        detail["pipelines"] = pip
+        large_m = large_m_line(uw, synth, torch, dev, stream, log)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(synth, cfg, w, Ms, log)
+
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.add(a, 1, out=b)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "uncompressed-equiv weight GB/s of decode+GEMM vs HBM roof; TFLOP/s at M>=1024",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B gate_proj shape, W 14336x4096 bf16 N(0,0.02) + 0.01% 2^+-10 outliers, "
+                               "exponent-compressed; X Mx4096 bf16, M in {1,16,64}; autotuned pipeline per M",
+                   "global_batch": int(sum(Ms)), "seq_len": 1, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+        "large_m": large_m,
+    }
+    print(json.dumps(out))
+
+
+def large_m_line(uw, synth, torch, dev, stream, log):
+    """TFLOP/s of the reconstructive GEMM on the down_proj shape at M = 4096 (MFMA-bound),
+    best of the direct-palette and plain-bf16 variants, vs the 2.5 PFLOP/s bf16 peak."""
+    cfg = synth.CONFIGS["down"]
+    w = synth.gen_weight(cfg, "down")
+    blob = uw.encode(w)
+    h = uw.inspect(blob)
+    N, K, M = h.N, h.K, 4096
+    b = torch.from_numpy(blob).to(dev)
+    idx = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    uw.transcode_palette(h, b, idx)
+    x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    ws = torch.empty(uw.workspace_bytes(h, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+    res = {}
+    for p in (uw.PIPE_DIRECT, uw.PIPE_FULL):
+        pl = uw.autotune(h, b, x, y, [M], d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), reps=5, warmup=2,
+                         pipeline_mask=1 << p)[0]
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            uw.run_pipeline(p, h, b, x, y, M, d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), variant=pl.variant, stream=stream)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(c) for a, c in ts]))
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        res[uw.PIPELINE_NAMES[p]] = {"variant": uw.variant_name(pl.variant), "ms": round(ms, 4), "tflops": round(tf, 1),
+                                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    log(f"[bench] large M: {res}")
+    return {"workload": "down_proj shape W 4096x14336, M=4096", "unit": "TFLOP/s", **res}
+
+
+def cpu_baseline(synth, cfg, w, Ms, log):
+    """The CPU oracle on one full step: for each M, bit-serial decode of the Huffman blob
+    to bf16 W, then the fp64 GEMM; single-threaded C."""
+    import oracle
+
+    blob = oracle.encode(w, chunk=256)
+    xs = {M: synth.gen_x(cfg, M, w.shape[1]) for M in Ms}
+    t = time.time()
+    for M in Ms:
+        d = oracle.decode(blob, want=("w",))
+        oracle.gemm(xs[M], d["w"])
+    dt = time.time() - t
+    N, K = w.shape
+    v = 2.0 * N * K * len(Ms) / dt / 1e9
+    log(f"[bench] cpu oracle step {dt:.1f}s -> {v:.3f} GB/s")
+    return {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (M in {{{', '.join(map(str, Ms))}}}: decode + fp64 GEMM each), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
