@@ -52,8 +52,9 @@ def algorithmic_bytes(h, M, pipeline):
     N, K = h.N, h.K
     side = 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw  # raw-group tables
     xy = 2 * M * K + 4 * M * N
-    if pipeline == 3:  # direct palette: sm plane + index plane + raw tables
-        return N * K + N * K // 2 + side + xy
+    if pipeline == 3:  # direct palette: the load-time direct plane (blocks, meta, raw side table)
+        T, G = (N + 15) // 16, K // 64
+        return 1536 * T * G + (8 * T * G + 63) // 64 * 64 + 64 * h.n_raw + xy
     huff = N * K + side + 4 * (h.n_chunks + 1) + h.bytes_stream  # Huffman-format blob
     plane = {0: 2 * N * K, 1: N * K, 2: N * K // 2}[pipeline]
     gemm_in = {0: 2 * N * K, 1: 2 * N * K + side, 2: N * K + N * K // 2 + side}[pipeline]
@@ -96,14 +97,14 @@ def main():
     log(f"[bench] gate {N}x{K}: blob {blob.size / 1e6:.1f} MB ({blob.size / (N * K):.3f} B/w), raw groups {h.n_raw}, "
         f"prep {time.time() - t0:.1f}s")
 
-    # R copies of the blob and of its load-time palette-index plane (direct palette)
+    # R copies of the blob and of its load-time direct-palette plane
     R = args.copies
     d_blob = torch.from_numpy(blob).to(dev)
     blobs, idxs = [], []
     for r in range(R):
         b = d_blob.clone()
-        i = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
-        uw.transcode_palette(h, b, i)
+        i = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+        uw.prepare_direct(h, b, i)
         blobs.append(b)
         idxs.append(i)
     del d_blob
@@ -117,7 +118,7 @@ def main():
     # autotune every M (cold-cache timing: the scrub buffer is overwritten before each rep)
     plans = {}
     for M in Ms:
-        plans[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_idx=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
+        plans[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
                                warmup=2, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
     log("[bench] plans: " + ", ".join(f"M={M}: {plans[M]!r} ({uw.variant_name(plans[M].variant)})" for M in Ms))
 
@@ -130,7 +131,7 @@ def main():
             p = plans[M]
             if events is not None:
                 events[M][0].record(stream)
-            uw.run_pipeline(p.pipeline, h, blobs[c], xs[M], ys[M], M, d_idx=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
+            uw.run_pipeline(p.pipeline, h, blobs[c], xs[M], ys[M], M, d_direct=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
                             variant=p.variant, stream=stream)
             if events is not None:
                 events[M][1].record(stream)
@@ -175,21 +176,21 @@ def main():
                                  "hbm_frac_compressed": round(algorithmic_bytes(h, M, plans[M].pipeline) / (mean_ms[M] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                         for M in Ms},
               "blob_bytes_per_weight": round(blob.size / (N * K), 4),
-              "palette_bytes_per_weight": round((N * K * 1.5 + 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw) / (N * K), 4)}
+              "direct_plane_bytes_per_weight": round(uw.direct_plane_bytes(h) / (N * K), 4)}
     large_m = None
     if not args.no_detail:
         # every pipeline at every M (best variant each), cold weights via rotation
         pip = {}
         for M in Ms:
             for p in range(4):
-                pl = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_idx=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=5,
+                pl = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=5,
                                  warmup=1, pipeline_mask=1 << p, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
                 ts = []
                 for r in range(3 * R):
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     c = r % R
                     a.record(stream)
-                    uw.run_pipeline(p, h, blobs[c], xs[M], ys[M], M, d_idx=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
+                    uw.run_pipeline(p, h, blobs[c], xs[M], ys[M], M, d_direct=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
                                     variant=pl.variant, stream=stream)
                     b.record(stream)
                     ts.append((a, b))
@@ -240,20 +241,20 @@ def large_m_line(uw, synth, torch, dev, stream, log):
     h = uw.inspect(blob)
     N, K, M = h.N, h.K, 4096
     b = torch.from_numpy(blob).to(dev)
-    idx = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
-    uw.transcode_palette(h, b, idx)
+    idx = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+    uw.prepare_direct(h, b, idx)
     x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
     y = torch.empty(M, N, dtype=torch.float32, device=dev)
     ws = torch.empty(uw.workspace_bytes(h, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
     res = {}
     for p in (uw.PIPE_DIRECT, uw.PIPE_FULL):
-        pl = uw.autotune(h, b, x, y, [M], d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), reps=5, warmup=2,
+        pl = uw.autotune(h, b, x, y, [M], d_direct=idx, d_ws=ws, ws_bytes=ws.numel(), reps=5, warmup=2,
                          pipeline_mask=1 << p)[0]
         ts = []
         for _ in range(10):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            uw.run_pipeline(p, h, b, x, y, M, d_idx=idx, d_ws=ws, ws_bytes=ws.numel(), variant=pl.variant, stream=stream)
+            uw.run_pipeline(p, h, b, x, y, M, d_direct=idx, d_ws=ws, ws_bytes=ws.numel(), variant=pl.variant, stream=stream)
             e1.record(stream)
             ts.append((e0, e1))
         torch.cuda.synchronize()

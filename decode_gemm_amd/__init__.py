@@ -16,9 +16,9 @@ import numpy as np
 
 __all__ = [
     "UwError", "Header", "Plan", "lib", "encode", "inspect", "validate_header", "decode_full",
-    "decode_exponent", "transcode_palette", "recon_gemm", "run_pipeline", "autotune", "swiglu",
-    "workspace_bytes", "variant_count", "variant_name", "variant_supports", "version",
-    "W_BF16", "W_EXP", "W_IDX", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT",
+    "decode_exponent", "transcode_palette", "prepare_direct", "recon_gemm", "run_pipeline", "autotune", "swiglu",
+    "workspace_bytes", "direct_plane_bytes", "variant_count", "variant_name", "variant_supports", "version",
+    "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT",
     "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS",
 ]
 
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuw.so")
 STATUS = {0: "UW_OK", 1: "UW_EINVAL", 2: "UW_ESHAPE", 3: "UW_EFORMAT", 4: "UW_ERANGE", 5: "UW_ENOSPACE",
           6: "UW_EHIP", 7: "UW_EUNSUPPORTED", 8: "UW_EINTERNAL"}
 OK, EINVAL, ESHAPE, EFORMAT, ERANGE, ENOSPACE, EHIP, EUNSUPPORTED, EINTERNAL = range(9)
-W_BF16, W_EXP, W_IDX = 0, 1, 2
+W_BF16, W_EXP, W_IDX, W_DIRECT = 0, 1, 2, 3
 PIPE_FULL, PIPE_EXP, PIPE_TRANSCODE, PIPE_DIRECT = 0, 1, 2, 3
 PIPELINE_NAMES = {0: "full", 1: "exp", 2: "transcode", 3: "direct"}
 DERR_BADCODE, DERR_CHUNKLEN = 1, 2
@@ -73,7 +73,7 @@ class Plan(ctypes.Structure):
 
 class TuneArgs(ctypes.Structure):
     _fields_ = [
-        ("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_idx", ctypes.c_void_p),
+        ("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_direct", ctypes.c_void_p),
         ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p), ("d_ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("reps", ctypes.c_int32), ("warmup", ctypes.c_int32), ("pipeline_mask", ctypes.c_uint32),
         ("variant_mask", ctypes.c_int32), ("d_scrub", ctypes.c_void_p), ("scrub_bytes", ctypes.c_size_t),
@@ -96,6 +96,8 @@ def _load():
         "uw_decode_full": ([H, P, P, P, P], ctypes.c_int),
         "uw_decode_exponent": ([H, P, P, P, P], ctypes.c_int),
         "uw_transcode_palette": ([H, P, P, P, P], ctypes.c_int),
+        "uw_prepare_direct": ([H, P, P, P, P], ctypes.c_int),
+        "uw_direct_plane_bytes": ([H, ctypes.POINTER(sz)], ctypes.c_int),
         "uw_recon_gemm": ([ctypes.POINTER(GemmArgs), P], ctypes.c_int),
         "uw_variant_count": ([], ctypes.c_int),
         "uw_variant_name": ([ctypes.c_int], ctypes.c_char_p),
@@ -204,6 +206,17 @@ def transcode_palette(h: Header, d_blob, d_idx, d_err=None, stream=None) -> None
     _check(lib.uw_transcode_palette(ctypes.byref(h), _ptr(d_blob), _ptr(d_idx), _ptr(d_err), _stream(stream)))
 
 
+def prepare_direct(h: Header, d_blob, d_direct, d_err=None, stream=None) -> None:
+    """uw_prepare_direct: the direct-palette plane (direct_plane_bytes(h) bytes), made once at load."""
+    _check(lib.uw_prepare_direct(ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), _ptr(d_err), _stream(stream)))
+
+
+def direct_plane_bytes(h: Header) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.uw_direct_plane_bytes(ctypes.byref(h), ctypes.byref(out)))
+    return out.value
+
+
 def recon_gemm(h: Header, d_blob, src: int, d_wplane, d_x, d_y, M: int, ldx: int | None = None,
                ldy: int | None = None, variant: int = -1, stream=None) -> None:
     a = GemmArgs(M, _ptr(d_x), h.K if ldx is None else ldx, ctypes.pointer(h), _ptr(d_blob), src, _ptr(d_wplane),
@@ -211,17 +224,17 @@ def recon_gemm(h: Header, d_blob, src: int, d_wplane, d_x, d_y, M: int, ldx: int
     _check(lib.uw_recon_gemm(ctypes.byref(a), _stream(stream)))
 
 
-def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_idx=None, d_ws=None, ws_bytes: int = 0,
+def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_direct=None, d_ws=None, ws_bytes: int = 0,
                  variant: int = -1, d_err=None, ldx: int | None = None, ldy: int | None = None, stream=None) -> None:
-    _check(lib.uw_run_pipeline(pipeline, variant, ctypes.byref(h), _ptr(d_blob), _ptr(d_idx), M, _ptr(d_x),
+    _check(lib.uw_run_pipeline(pipeline, variant, ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), M, _ptr(d_x),
                                h.K if ldx is None else ldx, _ptr(d_y), h.N if ldy is None else ldy, _ptr(d_ws),
                                ws_bytes, _ptr(d_err), _stream(stream)))
 
 
-def autotune(h: Header, d_blob, d_x, d_y, Ms, d_idx=None, d_ws=None, ws_bytes: int = 0, reps: int = 0,
+def autotune(h: Header, d_blob, d_x, d_y, Ms, d_direct=None, d_ws=None, ws_bytes: int = 0, reps: int = 0,
              warmup: int = 0, pipeline_mask: int = 0, variant_mask: int = 0, d_scrub=None, scrub_bytes: int = 0,
              stream=None) -> list:
-    a = TuneArgs(ctypes.pointer(h), _ptr(d_blob), _ptr(d_idx), _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes, reps,
+    a = TuneArgs(ctypes.pointer(h), _ptr(d_blob), _ptr(d_direct), _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes, reps,
                  warmup, pipeline_mask, variant_mask, _ptr(d_scrub), scrub_bytes)
     ms = (ctypes.c_int64 * len(Ms))(*Ms)
     out = (Plan * len(Ms))()

@@ -93,6 +93,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
             const uint32_t fc = tab[l], cnt = tab[16 + l];
             if (code >= fc && code - fc < cnt) {
                 const uint32_t s = byte_of(&tab[48], tab[32 + l] + (code - fc));
+                // tab[52..55]: palette (full / exponent modes) or value-order positions (direct)
                 const uint32_t v = MODE == DEC_IDX ? s : byte_of(&tab[52], s);
                 ent = l | (v << 8);
                 break;
@@ -127,7 +128,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
             const uint32_t bw = a.bitmap[r * a.words + (j >> 5)];
             uint32_t* row = stage + lane * kPitch;
             if ((bw >> (j & 31)) & 1u) {
-                if (MODE == DEC_IDX) {
+                if (MODE == DEC_IDX || MODE == DEC_DIRECT) {
                     for (int t = 0; t < 8; t++) row[t] = 0;  // raw groups carry index 0
                 } else {
                     uint32_t before = __popc(bw & ((1u << (j & 31)) - 1u));
@@ -145,19 +146,22 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
                     }
                 }
             } else {
-                constexpr int PER = MODE == DEC_IDX ? 8 : 4;    // values per dword
-                constexpr int SH = MODE == DEC_IDX ? 4 : 8;     // bits per value
+                constexpr bool NIB = MODE == DEC_IDX || MODE == DEC_DIRECT;
+                constexpr int PER = NIB ? 8 : 4;  // values per dword
 #pragma unroll
                 for (int d = 0; d < 64 / PER; d++) {
                     uint32_t packed = 0;
 #pragma unroll
                     for (int t = 0; t < PER; t++) {
+                        // index plane: weight t of the dword in nibble t; direct plane:
+                        // weights t and t+4 share byte t % 4 (low, high nibble)
+                        const int sh = MODE == DEC_IDX ? 4 * t : MODE == DEC_DIRECT ? (t < 4 ? 8 * t : 8 * (t - 4) + 4) : 8 * t;
                         const uint32_t peek = static_cast<uint32_t>(buf >> (64 - lmax));
                         const uint32_t ent = lut[peek];
                         uint32_t len = ent & 15u;
                         errbits |= len == 0 ? UW_DERR_BADCODE : 0u;
                         len = len ? len : lmax;
-                        packed |= (ent >> 8) << (SH * t);
+                        packed |= (ent >> 8) << sh;
                         buf <<= len;
                         nb -= static_cast<int>(len);
                         consumed += len;
@@ -200,7 +204,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
                     *reinterpret_cast<u32x4*>(out + fs + 8 * p) = v;
                 }
             }
-        } else {
+        } else if (MODE == DEC_IDX) {
             uint8_t* out = static_cast<uint8_t*>(a.out);
 #pragma unroll
             for (int q = 0; q < 2; q++) {
@@ -210,6 +214,28 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
                     const uint32_t* src = stage + s * kPitch + 4 * p;
                     u32x4 v = {src[0], src[1], src[2], src[3]};
                     *reinterpret_cast<u32x4*>(out + fs / 2 + 16 * p) = v;
+                }
+            }
+        } else {
+            // direct plane: tile-major blocks. Item (segment s, lane group g): the 16
+            // sign/mantissa bytes of weights 16g..16g+15 of the segment's group, rearranged
+            // as (mantissa << 1) | sign of the pair partner, and the two staged index
+            // dwords of those weights, stored where MFMA lane 16g + r of the row's tile
+            // reads them (raw groups keep their bytes; their staged indices are zero).
+            uint8_t* out = static_cast<uint8_t*>(a.out);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t item = q * 64 + lane, s = item >> 2, g = item & 3;
+                const int64_t fs = static_cast<int64_t>(wave_c0 + s) * a.chunk + 64 * static_cast<int64_t>(gi);
+                if (wave_c0 + s < a.n_chunks && fs < a.n_elems) {
+                    const int64_t n = fs / a.K, j = (fs - n * a.K) >> 6;
+                    const int64_t blk = 1536 * ((n >> 4) * (a.K >> 6) + j);
+                    const uint32_t l = 16 * g + static_cast<uint32_t>(n & 15);
+                    u32x4 v = *reinterpret_cast<const u32x4*>(a.sm + fs + 16 * g);
+                    v = (v & 0x7F7F7F7Fu) << 1 | ((v << 1) & 0x01000100u) | ((v >> 15) & 0x00010001u);
+                    *reinterpret_cast<u32x4*>(out + blk + 16 * l) = v;
+                    const uint32_t* src = stage + s * kPitch + 2 * g;
+                    *reinterpret_cast<u32x2*>(out + blk + 1024 + 8 * l) = u32x2{src[0], src[1]};
                 }
             }
         }
@@ -222,7 +248,83 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
     }
 }
 
+// Direct plane, second part: one thread per 16-row tile walks the tile's groups in
+// order and writes, per (tile, group), the mask of raw rows and the side-table index of
+// its first raw row, copies those rows' verbatim exponents from the blob's raw table into
+// the side table (ordered by tile, group, row), and zeroes the block bytes of rows past N.
+struct MetaArgs {
+    const uint32_t* bitmap;
+    const uint32_t* row_base;
+    const uint8_t* raw;
+    uint8_t* blocks;
+    uint32_t* meta;
+    uint8_t* side;
+    int64_t N, G;
+    uint32_t T, words, raw_max;
+};
+
+__global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
+{
+    const uint32_t t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= a.T) return;
+    if (t == 0) {  // zero the padding between the meta entries and the side table
+        uint8_t* pad = reinterpret_cast<uint8_t*>(a.meta + 2 * static_cast<int64_t>(a.T) * a.G);
+        for (uint8_t* q = pad; q < a.side; q++) *q = 0;
+    }
+    const int64_t row0 = 16 * static_cast<int64_t>(t);
+    uint32_t running = a.row_base[row0 < a.N ? row0 : a.N];
+    uint32_t rb[16], cnt[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        rb[r] = row0 + r < a.N ? a.row_base[row0 + r] : 0;
+        cnt[r] = 0;
+    }
+    for (uint32_t wd = 0; wd < a.words; wd++) {
+        uint32_t bw[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) bw[r] = row0 + r < a.N ? a.bitmap[(row0 + r) * a.words + wd] : 0;
+        const int64_t jend = (32 * static_cast<int64_t>(wd) + 32) < a.G ? 32 * static_cast<int64_t>(wd) + 32 : a.G;
+        for (int64_t j = 32 * static_cast<int64_t>(wd); j < jend; j++) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int r = 0; r < 16; r++) mask |= ((bw[r] >> (j & 31)) & 1u) << r;
+            uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
+            m[0] = mask;
+            m[1] = running;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                if ((mask >> r) & 1u) {
+                    uint32_t ri = rb[r] + cnt[r];
+                    ri = ri < a.raw_max ? ri : a.raw_max;
+                    const u32x4* src = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64);
+                    u32x4* dst = reinterpret_cast<u32x4*>(a.side + static_cast<uint64_t>(running) * 64);
+                    dst[0] = src[0];
+                    dst[1] = src[1];
+                    dst[2] = src[2];
+                    dst[3] = src[3];
+                    running++;
+                    cnt[r]++;
+                }
+            }
+            if (row0 + 16 > a.N) {  // last tile: rows past N are zero
+                uint8_t* blk = a.blocks + 1536 * (static_cast<int64_t>(t) * a.G + j);
+                for (int r = static_cast<int>(a.N - row0); r < 16; r++)
+                    for (int g = 0; g < 4; g++) {
+                        *reinterpret_cast<u32x4*>(blk + 16 * (16 * g + r)) = u32x4{0, 0, 0, 0};
+                        *reinterpret_cast<u32x2*>(blk + 1024 + 8 * (16 * g + r)) = u32x2{0, 0};
+                    }
+            }
+        }
+    }
+}
+
 }  // namespace
+
+uint64_t direct_plane_bytes(const uw_header* h)
+{
+    const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
+    return 1536 * T * G + (8 * T * G + 63) / 64 * 64 + 64 * static_cast<uint64_t>(h->n_raw);
+}
 
 uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err, void* stream)
 {
@@ -261,7 +363,13 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
         a.first_index[i] = t.first_index[i];
     }
     std::memcpy(&a.sorted_lo, t.sorted, 16);
-    std::memcpy(a.pal, h->palette, 16);
+    if (mode == DEC_DIRECT) {
+        ValueOrder vo;
+        value_order(h, &vo);
+        std::memcpy(a.pal, vo.order, 16);
+    } else {
+        std::memcpy(a.pal, h->palette, 16);
+    }
     const size_t lds = kStageDwords * 4 + (2u << h->lmax);
     const dim3 grid((h->n_chunks + 64 * kWaves - 1) / (64 * kWaves));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -269,7 +377,24 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
     case DEC_FULL: hipLaunchKernelGGL(decode_kernel<DEC_FULL>, grid, dim3(256), lds, s, a); break;
     case DEC_EXP: hipLaunchKernelGGL(decode_kernel<DEC_EXP>, grid, dim3(256), lds, s, a); break;
     case DEC_IDX: hipLaunchKernelGGL(decode_kernel<DEC_IDX>, grid, dim3(256), lds, s, a); break;
+    case DEC_DIRECT: hipLaunchKernelGGL(decode_kernel<DEC_DIRECT>, grid, dim3(256), lds, s, a); break;
     default: return fail(UW_EINVAL, "bad decode mode");
+    }
+    if (mode == DEC_DIRECT) {
+        MetaArgs m;
+        m.bitmap = a.bitmap;
+        m.row_base = a.row_base;
+        m.raw = a.raw;
+        m.blocks = static_cast<uint8_t*>(d_out);
+        const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
+        m.meta = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_out) + 1536 * T * G);
+        m.side = static_cast<uint8_t*>(d_out) + 1536 * T * G + (8 * T * G + 63) / 64 * 64;
+        m.N = h->N;
+        m.G = static_cast<int64_t>(G);
+        m.T = static_cast<uint32_t>(T);
+        m.words = h->bitmap_words;
+        m.raw_max = a.raw_max;
+        hipLaunchKernelGGL(direct_meta_kernel, dim3((m.T + 255) / 256), dim3(256), 0, s, m);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(UW_EHIP, "decode launch failed: %s", hipGetErrorString(e));
@@ -293,6 +418,19 @@ uw_status uw_decode_exponent(const uw_header* h, const void* d_blob, uint8_t* d_
 uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* d_idx, uint32_t* d_err, void* stream)
 {
     return uw::launch_decode(h, d_blob, d_idx, uw::DEC_IDX, d_err, stream);
+}
+
+uw_status uw_prepare_direct(const uw_header* h, const void* d_blob, uint8_t* d_direct, uint32_t* d_err, void* stream)
+{
+    return uw::launch_decode(h, d_blob, d_direct, uw::DEC_DIRECT, d_err, stream);
+}
+
+uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out)
+{
+    uw::clear_error();
+    if (!h || !out) return uw::fail(UW_EINVAL, "NULL argument");
+    *out = static_cast<size_t>(uw::direct_plane_bytes(h));
+    return UW_OK;
 }
 
 }  // extern "C"

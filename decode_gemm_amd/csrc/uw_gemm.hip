@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <utility>
 
 #include "uw_internal.h"
 #include "uw_recon.h"
@@ -47,7 +48,12 @@ struct GemmArgs {
     float* y;
     int64_t ldx, ldy, M, N, K;
     uint32_t words, raw_max;
-    uint32_t pal[4];
+    uint32_t pal[4];   // palette (rank order) for the index plane
+    uint32_t vpal[4];  // palette sorted by value, for the direct plane
+    uint32_t base4;    // smallest palette exponent * 0x01010101 (direct plane, contiguous palette)
+    const uint8_t* dmeta;  // direct plane: per (tile, group) raw mask and side-table base
+    const uint8_t* dside;  // direct plane: raw exponents, 64 bytes per raw (row, group)
+    uint32_t tiles;        // direct plane: ceil(N / 16)
 };
 
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c)
@@ -65,53 +71,172 @@ __device__ __forceinline__ uint32_t raw_index(const GemmArgs& a, int64_t row, ui
     return ri < a.raw_max ? ri : a.raw_max;
 }
 
-// Load and rebuild 16 consecutive weights W[row][k0 .. k0+15] (k0 a multiple of 16
-// inside 64-group j) as two 8-weight MFMA operand pieces.
+// ------------------------------------------------------------------------- loaders
+// The unit of work of both kernels: 16 consecutive weights W[row][k0 .. k0+15] (k0 a
+// multiple of 16 inside 64-group j) -> two 8-weight MFMA operand pieces. Per-lane base
+// pointers are set up once per row; a group's data then sits at a fixed stride.
+//   bf16:   32 B of weights                          (stride 128 B per group)
+//   exp:    16 B sign/mantissa + 16 B exponents       (64 + 64)
+//   idx:    16 B sign/mantissa + 8 B nibbles           (64 + 32)
+//   direct: 16 B sm' + 8 B nibbles of the (tile, group) block (1536 + 1536), so a
+//           wave's loads are 1 KB and 512 B contiguous
+struct W16 {
+    u32x4 a, b;
+};
+
 template <int SRC>
-__device__ __forceinline__ void load_w16(const GemmArgs& a, int64_t row, int64_t k0, uint32_t j, u32x4& p0, u32x4& p1)
-{
-    const int64_t off = row * a.K + k0;
-    if (SRC == UW_W_BF16) {
-        const u32x4* w = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.wplane) + off);
-        p0 = w[0];
-        p1 = w[1];
-    } else if (SRC == UW_W_EXP) {
-        const u32x4 s = *reinterpret_cast<const u32x4*>(a.sm + off);
-        const u32x4 e = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.wplane) + off);
-        uint32_t ea, eb;
-        split_exps(e.x, e.y, ea, eb);
-        p0 = piece_from_split(ea, eb, s.x, s.y);
-        split_exps(e.z, e.w, ea, eb);
-        p1 = piece_from_split(ea, eb, s.z, s.w);
-    } else {
-        const u32x4 s = *reinterpret_cast<const u32x4*>(a.sm + off);
-        const u32x2 iv = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(a.wplane) + off / 2);
-        const uint32_t bw = a.bitmap[row * a.words + (j >> 5)];
-        uint32_t ea0, eb0, ea1, eb1;
-        exps_from_idx(iv.x, a.pal, ea0, eb0);
-        exps_from_idx(iv.y, a.pal, ea1, eb1);
-        if ((bw >> (j & 31)) & 1u) {
-            const uint32_t ri = raw_index(a, row, j, bw);
-            const u32x4 e = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + (k0 & 63));
-            split_exps(e.x, e.y, ea0, eb0);
-            split_exps(e.z, e.w, ea1, eb1);
+struct Plane {
+    static constexpr int S0 = SRC == UW_W_BF16 ? 128 : SRC == UW_W_DIRECT ? 1536 : 64;
+    static constexpr int S1 = SRC == UW_W_BF16 ? 128 : SRC == UW_W_IDX ? 32 : SRC == UW_W_DIRECT ? 1536 : 64;
+    const uint8_t* p0;
+    const uint8_t* p1;
+
+    Plane() = default;
+    // lane's pointers for weights [row][16*g ..] of group 0
+    __device__ __forceinline__ Plane(const GemmArgs& a, int64_t row, int g)
+    {
+        const int64_t G = a.K >> 6;
+        if (SRC == UW_W_BF16) {
+            p0 = static_cast<const uint8_t*>(a.wplane) + 2 * (row * a.K + 16 * g);
+            p1 = p0;
+        } else if (SRC == UW_W_EXP) {
+            p0 = a.sm + row * a.K + 16 * g;
+            p1 = static_cast<const uint8_t*>(a.wplane) + row * a.K + 16 * g;
+        } else if (SRC == UW_W_IDX) {
+            p0 = a.sm + row * a.K + 16 * g;
+            p1 = static_cast<const uint8_t*>(a.wplane) + (row * a.K + 16 * g) / 2;
+        } else {
+            // tile-major blocks: rows past N exist (zero) up to the last tile
+            int64_t t = row >> 4;
+            t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
+            const int64_t l = 16 * g + (row & 15);
+            p0 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * G) + 16 * l;
+            p1 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * G) + 1024 + 8 * l;
         }
-        p0 = piece_from_split(ea0, eb0, s.x, s.y);
-        p1 = piece_from_split(ea1, eb1, s.z, s.w);
+    }
+
+    __device__ __forceinline__ void load(uint32_t j, W16& w) const
+    {
+        w.a = *reinterpret_cast<const u32x4*>(p0 + static_cast<int64_t>(S0) * j);
+        if (SRC == UW_W_BF16 || SRC == UW_W_EXP) {
+            w.b = *reinterpret_cast<const u32x4*>(p1 + static_cast<int64_t>(S1) * j + (SRC == UW_W_BF16 ? 16 : 0));
+        } else {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(p1 + static_cast<int64_t>(S1) * j);
+            w.b.x = v.x;
+            w.b.y = v.y;
+        }
+    }
+};
+
+// Verbatim exponents of a raw group (16 of them, from k0 & 63), natural order.
+__device__ __forceinline__ u32x4 raw_exps16(const GemmArgs& a, int64_t row, int64_t k0, uint32_t j, uint32_t bw)
+{
+    const uint32_t ri = raw_index(a, row, j, bw);
+    return *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + (k0 & 63));
+}
+
+// Rebuild the 16 weights of a W16 as two operand pieces. Raw groups are not handled
+// here: the index plane holds index 0 there (the weight comes out as sign, palette[0],
+// mantissa), the direct plane index 0 (smallest palette exponent); the kernels substitute
+// or correct those weights separately.
+template <int SRC, bool CONTIG>
+__device__ __forceinline__ void rebuild16(const GemmArgs& a, const W16& w, u32x4& p0, u32x4& p1)
+{
+    if (SRC == UW_W_BF16) {
+        p0 = w.a;
+        p1 = w.b;
+    } else if (SRC == UW_W_EXP) {
+        uint32_t ea, eb;
+        split_exps(w.b.x, w.b.y, ea, eb);
+        p0 = piece_from_split(ea, eb, w.a.x, w.a.y);
+        split_exps(w.b.z, w.b.w, ea, eb);
+        p1 = piece_from_split(ea, eb, w.a.z, w.a.w);
+    } else if (SRC == UW_W_IDX) {
+        uint32_t ea, eb;
+        exps_from_idx(w.b.x, a.pal, ea, eb);
+        p0 = piece_from_split(ea, eb, w.a.x, w.a.y);
+        exps_from_idx(w.b.y, a.pal, ea, eb);
+        p1 = piece_from_split(ea, eb, w.a.z, w.a.w);
+    } else {
+        uint32_t e0, e1;
+        unit_exps<CONTIG>(w.b.x, a.base4, a.vpal, e0, e1);
+        p0 = unit_piece(e0, e1, w.a.x, w.a.y);
+        unit_exps<CONTIG>(w.b.y, a.base4, a.vpal, e0, e1);
+        p1 = unit_piece(e0, e1, w.a.z, w.a.w);
     }
 }
 
-// ------------------------------------------------------------------------- skinny
-// Block = WPB waves (blockDim.x = 64 * WPB) covering rows [16*RT*blockIdx.x, +16*RT) and
-// all of K; wave w takes the 64-groups j = w, w + WPB, ... CT = ceil(M / 16) column tiles.
-template <int SRC, int CT, int RT>
-__global__ void __launch_bounds__(1024) gemm_skinny(GemmArgs a)
+// Direct plane, raw row: the block kept its sign/mantissa bytes; take the 16 verbatim
+// exponents (natural order) instead of the palette.
+__device__ __forceinline__ void rebuild16_raw(const W16& w, const u32x4& ex, u32x4& p0, u32x4& p1)
 {
+    p0 = unit_piece(ex.x, ex.y, w.a.x, w.a.y);
+    p1 = unit_piece(ex.z, ex.w, w.a.z, w.a.w);
+}
+
+// Side-table address of this lane's 16 raw exponents for a block with meta (mask, base),
+// or `dummy` (any readable 16 bytes) when its row is not raw there.
+__device__ __forceinline__ const u32x4* raw_exp_addr(const GemmArgs& a, u32x2 meta, int r, int g, const uint8_t* dummy)
+{
+    const bool raw = (meta.x >> r) & 1u;
+    const uint32_t ri = meta.y + __popc(meta.x & ((1u << r) - 1u));
+    return reinterpret_cast<const u32x4*>(raw ? a.dside + static_cast<uint64_t>(ri) * 64 + 16 * g : dummy);
+}
+
+// Operand pieces for the exact correction of raw group j of `row`, for the 16 weights
+// [16g, 16g+16) of the group: T = the true weights (blob sign/mantissa + verbatim
+// exponents), U = minus what rebuild16 produced for them. MFMA(T) + MFMA(U) adds
+// (true - rebuilt) * X exactly; both are bf16 values, so nothing is rounded here.
+template <int SRC>
+__device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint32_t j, uint32_t ri, int g, u32x4& t0,
+                                           u32x4& t1, u32x4& u0, u32x4& u1)
+{
+    // index plane: T = the true weights (blob sign/mantissa + verbatim exponents), U = minus
+    // what rebuild16 produced for them, (sign, palette[0], mantissa) -> flip the signs.
+    // MFMA(T) + MFMA(U) adds (true - rebuilt) * X exactly: both are bf16 values.
+    const int64_t off = row * a.K + 64 * static_cast<int64_t>(j) + 16 * g;
+    const u32x4 sm = *reinterpret_cast<const u32x4*>(a.sm + off);
+    const u32x4 ex = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * g);
+    uint32_t ea, eb;
+    split_exps(ex.x, ex.y, ea, eb);
+    t0 = piece_from_split(ea, eb, sm.x, sm.y);
+    split_exps(ex.z, ex.w, ea, eb);
+    t1 = piece_from_split(ea, eb, sm.z, sm.w);
+    const uint32_t p0 = (a.pal[0] & 0xFFu) * 0x01010101u;
+    u0 = piece_from_split(p0, p0, sm.x ^ 0x80808080u, sm.y ^ 0x80808080u);
+    u1 = piece_from_split(p0, p0, sm.z ^ 0x80808080u, sm.w ^ 0x80808080u);
+}
+
+// ------------------------------------------------------------------------- skinny
+// Block = NW waves covering rows [16*RT*blockIdx.x, +16*RT) and all of K; wave w takes
+// the 64-groups j = w, w + NW, w + 2NW, ... so the block walks its rows front to back.
+// Each lane owns 16 consecutive k of one row (the MFMA A operand) and keeps a ring of U
+// groups in flight: the compressed W of group t+U and its X operand pieces are requested
+// as soon as group t has been consumed, so ~U groups per wave stay outstanding -- at
+// 8 TB/s a whole gate matrix is only a few memory latencies long. Vector loads retire in
+// issue order, so X travels with the same lead as W; all control flow in the loop is
+// wave-uniform, so the compiler waits for exactly the slot it consumes. Lanes of columns
+// m >= M read row M-1 (their outputs are never stored). CT = ceil(M / 16).
+//
+// Raw groups. Direct plane: each slot also carries its block's raw-row mask (requested
+// with the slot, a full ring turn ahead) and, half a turn ahead, the lane's verbatim
+// exponents when its row is raw (any readable address otherwise), so a raw row is just a
+// per-lane select in the rebuild. Index plane: the rebuild yields (sign, palette[0],
+// mantissa) for raw groups and the exact difference to the true weights is added after
+// the loop with extra MFMAs, from metadata fetched when the kernel starts.
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW>
+__global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
+{
+    static_assert(U % 2 == 0, "ring depth must be even");
+    constexpr bool DIRECT = SRC == UW_W_DIRECT;
+    constexpr bool POSTRAW = SRC == UW_W_IDX;
     extern __shared__ float red[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int64_t nb = static_cast<int64_t>(blockIdx.x) * (16 * RT);
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
+    const uint32_t T = G > static_cast<uint32_t>(wave) ? (G - wave + NW - 1) / NW : 0;  // groups of this wave
 
     floatx4 acc[RT][CT];
 #pragma unroll
@@ -119,43 +244,162 @@ __global__ void __launch_bounds__(1024) gemm_skinny(GemmArgs a)
 #pragma unroll
         for (int c = 0; c < CT; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    int64_t row[RT];
+    Plane<SRC> pl[RT];
+    const uint8_t* pmeta[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) {
         const int64_t rr = nb + 16 * i + r;
-        row[i] = rr < a.N ? rr : a.N - 1;
+        pl[i] = Plane<SRC>(a, DIRECT ? rr : (rr < a.N ? rr : a.N - 1), g);
+        if (DIRECT) {
+            int64_t t = (nb >> 4) + i;
+            t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
+            pmeta[i] = a.dmeta + 8 * t * G;
+        }
     }
     const uint16_t* xrow[CT];
-    bool xok[CT];
 #pragma unroll
     for (int c = 0; c < CT; c++) {
         const int64_t m = 16 * c + r;
-        xok[c] = m < a.M;
-        xrow[c] = a.x + (xok[c] ? m : 0) * a.ldx + 16 * g;
+        xrow[c] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
     }
 
-    for (uint32_t j = wave; j < G; j += nw) {
-        const int64_t k0 = 64 * static_cast<int64_t>(j) + 16 * g;
-        u32x4 A[RT][2], B[CT][2];
+    // Index plane: raw-group metadata of this wave's rows (local rows wave + NW * q),
+    // fetched now and consumed after the main loop: lane q holds row_base of row q, and
+    // the bitmap words (row q, word wd) sit at flat position q * words + wd across BWV
+    // registers. Larger shapes fall back to direct loads after the loop.
+    constexpr int RPW = (16 * RT + NW - 1) / NW;  // rows per wave
+    constexpr int BWV = 4;
+    const uint32_t words = a.words;
+    const bool meta_fits = RPW * words <= 64u * BWV;
+    uint32_t rbv = 0, bwv[BWV] = {0, 0, 0, 0};
+    if (POSTRAW) {
+        const int64_t rq = nb + wave + NW * lane;
+        if (lane < RPW && rq < a.N) rbv = a.row_base[rq];
+        if (meta_fits) {
 #pragma unroll
-        for (int i = 0; i < RT; i++) load_w16<SRC>(a, row[i], k0, j, A[i][0], A[i][1]);
-#pragma unroll
-        for (int c = 0; c < CT; c++) {
-            if (xok[c]) {
-                const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[c] + 64 * static_cast<int64_t>(j));
-                B[c][0] = xp[0];
-                B[c][1] = xp[1];
-            } else {
-                B[c][0] = u32x4{0, 0, 0, 0};
-                B[c][1] = u32x4{0, 0, 0, 0};
+            for (int k = 0; k < BWV; k++) {
+                const uint32_t f = lane + 64 * k, q = f / words, wd = f - q * words;
+                const int64_t row = nb + wave + NW * static_cast<int64_t>(q);
+                if (q < static_cast<uint32_t>(RPW) && row < a.N) bwv[k] = a.bitmap[row * words + wd];
             }
         }
+    }
+
+    auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) {
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int c = 0; c < CT; c++) {
+            const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[c] + 64 * static_cast<int64_t>(j));
+            B[c][0] = xp[0];
+            B[c][1] = xp[1];
+        }
+    };
+    W16 ring[U][RT];
+    u32x4 xr[U][CT][2];
+    u32x2 mr[DIRECT ? U : 1][RT];  // direct: raw-row mask and side base of the slot's block
+    u32x4 rx[DIRECT ? U : 1][RT];  // direct: this lane's raw exponents for the slot's group
+    auto load_slot = [&](uint32_t j, auto uc) {
+        constexpr int u = decltype(uc)::value;
+#pragma unroll
+        for (int i = 0; i < RT; i++) {
+            pl[i].load(j, ring[u][i]);
+            if (DIRECT) mr[u % (DIRECT ? U : 1)][i] = *reinterpret_cast<const u32x2*>(pmeta[i] + 8 * static_cast<int64_t>(j));
+        }
+    };
+    auto load_raw = [&](uint32_t j, auto vc) {
+        constexpr int v = decltype(vc)::value % (DIRECT ? U : 1);
+#pragma unroll
+        for (int i = 0; i < RT; i++)
+            rx[v][i] = *raw_exp_addr(a, mr[v][i], r, g, pl[i].p0 + static_cast<int64_t>(Plane<SRC>::S0) * j);
+    };
+    // one group: rebuild ring slot u (group t), refill it with group t + U, request the
+    // raw exponents of group t + U/2, multiply, then refill the X pieces
+    auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) {
+        constexpr int u = decltype(uc)::value;
+        const uint32_t j = wave + NW * t;
+        u32x4 A[RT][2];
+#pragma unroll
+        for (int i = 0; i < RT; i++) {
+            rebuild16<SRC, CONTIG>(a, ring[u][i], A[i][0], A[i][1]);
+            if (DIRECT) {
+                if ((mr[u % (DIRECT ? U : 1)][i].x >> r) & 1u) rebuild16_raw(ring[u][i], rx[u % (DIRECT ? U : 1)][i], A[i][0], A[i][1]);
+            }
+        }
+        if (refill) load_slot(j + NW * U, uc);
+        if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
             for (int i = 0; i < RT; i++)
 #pragma unroll
-                for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s], B[c][s], acc[i][c]);
+                for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[u][c][s2], acc[i][c]);
+        if (refill) load_x(j + NW * U, xr[u]);
+    };
+    [&]<int... us>(std::integer_sequence<int, us...>) {
+        ((static_cast<uint32_t>(us) < T ? (load_slot(wave + NW * us, std::integral_constant<int, us>{}),
+                                           load_x(wave + NW * us, xr[us]))
+                                        : void()),
+         ...);
+        if (DIRECT)
+            ((us < U / 2 && static_cast<uint32_t>(us) < T ? load_raw(wave + NW * us, std::integral_constant<int, us>{})
+                                                          : void()),
+             ...);
+    }(std::make_integer_sequence<int, U>{});
+    uint32_t t0 = 0;
+    // steady state: every slot is consumed and refilled, no guards, so the compiler waits
+    // for exactly the slot it needs
+    for (; t0 + 2 * U <= T; t0 += U) {
+        [&]<int... us>(std::integer_sequence<int, us...>) {
+            (step(t0 + us, std::integral_constant<int, us>{}, true, true), ...);
+        }(std::make_integer_sequence<int, U>{});
+    }
+    // tail: the last one or two turns of the ring
+    for (; t0 < T; t0 += U) {
+        [&]<int... us>(std::integer_sequence<int, us...>) {
+            ((t0 + us < T ? step(t0 + us, std::integral_constant<int, us>{}, t0 + us + U < T, t0 + us + U / 2 < T)
+                          : void()),
+             ...);
+        }(std::make_integer_sequence<int, U>{});
+    }
+
+    if (POSTRAW) {
+        // raw groups of this wave's rows, corrected exactly with extra MFMAs each
+        for (int q = 0; q < RPW; q++) {
+            const int li = wave + NW * q;
+            const int64_t row = nb + li;
+            if (li >= 16 * RT || row >= a.N) break;
+            uint32_t ri = __builtin_amdgcn_readlane(rbv, q);
+            for (uint32_t wd = 0; wd < words; wd++) {
+                uint32_t bits;
+                if (meta_fits) {
+                    const uint32_t f = q * words + wd, k = f >> 6, l = f & 63;
+                    const uint32_t v = k == 0 ? bwv[0] : k == 1 ? bwv[1] : k == 2 ? bwv[2] : bwv[3];
+                    bits = __builtin_amdgcn_readlane(v, l);
+                } else {
+                    bits = __builtin_amdgcn_readfirstlane(a.bitmap[row * words + wd]);
+                }
+                while (bits) {
+                    const uint32_t j = 32 * wd + __builtin_ctz(bits);
+                    bits &= bits - 1;
+                    u32x4 t0v = {0, 0, 0, 0}, t1v = t0v, u0v = t0v, u1v = t0v;
+                    if (r == (li & 15)) raw_pieces<SRC>(a, row, j, ri, g, t0v, t1v, u0v, u1v);
+                    ri++;
+                    u32x4 B[CT][2];
+                    load_x(j, B);
+#pragma unroll
+                    for (int i = 0; i < RT; i++) {
+                        if (i == (li >> 4)) {
+#pragma unroll
+                            for (int c = 0; c < CT; c++) {
+                                acc[i][c] = mfma16(t0v, B[c][0], acc[i][c]);
+                                acc[i][c] = mfma16(t1v, B[c][1], acc[i][c]);
+                                acc[i][c] = mfma16(u0v, B[c][0], acc[i][c]);
+                                acc[i][c] = mfma16(u1v, B[c][1], acc[i][c]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
     }
 
     // cross-wave reduction: red[w][i][c][q][lane]
@@ -169,14 +413,15 @@ __global__ void __launch_bounds__(1024) gemm_skinny(GemmArgs a)
     __syncthreads();
     // output element o = ((tile * 16 + m_local) * 16 + n_local): consecutive threads write
     // consecutive n of one Y row
-    for (int o = threadIdx.x; o < TILES * 256; o += blockDim.x) {
+    for (int o = threadIdx.x; o < TILES * 256; o += 64 * NW) {
         const int tile = o >> 8, ml = (o >> 4) & 15, nl = o & 15;
         const int i = tile / CT, c = tile % CT;
         const int src_lane = (nl >> 2) * 16 + ml, q = nl & 3;
-        float s = 0.f;
-        for (int w = 0; w < nw; w++) s += red[((w * TILES + tile) * 4 + q) * 64 + src_lane];
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) sum += red[((w * TILES + tile) * 4 + q) * 64 + src_lane];
         const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
-        if (n < a.N && m < a.M) a.y[m * a.ldy + n] = s;
+        if (n < a.N && m < a.M) a.y[m * a.ldy + n] = sum;
     }
 }
 
@@ -186,86 +431,13 @@ __global__ void __launch_bounds__(1024) gemm_skinny(GemmArgs a)
 // in operand order: [16-row tile][k-half][lane][8 values].
 template <int BN, int BM>
 struct TiledCfg {
-    static constexpr int TN = BN / 32, TM = BM / 32;  // 16x16 tiles per wave
+    static constexpr int TN = BN / 32, TM = BM / 32;     // 16x16 tiles per wave
     static constexpr int WITEMS = (BN * 2 + 255) / 256;  // (row, k-half) items per thread, W
     static constexpr int XITEMS = (BM * 2 + 255) / 256;  // same for X (threads past BM*2 idle)
-    static constexpr int A_BYTES = BN * 64 * 2;       // one stage of rebuilt W
+    static constexpr int A_BYTES = BN * 64 * 2;          // one stage of rebuilt W
     static constexpr int B_BYTES = BM * 64 * 2;
     static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
 };
-
-// Compressed / raw global data for one (row, k-half) item of the W slice.
-struct WRegs {
-    u32x4 v0, v1, v2, v3;  // bf16: 64 B; exp: sm 32 B + exp 32 B; idx: sm 32 B + idx 16 B
-    uint32_t bw;
-};
-
-template <int SRC>
-__device__ __forceinline__ void tiled_load_w(const GemmArgs& a, int64_t row, int64_t kk, uint32_t j, WRegs& w)
-{
-    const int64_t off = row * a.K + kk;
-    if (SRC == UW_W_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.wplane) + off);
-        w.v0 = p[0];
-        w.v1 = p[1];
-        w.v2 = p[2];
-        w.v3 = p[3];
-    } else {
-        const u32x4* s = reinterpret_cast<const u32x4*>(a.sm + off);
-        w.v0 = s[0];
-        w.v1 = s[1];
-        if (SRC == UW_W_EXP) {
-            const u32x4* e = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.wplane) + off);
-            w.v2 = e[0];
-            w.v3 = e[1];
-        } else {
-            w.v2 = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.wplane) + off / 2);
-            w.bw = a.bitmap[row * a.words + (j >> 5)];
-        }
-    }
-}
-
-// Rebuild the 32 weights of an item and store them as 4 operand pieces.
-template <int SRC>
-__device__ __forceinline__ void tiled_store_w(const GemmArgs& a, int64_t row, int64_t kk, uint32_t j, const WRegs& w,
-                                              u32x4* dst /* piece g at dst[16 * g] */)
-{
-    if (SRC == UW_W_BF16) {
-        dst[0] = w.v0;
-        dst[16] = w.v1;
-        dst[32] = w.v2;
-        dst[48] = w.v3;
-    } else if (SRC == UW_W_EXP) {
-        uint32_t ea, eb;
-        split_exps(w.v2.x, w.v2.y, ea, eb);
-        dst[0] = piece_from_split(ea, eb, w.v0.x, w.v0.y);
-        split_exps(w.v2.z, w.v2.w, ea, eb);
-        dst[16] = piece_from_split(ea, eb, w.v0.z, w.v0.w);
-        split_exps(w.v3.x, w.v3.y, ea, eb);
-        dst[32] = piece_from_split(ea, eb, w.v1.x, w.v1.y);
-        split_exps(w.v3.z, w.v3.w, ea, eb);
-        dst[48] = piece_from_split(ea, eb, w.v1.z, w.v1.w);
-    } else {
-        uint32_t ea[4], eb[4];
-        exps_from_idx(w.v2.x, a.pal, ea[0], eb[0]);
-        exps_from_idx(w.v2.y, a.pal, ea[1], eb[1]);
-        exps_from_idx(w.v2.z, a.pal, ea[2], eb[2]);
-        exps_from_idx(w.v2.w, a.pal, ea[3], eb[3]);
-        if ((w.bw >> (j & 31)) & 1u) {
-            const uint32_t ri = raw_index(a, row, j, w.bw);
-            const u32x4* e = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + (kk & 63));
-            const u32x4 e0 = e[0], e1 = e[1];
-            split_exps(e0.x, e0.y, ea[0], eb[0]);
-            split_exps(e0.z, e0.w, ea[1], eb[1]);
-            split_exps(e1.x, e1.y, ea[2], eb[2]);
-            split_exps(e1.z, e1.w, ea[3], eb[3]);
-        }
-        dst[0] = piece_from_split(ea[0], eb[0], w.v0.x, w.v0.y);
-        dst[16] = piece_from_split(ea[1], eb[1], w.v0.z, w.v0.w);
-        dst[32] = piece_from_split(ea[2], eb[2], w.v1.x, w.v1.y);
-        dst[48] = piece_from_split(ea[3], eb[3], w.v1.z, w.v1.w);
-    }
-}
 
 // blockIdx -> (n tile, m tile): consecutive hardware workgroups are dealt round-robin to
 // the 8 XCDs, so first regroup them so each XCD gets a contiguous run of logical tiles,
@@ -287,10 +459,12 @@ __device__ __forceinline__ void tile_of_block(uint32_t bid, uint32_t nblocks, ui
     tm = in_group / gsize;
 }
 
-template <int SRC, int BN, int BM>
+template <int SRC, bool CONTIG, int BN, int BM>
 __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 {
     using C = TiledCfg<BN, BM>;
+    constexpr bool RAW = SRC == UW_W_IDX;  // index plane: raw items found from the bitmap
+    constexpr bool DIRECT = SRC == UW_W_DIRECT;  // direct plane: raw rows from the block meta
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // stage st of the rebuilt W slice: As + st * A_VEC; of the X slice: Bs + st * B_VEC
     u32x4* const As = reinterpret_cast<u32x4*>(lds);
@@ -303,19 +477,35 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
     tile_of_block(blockIdx.x, gridDim.x, tiles_n, tiles_m, tn, tm);
     const int64_t n0 = static_cast<int64_t>(tn) * BN, m0 = static_cast<int64_t>(tm) * BM;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave >> 1, wm = wave & 1;
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
 
-    // item t of a slice: row R = t >> 1 inside the tile, k-half h = t & 1
+    // item t of a slice: row R = t >> 1 inside the tile, k-half h = t & 1 (32 weights =
+    // two 16-weight units, lane groups g = 2h and 2h + 1)
     int64_t wrow[C::WITEMS];
     int wdst[C::WITEMS];
+    Plane<SRC> wpl[C::WITEMS][2];
+    uint32_t bword[C::WITEMS], rbase[C::WITEMS];  // raw groups: current bitmap word, raw index at its start
+    const uint8_t* pmeta[C::WITEMS];               // direct plane: the item tile's meta row
+    u32x2 mcur[C::WITEMS], mnext[C::WITEMS];       // direct plane: meta of this step and the next
 #pragma unroll
     for (int it = 0; it < C::WITEMS; it++) {
         const int t = tid + 256 * it, R = t >> 1, h = t & 1;
         const int64_t rr = n0 + R;
-        wrow[it] = rr < a.N ? rr : a.N - 1;
-        wdst[it] = ((R >> 4) * 2 + h) * 64 + (R & 15);  // piece g adds 16 * g
+        wrow[it] = DIRECT ? rr : (rr < a.N ? rr : a.N - 1);
+        wdst[it] = ((R >> 4) * 2 + h) * 64 + (R & 15);  // piece q adds 16 * q
+        wpl[it][0] = Plane<SRC>(a, wrow[it], 2 * h);
+        wpl[it][1] = Plane<SRC>(a, wrow[it], 2 * h + 1);
+        bword[it] = 0;
+        rbase[it] = RAW ? a.row_base[wrow[it]] : 0;
+        if (DIRECT) {
+            int64_t tt = rr >> 4;
+            tt = tt < static_cast<int64_t>(a.tiles) ? tt : a.tiles - 1;
+            pmeta[it] = a.dmeta + 8 * tt * G;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it]);
+        }
     }
     const uint16_t* xsrc[C::XITEMS];
     bool xok[C::XITEMS];
@@ -335,13 +525,50 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 #pragma unroll
         for (int c = 0; c < C::TM; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    WRegs wr[C::WITEMS];
+    W16 wr[C::WITEMS][2];
+    u32x4 rsm[C::WITEMS][2], rex[C::WITEMS][2];  // true sign/mantissa + exponents of a raw item
+    bool israw[C::WITEMS];
     u32x4 xr[C::XITEMS][4];
+    // Issue every global load step j needs. The raw-group decision for step j uses the
+    // bitmap word fetched at the last multiple of 32, so a raw item's true data is
+    // requested here too, together with the rest, and never from the rebuild.
     auto load_step = [&](uint32_t j) {
 #pragma unroll
         for (int it = 0; it < C::WITEMS; it++) {
-            const int h = (tid + 256 * it) & 1;
-            tiled_load_w<SRC>(a, wrow[it], 64 * static_cast<int64_t>(j) + 32 * h, j, wr[it]);
+            if (RAW && (j & 31) == 0) {  // once every 32 steps, before this step's other loads
+                if (j) rbase[it] += __popc(bword[it]);
+                bword[it] = a.bitmap[wrow[it] * a.words + (j >> 5)];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::WITEMS; it++) {
+            wpl[it][0].load(j, wr[it][0]);
+            wpl[it][1].load(j, wr[it][1]);
+            if (DIRECT) {
+                // meta of step j arrived with the previous step; this step's raw exponents
+                // ride with its other loads, the next step's meta is requested now
+                const int R = (tid + 256 * it) >> 1, h = (tid + 256 * it) & 1;
+                mcur[it] = mnext[it];
+                israw[it] = (mcur[it].x >> (R & 15)) & 1u;
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+                    rex[it][q] = *raw_exp_addr(a, mcur[it], R & 15, 2 * h + q, wpl[it][q].p0 + 1536 * static_cast<int64_t>(j));
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
+            }
+            if (RAW) {
+                israw[it] = (bword[it] >> (j & 31)) & 1u;
+                if (israw[it]) {
+                    const int h = (tid + 256 * it) & 1;
+                    uint32_t ri = rbase[it] + __popc(bword[it] & ((1u << (j & 31)) - 1u));
+                    ri = ri < a.raw_max ? ri : a.raw_max;
+                    const u32x4* sp = reinterpret_cast<const u32x4*>(a.sm + wrow[it] * a.K + 64 * static_cast<int64_t>(j) + 32 * h);
+                    const u32x4* ep = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 32 * h);
+                    rsm[it][0] = sp[0];
+                    rsm[it][1] = sp[1];
+                    rex[it][0] = ep[0];
+                    rex[it][1] = ep[1];
+                }
+            }
         }
 #pragma unroll
         for (int it = 0; it < C::XITEMS; it++) {
@@ -357,11 +584,25 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
             }
         }
     };
-    auto store_step = [&](uint32_t j, int st) {
+    auto store_step = [&](int st) {
 #pragma unroll
         for (int it = 0; it < C::WITEMS; it++) {
-            const int h = (tid + 256 * it) & 1;
-            tiled_store_w<SRC>(a, wrow[it], 64 * static_cast<int64_t>(j) + 32 * h, j, wr[it], As + st * A_VEC + wdst[it]);
+            u32x4* dst = As + st * A_VEC + wdst[it];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                u32x4 p0, p1;
+                rebuild16<SRC, CONTIG>(a, wr[it][q], p0, p1);
+                if (DIRECT && israw[it]) rebuild16_raw(wr[it][q], rex[it][q], p0, p1);
+                if (RAW && israw[it]) {
+                    uint32_t ea, eb;
+                    split_exps(rex[it][q].x, rex[it][q].y, ea, eb);
+                    p0 = piece_from_split(ea, eb, rsm[it][q].x, rsm[it][q].y);
+                    split_exps(rex[it][q].z, rex[it][q].w, ea, eb);
+                    p1 = piece_from_split(ea, eb, rsm[it][q].z, rsm[it][q].w);
+                }
+                dst[16 * (2 * q)] = p0;
+                dst[16 * (2 * q + 1)] = p1;
+            }
         }
 #pragma unroll
         for (int it = 0; it < C::XITEMS; it++)
@@ -371,7 +612,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
     };
 
     load_step(0);
-    store_step(0, 0);
+    store_step(0);
     __syncthreads();
     for (uint32_t j = 0; j < G; j++) {
         const int st = j & 1;
@@ -388,7 +629,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 #pragma unroll
                 for (int c = 0; c < C::TM; c++) acc[i][c] = mfma16(af[i], bf[c], acc[i][c]);
         }
-        if (j + 1 < G) store_step(j + 1, st ^ 1);
+        if (j + 1 < G) store_step(st ^ 1);
         __syncthreads();
     }
 
@@ -416,14 +657,16 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 struct Variant {
     const char* name;
     int kind;  // 0 skinny, 1 tiled
-    int rt, wpb;
+    int rt, nw, u;
     int bn, bm;
 };
 
 const Variant kVariants[] = {
-    {"skinny rt1 w4", 0, 1, 4, 0, 0},   {"skinny rt1 w8", 0, 1, 8, 0, 0},  {"skinny rt1 w16", 0, 1, 16, 0, 0},
-    {"skinny rt2 w4", 0, 2, 4, 0, 0},   {"skinny rt2 w8", 0, 2, 8, 0, 0},  {"skinny rt2 w16", 0, 2, 16, 0, 0},
-    {"tiled 128x128", 1, 0, 0, 128, 128}, {"tiled 128x64", 1, 0, 0, 128, 64}, {"tiled 256x128", 1, 0, 0, 256, 128},
+    {"skinny rt1 u8 w4", 0, 1, 4, 8, 0, 0},  {"skinny rt1 u4 w8", 0, 1, 8, 4, 0, 0},
+    {"skinny rt1 u4 w4", 0, 1, 4, 4, 0, 0},  {"skinny rt2 u4 w4", 0, 2, 4, 4, 0, 0},
+    {"skinny rt2 u4 w8", 0, 2, 8, 4, 0, 0},  {"skinny rt4 u2 w4", 0, 4, 4, 2, 0, 0},
+    {"tiled 128x128", 1, 0, 0, 0, 128, 128}, {"tiled 128x64", 1, 0, 0, 0, 128, 64},
+    {"tiled 256x128", 1, 0, 0, 0, 256, 128},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -437,51 +680,55 @@ hipError_t allow_lds(const void* fn, size_t bytes, bool& done)
     return e;
 }
 
-template <int SRC, int CT, int RT>
-hipError_t launch_skinny_ct(const GemmArgs& g, int wpb, hipStream_t s)
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW>
+hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
-    const size_t lds = static_cast<size_t>(wpb) * RT * CT * 256 * 4;
+    constexpr size_t lds = static_cast<size_t>(NW) * RT * CT * 256 * 4;
     static bool attr_done = false;  // benign race: every writer stores the same value
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CT, RT>), 16 * RT * CT * 256 * 4, attr_done);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW>), lds, attr_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_skinny<SRC, CT, RT>), grid, dim3(64 * wpb), lds, s, g);
+    hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW>), grid, dim3(64 * NW), lds, s, g);
     return hipGetLastError();
 }
 
-template <int SRC, int RT>
-hipError_t launch_skinny_rt(const GemmArgs& g, int wpb, hipStream_t s)
+template <int SRC, bool CONTIG, int RT, int U, int NW>
+hipError_t launch_skinny_rt(const GemmArgs& g, hipStream_t s)
 {
     const int ct = static_cast<int>((g.M + 15) / 16);
     switch (ct) {
-    case 1: return launch_skinny_ct<SRC, 1, RT>(g, wpb, s);
-    case 2: return launch_skinny_ct<SRC, 2, RT>(g, wpb, s);
-    case 3: return launch_skinny_ct<SRC, 3, RT>(g, wpb, s);
-    default: return launch_skinny_ct<SRC, 4, RT>(g, wpb, s);
+    case 1: return launch_skinny_ct<SRC, CONTIG, 1, RT, U, NW>(g, s);
+    case 2: return launch_skinny_ct<SRC, CONTIG, 2, RT, U, NW>(g, s);
+    default: return launch_skinny_ct<SRC, CONTIG, 4, RT, U, NW>(g, s);
     }
 }
 
-template <int SRC, int BN, int BM>
+template <int SRC, bool CONTIG, int BN, int BM>
 hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
 {
     using C = TiledCfg<BN, BM>;
     static bool attr_done = false;  // benign race: every writer stores the same value
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_tiled<SRC, BN, BM>), C::LDS, attr_done);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_tiled<SRC, CONTIG, BN, BM>), C::LDS, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_tiled<SRC, BN, BM>), dim3(tiles), dim3(256), C::LDS, s, g);
+    hipLaunchKernelGGL((gemm_tiled<SRC, CONTIG, BN, BM>), dim3(tiles), dim3(256), C::LDS, s, g);
     return hipGetLastError();
 }
 
-template <int SRC>
+template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
     if (v.kind == 0) {
-        return v.rt == 1 ? launch_skinny_rt<SRC, 1>(g, v.wpb, s) : launch_skinny_rt<SRC, 2>(g, v.wpb, s);
+        if (v.rt == 1 && v.u == 8) return launch_skinny_rt<SRC, CONTIG, 1, 8, 4>(g, s);
+        if (v.rt == 1 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 1, 4, 8>(g, s);
+        if (v.rt == 1) return launch_skinny_rt<SRC, CONTIG, 1, 4, 4>(g, s);
+        if (v.rt == 2 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8>(g, s);
+        if (v.rt == 2) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4>(g, s);
+        return launch_skinny_rt<SRC, CONTIG, 4, 2, 4>(g, s);
     }
-    if (v.bn == 128 && v.bm == 128) return launch_tiled_t<SRC, 128, 128>(g, s);
-    if (v.bn == 128 && v.bm == 64) return launch_tiled_t<SRC, 128, 64>(g, s);
-    return launch_tiled_t<SRC, 256, 128>(g, s);
+    if (v.bn == 128 && v.bm == 128) return launch_tiled_t<SRC, CONTIG, 128, 128>(g, s);
+    if (v.bn == 128 && v.bm == 64) return launch_tiled_t<SRC, CONTIG, 128, 64>(g, s);
+    return launch_tiled_t<SRC, CONTIG, 256, 128>(g, s);
 }
 
 }  // namespace
@@ -491,10 +738,9 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
     (void)K;
     (void)src;
     if (M <= 64) {
-        const int64_t blocks = (N + 15) / 16;
-        if (blocks >= 2048) return 0;
-        if (blocks >= 512) return 1;
-        return 2;
+        const int64_t tiles = (N + 15) / 16;  // 16-row tiles
+        if (M > 16) return tiles >= 1024 ? 3 : 2;
+        return tiles >= 2048 ? 0 : tiles >= 512 ? 1 : 2;
     }
     return M <= 128 ? 7 : 6;
 }
@@ -512,7 +758,7 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     if (p->ldy < h->N) return fail(UW_EINVAL, "ldy must be >= N");
     if (!aligned(p->d_x, 16) || !aligned(p->d_y, 16) || !aligned(p->d_wplane, 16))
         return fail(UW_EINVAL, "device pointers must be 16-byte aligned");
-    if (p->src != UW_W_BF16 && p->src != UW_W_EXP && p->src != UW_W_IDX) return fail(UW_EINVAL, "bad src %d", p->src);
+    if (p->src < UW_W_BF16 || p->src > UW_W_DIRECT) return fail(UW_EINVAL, "bad src %d", p->src);
     int v = p->variant < 0 ? default_variant(h->N, h->K, p->M, p->src) : p->variant;
     if (v >= kNumVariants) return fail(UW_EINVAL, "variant %d out of range", v);
     if (!uw_variant_supports(v, h->N, h->K, p->M, p->src)) return fail(UW_EUNSUPPORTED, "variant %d does not support this problem", v);
@@ -526,6 +772,7 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     g.M = p->M;
     g.N = h->N;
     g.K = h->K;
+    bool contig = false;
     if (p->src != UW_W_BF16) {
         if (!p->d_blob) return fail(UW_EINVAL, "d_blob needed for this src");
         uw_status st = check_header(h, h->total_bytes);
@@ -539,14 +786,24 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
         g.words = h->bitmap_words;
         g.raw_max = h->n_raw > 0 ? static_cast<uint32_t>(h->n_raw - 1) : 0;
         std::memcpy(g.pal, h->palette, 16);
+        ValueOrder vo;
+        value_order(h, &vo);
+        std::memcpy(g.vpal, vo.sorted, 16);
+        g.base4 = vo.sorted[0] * 0x01010101u;
+        contig = vo.contiguous;
+        const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
+        g.tiles = static_cast<uint32_t>(T);
+        g.dmeta = static_cast<const uint8_t*>(p->d_wplane) + 1536 * T * G;
+        g.dside = g.dmeta + (8 * T * G + 63) / 64 * 64;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const Variant& var = kVariants[v];
     switch (p->src) {
-    case UW_W_BF16: e = launch_src<UW_W_BF16>(g, var, s); break;
-    case UW_W_EXP: e = launch_src<UW_W_EXP>(g, var, s); break;
-    default: e = launch_src<UW_W_IDX>(g, var, s); break;
+    case UW_W_BF16: e = launch_src<UW_W_BF16, false>(g, var, s); break;
+    case UW_W_EXP: e = launch_src<UW_W_EXP, false>(g, var, s); break;
+    case UW_W_IDX: e = launch_src<UW_W_IDX, false>(g, var, s); break;
+    default: e = contig ? launch_src<UW_W_DIRECT, true>(g, var, s) : launch_src<UW_W_DIRECT, false>(g, var, s); break;
     }
     if (e != hipSuccess) return fail(UW_EHIP, "GEMM launch failed: %s", hipGetErrorString(e));
     return UW_OK;

@@ -154,6 +154,20 @@ void canon_tables(const uw_header* h, CanonTables* t)
     t->n_used = idx;
 }
 
+void value_order(const uw_header* h, ValueOrder* v)
+{
+    const int n = static_cast<int>(std::min<uint32_t>(h->n_pal, 16));
+    std::memset(v, 0, sizeof *v);
+    for (int i = 0; i < n; i++) {
+        int below = 0;
+        for (int k = 0; k < n; k++) below += h->palette[k] < h->palette[i];
+        v->order[i] = static_cast<uint8_t>(below);
+        v->sorted[below] = h->palette[i];
+    }
+    v->contiguous = true;
+    for (int k = 1; k < n; k++) v->contiguous &= v->sorted[k] == v->sorted[0] + k;
+}
+
 uw_status check_header(const uw_header* h, size_t blob_bytes)
 {
     if (h->magic != kMagic) return fail(UW_EFORMAT, "bad magic 0x%08x", h->magic);

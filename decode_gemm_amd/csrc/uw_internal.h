@@ -23,6 +23,16 @@ struct CanonTables {
 };
 void canon_tables(const uw_header* h, CanonTables* t);
 
+// The palette sorted by exponent value: sorted[v] = v-th smallest palette exponent,
+// order[i] = position of palette[i] in that order; contiguous = the n_pal values are
+// consecutive integers (then exponent = sorted[0] + position).
+struct ValueOrder {
+    uint8_t sorted[16];
+    uint8_t order[16];
+    bool contiguous;
+};
+void value_order(const uw_header* h, ValueOrder* v);
+
 // Header-level checks shared by uw_inspect / uw_validate_header.
 uw_status check_header(const uw_header* h, size_t blob_bytes);
 
@@ -39,11 +49,12 @@ constexpr uint64_t kSectionAlign = 256;
 constexpr uint64_t kStreamSlack = 64;
 
 // Device-side launchers (uw_decode.hip, uw_gemm.hip).
-enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2 };
+enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2, DEC_DIRECT = 3 };
 uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err,
                         void* stream);
 uw_status launch_gemm(const uw_gemm_args* a, void* stream);
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
+uint64_t direct_plane_bytes(const uw_header* h);
 
 bool aligned(const void* p, size_t a);
 

@@ -74,4 +74,42 @@ __device__ __forceinline__ u32x4 piece_from_split(uint32_t ea, uint32_t eb, uint
     return r;
 }
 
+// ---- direct plane (see uw_prepare_direct): per 8-weight unit, one index dword whose
+// byte b holds weight b (low nibble) and weight b+4 (high nibble), and two dwords of
+// rearranged sign/mantissa bytes (mantissa << 1 | sign of the pair partner).
+
+// Two bf16 weights from [sm'_a, e_a, sm'_b, e_b]: rotating right by one bit moves each
+// mantissa into bits 0..6 / 16..22, each exponent into bits 7..14 / 23..30, and each
+// partner-sign bit into the other half's sign position.
+__device__ __forceinline__ uint32_t rotr1(uint32_t v) { return __builtin_rotateright32(v, 1); }
+
+// Exponent bytes [e0, e1, e2, e3] (lo) and [e4..e7] (hi) of one unit. CONTIG: the
+// value-sorted palette is a run of consecutive exponents starting at base (base4 =
+// base * 0x01010101), so exponent = base + index, a byte-wise add with no carries.
+// Otherwise two 8-entry byte lookups in the value-sorted palette vpal.
+template <bool CONTIG>
+__device__ __forceinline__ void unit_exps(uint32_t idx, uint32_t base4, const uint32_t* vpal, uint32_t& lo, uint32_t& hi)
+{
+    const uint32_t x = idx & 0x0F0F0F0Fu, y = (idx >> 4) & 0x0F0F0F0Fu;
+    if (CONTIG) {
+        lo = x + base4;
+        hi = y + base4;
+    } else {
+        lo = palette_lookup(x & 0x07070707u, byte_mask_bit7(x << 4), vpal);
+        hi = palette_lookup(y & 0x07070707u, byte_mask_bit7(y << 4), vpal);
+    }
+}
+
+// 8 bf16 weights (one MFMA operand piece) of a unit from its exponent dwords (natural
+// order) and its two sign/mantissa dwords.
+__device__ __forceinline__ u32x4 unit_piece(uint32_t e_lo, uint32_t e_hi, uint32_t s_lo, uint32_t s_hi)
+{
+    u32x4 r;
+    r.x = rotr1(__builtin_amdgcn_perm(e_lo, s_lo, 0x05010400u));  // [s0, e0, s1, e1]
+    r.y = rotr1(__builtin_amdgcn_perm(e_lo, s_lo, 0x07030602u));  // [s2, e2, s3, e3]
+    r.z = rotr1(__builtin_amdgcn_perm(e_hi, s_hi, 0x05010400u));
+    r.w = rotr1(__builtin_amdgcn_perm(e_hi, s_hi, 0x07030602u));
+    return r;
+}
+
 }  // namespace uw

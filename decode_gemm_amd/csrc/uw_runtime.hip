@@ -74,7 +74,7 @@ using namespace uw;
 
 extern "C" {
 
-uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob, const uint8_t* d_idx,
+uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob, const uint8_t* d_direct,
                           int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y, int64_t ldy, void* d_ws,
                           size_t ws_bytes, uint32_t* d_err, void* stream)
 {
@@ -111,9 +111,9 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
         g.d_wplane = d_ws;
         break;
     case UW_PIPE_DIRECT:
-        if (!d_idx) return fail(UW_EINVAL, "direct palette needs the index plane");
-        g.src = UW_W_IDX;
-        g.d_wplane = d_idx;
+        if (!d_direct) return fail(UW_EINVAL, "direct palette needs the direct plane (uw_prepare_direct)");
+        g.src = UW_W_DIRECT;
+        g.d_wplane = d_direct;
         break;
     default: return fail(UW_EINVAL, "unknown pipeline %d", pipeline);
     }
@@ -147,11 +147,11 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
             best.reserved = 0;
             for (int p = 0; p < 4 && result == UW_OK; p++) {
                 if (!(pmask >> p & 1u)) continue;
-                if (p == UW_PIPE_DIRECT && !a->d_idx) continue;
+                if (p == UW_PIPE_DIRECT && !a->d_direct) continue;
                 size_t need = 0;
                 uw_workspace_bytes(h, p, &need);
                 if (need > a->ws_bytes) continue;
-                const int32_t src = p == UW_PIPE_FULL ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP : UW_W_IDX;
+                const int32_t src = p == UW_PIPE_FULL ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP : p == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
                 for (int v = 0; v < uw_variant_count() && result == UW_OK; v++) {
                     if (!(vmask >> v & 1u) || !uw_variant_supports(v, h->N, h->K, M, src)) continue;
                     std::vector<float> t;
@@ -160,7 +160,7 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
                             if ((result = scrub(a->d_scrub, a->scrub_bytes, static_cast<uint32_t>(r), s)) != UW_OK) break;
                         }
                         if (r >= warmup && hipEventRecord(e0, s) != hipSuccess) { result = fail(UW_EHIP, "event record failed"); break; }
-                        uw_status st = uw_run_pipeline(p, v, h, a->d_blob, a->d_idx, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
+                        uw_status st = uw_run_pipeline(p, v, h, a->d_blob, a->d_direct, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
                                                        a->ws_bytes, nullptr, stream);
                         if (st != UW_OK) { result = st; break; }
                         if (r >= warmup) {

@@ -154,6 +154,37 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
                                void* stream);
 
 /*
+ * uw_prepare_direct (device). The load-time preparation of the direct-palette pipeline
+ * ("Four ways to use compressed weights": weights are transcoded once at model load
+ * into a compact 4-bit palette form that the matmul consumes with no per-call
+ * preprocessing). Decodes the Huffman stream into the direct plane d_direct
+ * (uw_direct_plane_bytes, 16-byte aligned), laid out for the reconstructive GEMM's
+ * operand registers. With T = ceil(N/16) row tiles and G = K/64 groups:
+ *   blocks  T*G blocks of 1536 bytes, block (t, j) at 1536*(t*G + j). Lane l = 16*g + r
+ *           (g = 0..3, r = 0..15) of the MFMA operand owns row 16t+r, weights
+ *           64j+16g .. 64j+16g+15:
+ *             bytes 16l .. 16l+15    weight x: (mantissa_x << 1) | sign of weight x^1
+ *                                    (each byte keeps its own mantissa and its pair
+ *                                    partner's sign, so two bf16 weights are one byte
+ *                                    permute and one rotate)
+ *             bytes 1024+8l .. +7    two index dwords, one per 8-weight unit; byte b of
+ *                                    a unit dword holds unit weight b in its low nibble
+ *                                    and weight b+4 in its high nibble
+ *           The index is the position of the weight's exponent in the palette sorted by
+ *           exponent value (ascending); in a raw group it is 0 and the sign/mantissa
+ *           bytes are still those of the weights. Rows >= N are zero.
+ *   meta    at 1536*T*G: per block two u32: a mask whose bit r says row 16t+r's group j
+ *           is raw, and the side-table index of the block's first raw row.
+ *   side    at 1536*T*G + round_up(8*T*G, 64) (the bytes in between are zero): 64
+ *           exponent bytes per raw (row, group), ordered by tile, then group, then row.
+ * A wave therefore reads one contiguous kilobyte per operand load, and a raw row only
+ * swaps in its verbatim exponents. d_err as for the decoders.
+ */
+uw_status uw_prepare_direct(const uw_header* h, const void* d_blob, uint8_t* d_direct, uint32_t* d_err, void* stream);
+/* Bytes of the direct plane of a blob: 1536*T*G + round_up(8*T*G, 64) + 64*n_raw. */
+uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out);
+
+/*
  * uw_recon_gemm (device). Y = X * W^T with W taken from one of three planes ("How the
  * reconstructive matmul works"): the bf16 weights themselves (plain GEMM of the
  * full-decode pipeline), the exponent plane plus the blob's sign/mantissa plane, or the
@@ -161,7 +192,7 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
  * groups. Weights are rebuilt in registers / LDS and fed to bf16 MFMA; they are never
  * written to memory. Accumulation is fp32; Y is overwritten (not accumulated into).
  */
-typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2 } uw_wsrc;
+typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2, UW_W_DIRECT = 3 } uw_wsrc;
 
 typedef struct {
     int64_t M;             /* rows of X and Y; 0 is a no-op */
@@ -170,7 +201,8 @@ typedef struct {
     const uw_header* h;    /* N, K, palette */
     const void* d_blob;    /* device blob (sm plane, raw tables); unused for UW_W_BF16 */
     int32_t src;           /* uw_wsrc */
-    const void* d_wplane;  /* bf16 W [N][K] | exponent plane [N][K] | index plane [N*K/2] */
+    const void* d_wplane;  /* bf16 W [N][K] | exponent plane [N][K] | index plane [N*K/2] |
+                              direct plane (uw_prepare_direct) */
     float* d_y;            /* Y fp32 [M][ldy], 16-byte aligned */
     int64_t ldy;           /* >= N */
     int32_t variant;       /* kernel variant id, -1 = default for (N, K, M) */
@@ -191,7 +223,8 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
  *   UW_PIPE_FULL      uw_decode_full into workspace, then plain bf16 GEMM
  *   UW_PIPE_EXP       uw_decode_exponent into workspace, then reconstructive GEMM
  *   UW_PIPE_TRANSCODE uw_transcode_palette into workspace, then reconstructive GEMM
- *   UW_PIPE_DIRECT    reconstructive GEMM on an index plane prepared once at load
+ *   UW_PIPE_DIRECT    reconstructive GEMM on the direct plane prepared once at load
+ *                     (uw_prepare_direct)
  */
 typedef enum { UW_PIPE_FULL = 0, UW_PIPE_EXP = 1, UW_PIPE_TRANSCODE = 2, UW_PIPE_DIRECT = 3 } uw_pipeline;
 
@@ -209,9 +242,10 @@ typedef struct {
 uw_status uw_workspace_bytes(const uw_header* h, int32_t pipeline, size_t* out);
 
 /* Run one pipeline end to end on `stream`: decode into d_ws if the pipeline needs it,
- * then the GEMM. d_idx = the persistent palette-index plane (UW_PIPE_DIRECT only). */
+ * then the GEMM. d_direct = the direct plane from uw_prepare_direct (UW_PIPE_DIRECT
+ * only). */
 uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob,
-                          const uint8_t* d_idx, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
+                          const uint8_t* d_direct, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
                           int64_t ldy, void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream);
 
 /*
@@ -219,7 +253,7 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
  * variant) pair on the caller's buffers with HIP events (warmup untimed launches, then
  * the median of reps timed ones) and return the fastest in out[i] ("Why no single
  * pipeline wins", "Sharing the GPU between decode and compute": measured, not
- * heuristic). d_idx may be NULL, in which case UW_PIPE_DIRECT is not a candidate.
+ * heuristic). d_direct may be NULL, in which case UW_PIPE_DIRECT is not a candidate.
  * d_x must hold max(Ms) rows of K bf16, d_y max(Ms) rows of N fp32, and d_ws at least
  * the largest uw_workspace_bytes of the candidate pipelines (smaller workspaces drop
  * the pipelines that do not fit). Blocks until the measurements finish.
@@ -227,7 +261,7 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
 typedef struct {
     const uw_header* h;
     const void* d_blob;
-    const uint8_t* d_idx; /* persistent palette-index plane or NULL */
+    const uint8_t* d_direct; /* direct plane (uw_prepare_direct) or NULL */
     const uint16_t* d_x;  /* [max M][K] bf16 */
     float* d_y;           /* [max M][N] fp32 */
     void* d_ws;

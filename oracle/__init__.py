@@ -72,6 +72,9 @@ def _load():
         lib.or_gemm_pairs.argtypes = [P, i64, P, i64, i64, P, P, i64, P, P]
         lib.or_gemm.argtypes = [P, P, i64, i64, i64, P, P]
         lib.or_swiglu.argtypes = [P, P, i64, P]
+        lib.or_direct_plane.argtypes = [P, i64, i64, P]
+        lib.or_direct_plane_bytes.argtypes = [i64, i64, i64]
+        lib.or_direct_plane_bytes.restype = u64
         lib.or_f64_to_bf16.argtypes = [ctypes.c_double]
         lib.or_f64_to_bf16.restype = ctypes.c_uint16
         _lib = lib
@@ -227,6 +230,22 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     h = np.empty(g.shape, np.uint16)
     _load().or_swiglu(_p(g), _p(u), g.size, _p(h))
     return h
+
+
+def direct_plane_bytes(N: int, K: int, n_raw: int) -> int:
+    return int(_load().or_direct_plane_bytes(N, K, n_raw))
+
+
+def direct_plane(w: np.ndarray) -> np.ndarray:
+    """The direct-palette plane of W (tile-major blocks, meta, raw side table), see oracle.c."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    N, K = w.shape
+    _, e = split(w)
+    pal, _ = palette(e)
+    _, row_base, _ = raw_groups(e, pal)
+    out = np.zeros(direct_plane_bytes(N, K, int(row_base[-1])), np.uint8)
+    _load().or_direct_plane(_p(w), N, K, _p(out))
+    return out
 
 
 def f64_to_bf16(x: float) -> int:

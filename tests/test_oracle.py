@@ -492,3 +492,66 @@ def test_swiglu_against_expit():
         for nb in (b - 1, b + 1):
             if 0 <= nb < 0x10000 and (nb & 0x7F80) != 0x7F80 and (nb ^ b) < 0x8000:
                 assert abs(float(synth.bf16_bits_to_f32(np.array([nb]))[0]) - ref[i]) >= abs(hf[i] - ref[i])
+
+
+# ---------------------------------------------------------------- direct plane
+def _rebuild_from_direct(plane, pal_sorted, N, K):
+    """Invert the direct-plane layout as the format text states it (independent code):
+    in block (t, j), lane l = 16g + r holds row 16t+r, weights 64j+16g..+15; weight x
+    takes its mantissa from bits 1..7 of its byte, its sign from bit 0 of the byte of
+    weight x^1, and its exponent from the value-sorted palette via its nibble, or, when
+    bit r of the block's meta mask is set, from the side table."""
+    T, G = (N + 15) // 16, K // 64
+    nb = 1536 * T * G
+    blocks = plane[:nb].reshape(T, G, 1536)
+    meta = plane[nb : nb + 8 * T * G].view("<u4").reshape(T, G, 2)
+    side = plane[nb + (8 * T * G + 63) // 64 * 64 :].reshape(-1, 64)
+    out = np.zeros((T * 16, K), np.uint16)
+    for t in range(T):
+        for j in range(G):
+            blk = blocks[t, j]
+            mask, base = int(meta[t, j, 0]), int(meta[t, j, 1])
+            k = 0
+            for r in range(16):
+                raw = mask >> r & 1
+                for g in range(4):
+                    l = 16 * g + r
+                    smb = blk[16 * l : 16 * l + 16].astype(np.uint16)
+                    units = blk[1024 + 8 * l : 1024 + 8 * l + 8]
+                    idx = np.concatenate([units[0:4] & 15, units[0:4] >> 4, units[4:8] & 15, units[4:8] >> 4])
+                    e = np.asarray(pal_sorted, np.uint16)[idx]
+                    if raw:
+                        e = side[base + k, 16 * g : 16 * g + 16].astype(np.uint16)
+                    sign = (smb & 1)[np.arange(16) ^ 1]
+                    out[16 * t + r, 64 * j + 16 * g : 64 * j + 16 * g + 16] = (sign << 15) | (e << 7) | (smb >> 1)
+                k += raw
+    return out[:N]
+
+
+def test_direct_plane_roundtrip_and_hand_block(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "hand_stream.json")))
+    w, sm = _hand_matrix(g)
+    d = oracle.direct_plane(w)
+    assert d.size == 1536 + 64  # one block, meta rounded up to 64 bytes, no raw group
+    # by hand: value-sorted palette [119, 120, 121, 122]; weights 0..31 -> index 1,
+    # 32..47 -> 2, 48..55 -> 0, 56..63 -> 3. Lane l = 16g (row 0) holds weights 16g..16g+15;
+    # its two unit dwords pair weight b with b+4 in each byte.
+    lanes = {0: [0x11] * 8, 16: [0x11] * 8, 32: [0x22] * 8, 48: [0x00] * 4 + [0x33] * 4}
+    for l, exp in lanes.items():
+        assert d[1024 + 8 * l : 1024 + 8 * l + 8].tolist() == exp
+    # rows 1..15 of the tile do not exist: their bytes are zero
+    assert not d[16 * 1 : 16 * 16].any() and not d[1024 + 8 : 1024 + 8 * 16].any()
+    # weight 4 (sm 148: sign 1, mantissa 20) keeps its mantissa and weight 5's sign (sm 185: 1)
+    assert d[4] == (20 << 1) | 1 and d[5] == (57 << 1) | 1 and d[0] == 0
+    assert d[1536:1544].tolist() == [0] * 8
+    assert (_rebuild_from_direct(d, [119, 120, 121, 122], 1, 64) == w).all()
+    # a matrix with raw groups, 16 palette entries and a ragged last tile
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.gen_weight(cfg, "w")[:200]
+    N, K = w.shape
+    d = oracle.direct_plane(w)
+    _, e = oracle.split(w)
+    pal, _ = oracle.palette(e)
+    _, row_base, raw = oracle.raw_groups(e.reshape(N, K), pal)
+    assert len(raw) > 0 and d.size == oracle.direct_plane_bytes(N, K, len(raw))
+    assert (_rebuild_from_direct(d, sorted(pal.tolist()), N, K) == w).all()
