@@ -46,27 +46,45 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(h, M, pipeline):
-    """HBM bytes a pipeline must move per forward: its resident compressed input, X and Y,
-    plus the preprocessing plane it writes and reads back (none for direct palette)."""
+def section_bytes(h):
+    """Bytes of each section of the Huffman-format blob."""
     N, K = h.N, h.K
-    side = 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw  # raw-group tables
-    xy = 2 * M * K + 4 * M * N
-    if pipeline == 3:  # direct palette: the load-time direct plane (blocks, meta, raw side table)
-        T, G = (N + 15) // 16, K // 64
-        return 1536 * T * G + (8 * T * G + 63) // 64 * 64 + 64 * h.n_raw + xy
-    huff = N * K + side + 4 * (h.n_chunks + 1) + h.bytes_stream  # Huffman-format blob
-    plane = {0: 2 * N * K, 1: N * K, 2: N * K // 2}[pipeline]
-    gemm_in = {0: 2 * N * K, 1: 2 * N * K + side, 2: N * K + N * K // 2 + side}[pipeline]
-    return huff + plane + gemm_in + xy
+    return {"sm": N * K, "stream": h.bytes_stream, "offs": 4 * (h.n_chunks + 1), "bitmap": 4 * N * h.bitmap_words,
+            "row_base": 4 * (N + 1), "raw": 64 * h.n_raw}
+
+
+def direct_bytes(h):
+    """Bytes of the load-time direct-palette plane (blocks, meta, raw side table)."""
+    T, G = (h.N + 15) // 16, h.K // 64
+    return 1536 * T * G + (8 * T * G + 63) // 64 * 64 + 64 * h.n_raw
+
+
+def decode_bytes(h, mode):
+    """HBM bytes a decoder must read and write: the blob sections it consumes and its output."""
+    s = section_bytes(h)
+    NK = h.N * h.K
+    codes = s["stream"] + s["offs"] + s["bitmap"]
+    return {"full": s["sm"] + codes + s["row_base"] + s["raw"] + 2 * NK,
+            "exp": codes + s["row_base"] + s["raw"] + NK,
+            "idx": codes + NK // 2,
+            "direct": s["sm"] + codes + s["row_base"] + s["raw"] + direct_bytes(h)}[mode]
 
 
 def gemm_bytes(h, M, src):
-    """HBM bytes of the GEMM kernel alone (its own inputs and output)."""
-    N, K = h.N, h.K
-    side = 4 * N * h.bitmap_words + 4 * (N + 1) + 64 * h.n_raw
-    w = {0: 2 * N * K, 1: 2 * N * K, 2: N * K + N * K // 2 + side}[src]
-    return w + 2 * M * K + 4 * M * N
+    """HBM bytes of the GEMM kernel alone: its weight planes, X and Y."""
+    s = section_bytes(h)
+    NK = h.N * h.K
+    w = {0: 2 * NK, 1: 2 * NK, 2: NK // 2 + NK + s["bitmap"] + s["row_base"] + s["raw"], 3: direct_bytes(h)}[src]
+    return w + 2 * M * h.K + 4 * M * h.N
+
+
+def algorithmic_bytes(h, M, pipeline):
+    """HBM bytes a pipeline must move per forward: the decoder's reads and writes (none for
+    direct palette, whose plane is made at load) plus the GEMM's."""
+    if pipeline == 3:
+        return gemm_bytes(h, M, 3)
+    mode, src = {0: ("full", 0), 1: ("exp", 1), 2: ("idx", 2)}[pipeline]
+    return decode_bytes(h, mode) + gemm_bytes(h, M, src)
 
 
 def main():
@@ -201,6 +219,7 @@ def main():
                     "uncompressed_GBs": round(2 * N * K / (us * 1e-6) / 1e9, 1),
                     "hbm_frac_compressed": round(algorithmic_bytes(h, M, p) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         detail["pipelines"] = pip
+        detail["decoders"] = decoder_detail(uw, torch, h, blobs, stream, log)
         large_m = large_m_line(uw, synth, torch, dev, stream, log)
 
     cpu = None
@@ -230,6 +249,38 @@ def main():
         "large_m": large_m,
     }
     print(json.dumps(out))
+
+
+def decoder_detail(uw, torch, h, blobs, stream, log):
+    """Each decoder alone on rotated copies of the gate blob: median time, the bytes it must
+    move, and the fraction of the HBM roof that rate is."""
+    N, K = h.N, h.K
+    outs = {"full": torch.empty(2 * N * K, dtype=torch.uint8, device=blobs[0].device),
+            "exp": torch.empty(N * K, dtype=torch.uint8, device=blobs[0].device),
+            "idx": torch.empty(N * K // 2, dtype=torch.uint8, device=blobs[0].device),
+            "direct": torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=blobs[0].device)}
+    fns = {"full": lambda b, o: uw.decode_full(h, b, o, stream=stream),
+           "exp": lambda b, o: uw.decode_exponent(h, b, o, stream=stream),
+           "idx": lambda b, o: uw.transcode_palette(h, b, o, stream=stream),
+           "direct": lambda b, o: uw.prepare_direct(h, b, o, stream=stream)}
+    res = {}
+    R = len(blobs)
+    for mode, fn in fns.items():
+        fn(blobs[0], outs[mode])
+        ts = []
+        for r in range(3 * R):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(blobs[r % R], outs[mode])
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+        nbytes = decode_bytes(h, mode)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[mode] = {"us": round(us, 2), "bytes": int(nbytes), "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] decoders: {res}")
+    return res
 
 
 def large_m_line(uw, synth, torch, dev, stream, log):

@@ -10,6 +10,7 @@ Importing this package loads libuw.so and raises ImportError if it has not been 
 from __future__ import annotations
 
 import ctypes
+import importlib.util
 import os
 
 import numpy as np
@@ -80,9 +81,25 @@ class TuneArgs(ctypes.Structure):
     ]
 
 
+def _preload_torch_hip():
+    """Load the HIP runtime that PyTorch ships, if PyTorch is installed, before libuw.so.
+
+    A process can drive the GPU through one HIP runtime only, and the tensors handed to
+    libuw come from PyTorch's. With PyTorch's copy already loaded, libuw's dependency on
+    libamdhip64 resolves to it whatever the import order; otherwise the system copy would
+    be loaded first and the second runtime to start would find no device."""
+    spec = importlib.util.find_spec("torch")
+    for d in (spec.submodule_search_locations or []) if spec else []:
+        path = os.path.join(d, "lib", "libamdhip64.so")
+        if os.path.exists(path):
+            ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+            return
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libuw.so not built at {LIB_PATH}; run `python -m decode_gemm_amd.build`")
+    _preload_torch_hip()
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
     H = ctypes.POINTER(Header)

@@ -15,9 +15,12 @@
 // instruction covers whole 64..128-byte segments instead of 64 scattered bytes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "uw_internal.h"
+#include "uw_recon.h"
 
 namespace uw {
 
@@ -26,9 +29,6 @@ namespace {
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kPitch = 17;       // dwords per lane row of the staging tile (16 + 1 pad)
 constexpr int kStageDwords = kWaves * 64 * kPitch;
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
     const uint8_t* sm;
@@ -248,10 +248,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
     }
 }
 
-// Direct plane, second part: one thread per 16-row tile walks the tile's groups in
-// order and writes, per (tile, group), the mask of raw rows and the side-table index of
-// its first raw row, copies those rows' verbatim exponents from the blob's raw table into
-// the side table (ordered by tile, group, row), and zeroes the block bytes of rows past N.
+// Direct plane, second part: one wave per 16-row tile, lane j per 64-weight group. Per
+// (tile, group) it writes the mask of raw rows and the side-table index of the first raw
+// row, copies those rows' verbatim exponents from the blob's raw table into the side
+// table (ordered by tile, group, row), and zeroes the block bytes of rows past N.
 struct MetaArgs {
     const uint32_t* bitmap;
     const uint32_t* row_base;
@@ -263,62 +263,596 @@ struct MetaArgs {
     uint32_t T, words, raw_max;
 };
 
+__device__ inline uint32_t lanes_below(uint64_t ballot, uint32_t lane)
+{
+    return __popcll(ballot & ((1ull << lane) - 1ull));
+}
+
 __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
 {
-    const uint32_t t = blockIdx.x * 256 + threadIdx.x;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (t >= a.T) return;
-    if (t == 0) {  // zero the padding between the meta entries and the side table
+    if (t == 0 && lane == 0) {  // zero the padding between the meta entries and the side table
         uint8_t* pad = reinterpret_cast<uint8_t*>(a.meta + 2 * static_cast<int64_t>(a.T) * a.G);
         for (uint8_t* q = pad; q < a.side; q++) *q = 0;
     }
     const int64_t row0 = 16 * static_cast<int64_t>(t);
-    uint32_t running = a.row_base[row0 < a.N ? row0 : a.N];
-    uint32_t rb[16], cnt[16];
+    const int nrows = static_cast<int>(a.N - row0 < 16 ? a.N - row0 : 16);
+    uint32_t running = a.row_base[row0];  // raw groups in rows before the tile
+    uint32_t rb[16], carry[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        rb[r] = row0 + r < a.N ? a.row_base[row0 + r] : 0;
-        cnt[r] = 0;
+        rb[r] = r < nrows ? a.row_base[row0 + r] : 0;
+        carry[r] = 0;
     }
-    for (uint32_t wd = 0; wd < a.words; wd++) {
-        uint32_t bw[16];
+    for (int64_t jb = 0; jb < a.G; jb += 64) {
+        const int64_t j = jb + lane;
+        const bool valid = j < a.G;
+        uint32_t mask = 0;
 #pragma unroll
-        for (int r = 0; r < 16; r++) bw[r] = row0 + r < a.N ? a.bitmap[(row0 + r) * a.words + wd] : 0;
-        const int64_t jend = (32 * static_cast<int64_t>(wd) + 32) < a.G ? 32 * static_cast<int64_t>(wd) + 32 : a.G;
-        for (int64_t j = 32 * static_cast<int64_t>(wd); j < jend; j++) {
-            uint32_t mask = 0;
+        for (int r = 0; r < 16; r++) {
+            if (valid && r < nrows) mask |= ((a.bitmap[(row0 + r) * a.words + (j >> 5)] >> (j & 31)) & 1u) << r;
+        }
+        // exclusive prefix of the per-lane raw counts (<= 16, five bits) over the wave
+        const uint32_t cnt = __popc(mask);
+        uint32_t prefix = 0, total = 0;
 #pragma unroll
-            for (int r = 0; r < 16; r++) mask |= ((bw[r] >> (j & 31)) & 1u) << r;
+        for (int b = 0; b < 5; b++) {
+            const uint64_t bal = __ballot((cnt >> b) & 1u);
+            prefix += lanes_below(bal, lane) << b;
+            total += static_cast<uint32_t>(__popcll(bal)) << b;
+        }
+        const uint32_t first = running + prefix;
+        if (valid) {
             uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
             m[0] = mask;
-            m[1] = running;
+            m[1] = first;
+        }
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                if ((mask >> r) & 1u) {
-                    uint32_t ri = rb[r] + cnt[r];
-                    ri = ri < a.raw_max ? ri : a.raw_max;
-                    const u32x4* src = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64);
-                    u32x4* dst = reinterpret_cast<u32x4*>(a.side + static_cast<uint64_t>(running) * 64);
-                    dst[0] = src[0];
-                    dst[1] = src[1];
-                    dst[2] = src[2];
-                    dst[3] = src[3];
-                    running++;
-                    cnt[r]++;
+        for (int r = 0; r < 16; r++) {
+            const bool bit = (mask >> r) & 1u;
+            const uint64_t bal = __ballot(bit);
+            if (bit) {
+                uint32_t ri = rb[r] + carry[r] + lanes_below(bal, lane);
+                ri = ri < a.raw_max ? ri : a.raw_max;
+                const uint32_t dst = first + __popc(mask & ((1u << r) - 1u));
+                const u32x4* src = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64);
+                u32x4* out = reinterpret_cast<u32x4*>(a.side + static_cast<uint64_t>(dst) * 64);
+                out[0] = src[0];
+                out[1] = src[1];
+                out[2] = src[2];
+                out[3] = src[3];
+            }
+            carry[r] += static_cast<uint32_t>(__popcll(bal));
+        }
+        running += total;
+        if (valid && nrows < 16) {  // last tile: rows past N are zero
+            uint8_t* blk = a.blocks + 1536 * (static_cast<int64_t>(t) * a.G + j);
+            for (int r = nrows; r < 16; r++)
+                for (int g = 0; g < 4; g++) {
+                    *reinterpret_cast<u32x4*>(blk + 16 * (16 * g + r)) = u32x4{0, 0, 0, 0};
+                    *reinterpret_cast<u32x2*>(blk + 1024 + 8 * (16 * g + r)) = u32x2{0, 0};
                 }
-            }
-            if (row0 + 16 > a.N) {  // last tile: rows past N are zero
-                uint8_t* blk = a.blocks + 1536 * (static_cast<int64_t>(t) * a.G + j);
-                for (int r = static_cast<int>(a.N - row0); r < 16; r++)
-                    for (int g = 0; g < 4; g++) {
-                        *reinterpret_cast<u32x4*>(blk + 16 * (16 * g + r)) = u32x4{0, 0, 0, 0};
-                        *reinterpret_cast<u32x2*>(blk + 1024 + 8 * (16 * g + r)) = u32x2{0, 0};
-                    }
-            }
         }
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Table-driven decoder for lmax <= 12 and chunks of at most 2048 elements.
+//
+// Workgroups are persistent (one per CU). Each owns two tables in LDS, indexed by the
+// next lmax stream bits: a single-code table (length | value) and a multi-code table
+// whose entry holds every whole code that starts those bits, up to six: their values
+// (4 bits each), their count and their total length. One table read then advances a
+// lane by ~4 symbols on these exponent statistics instead of one.
+//
+// A wave takes 64 consecutive chunks (one per lane) as a task. It copies the stream
+// words those chunks span (their bit offsets bound the span) into an LDS window with
+// coalesced 16-byte loads, so the bit reader refills from LDS; a span larger than the
+// window is read from global memory instead (the same code instantiated twice, chosen per
+// wave). Everything a task reads before decoding (bit offsets, bitmap words, the window)
+// is loaded during the previous task. Each lane decodes the symbols of its chunk's
+// non-raw groups, up to 256 weights per segment, into a nibble buffer in LDS: multi-code
+// steps while six more symbols fit, then single codes. The wave then writes the segment's
+// outputs cooperatively, taking raw groups from the blob's raw table.
+//
+// The workgroup size is chosen per launch so that every wave gets the same number of
+// tasks (the last round would otherwise run on a fraction of the waves).
+namespace lut {
+
+constexpr uint32_t kMaxWaves = 8;          // waves per workgroup at most
+constexpr int kWinWords = 1792;            // stream window per wave (7 KB)
+constexpr int kWinLoads = kWinWords / 256; // 16-byte loads per lane to fill it
+constexpr int kSegElems = 256;             // weights per lane per segment (four groups)
+constexpr int kSymPitch = kSegElems / 8 + 1;
+constexpr int kInfo = 128;                 // per-wave lane info: raw mask, raw-table base
+constexpr int kWaveDwords = kWinWords + 64 * kSymPitch + kInfo;
+constexpr int kLutEntries = 4096;          // multi-code table, u32 entries
+constexpr int kT1Dwords = 1024;            // single-code table, u8 entries
+constexpr uint32_t kMaxSyms = 6;
+constexpr uint32_t kMaxChunk = 2048;
+
+constexpr size_t lds_bytes(uint32_t waves) { return 4u * (kLutEntries + kT1Dwords + waves * kWaveDwords); }
+
+struct Args {
+    const uint8_t* sm;
+    const uint32_t* bitmap;
+    const uint32_t* row_base;
+    const uint8_t* raw;
+    const uint32_t* offs;
+    const uint32_t* stream;
+    uint8_t* out;
+    uint32_t* err;
+    uint32_t K, Gr, words, chunk, n_chunks, n_tasks, n_elems;
+    uint32_t lmax, n_words, raw_max;
+    uint32_t simple;     // chunk is a power of two dividing K: a chunk's groups share one bitmap word
+    uint32_t ranges[16];  // canonical rank r: first entry | length << 16 | value << 20 (length 0: unused)
+    uint32_t pal[4];      // palette exponents (byte i = exponent of index i)
+};
+
+// Multi-code entry: values in bits 0..23, total length 24..27, count 28..30, bit 31 set
+// when the bits start no code (then count 1, length lmax, value 0).
+__device__ __forceinline__ uint32_t ent_len(uint32_t e) { return (e >> 24) & 15u; }
+__device__ __forceinline__ uint32_t ent_n(uint32_t e) { return (e >> 28) & 7u; }
+constexpr uint32_t kEntErr = 0x80000000u;
+
+
+// Exponent bytes of four palette indices held one per byte (values 0..15).
+__device__ __forceinline__ uint32_t pal4(uint32_t idx4, const uint32_t* pal)
+{
+    return palette_lookup(idx4 & 0x07070707u, byte_mask_bit7(idx4 << 4), pal);
+}
+
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Sum over the wave of v (< 64).
+__device__ __forceinline__ uint32_t wave_sum6(uint32_t v)
+{
+    uint32_t s = 0;
+#pragma unroll
+    for (int b = 0; b < 6; b++) s += static_cast<uint32_t>(__popcll(__ballot((v >> b) & 1u))) << b;
+    return s;
+}
+
+// Sum of v (< 64) over the lanes below this one.
+__device__ __forceinline__ uint32_t wave_prefix6(uint32_t v, uint32_t lane)
+{
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t s = 0;
+#pragma unroll
+    for (int b = 0; b < 6; b++) s += static_cast<uint32_t>(__popcll(__ballot((v >> b) & 1u) & below)) << b;
+    return s;
+}
+
+// Stream word i, from the wave's LDS window (words from wa on) or from global memory.
+template <bool IN_LDS>
+__device__ __forceinline__ uint32_t read_word(const Args& a, const uint32_t* win, uint32_t wa, uint32_t i)
+{
+    if (IN_LDS) return win[min(i - wa, static_cast<uint32_t>(kWinWords - 1))];
+    return a.stream[min(i, a.n_words - 1)];
+}
+
+// Global inputs of one task, loaded a task ahead.
+struct TaskIn {
+    uint32_t pos0, pos1;  // this lane's chunk: first bit, first bit of the next chunk
+    uint32_t wlo, whi;    // first bit of the wave's first chunk / of the chunk after its last
+    uint32_t bw;          // bitmap word with this lane's groups (simple layout)
+    uint32_t rb;          // row_base of the row holding the wave's first group
+    uint32_t pre;         // lane i <= word of that group: bitmap word i of that row
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
+{
+    extern __shared__ uint32_t smem[];
+    uint32_t* lut = smem;
+    uint8_t* t1 = reinterpret_cast<uint8_t*>(smem + kLutEntries);
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const uint32_t nthreads = blockDim.x, waves = nthreads >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t* win = smem + kLutEntries + kT1Dwords + wave * kWaveDwords;
+    uint32_t* sym = win + kWinWords;
+    uint32_t* info = sym + 64 * kSymPitch;
+    uint32_t* mysym = sym + lane * kSymPitch;
+
+    // ---- tables
+    const uint32_t L = a.lmax, lsize = 1u << L;
+    // t1: zero (no code), then each canonical code fills the 2^(L - len) entries that
+    // start with it
+    for (uint32_t d = tid; d < kT1Dwords; d += nthreads) reinterpret_cast<uint32_t*>(t1)[d] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const uint32_t g = a.ranges[r], len = (g >> 16) & 15u;
+        if (len == 0) continue;
+        const uint32_t lo = g & 0xFFFFu, cnt = 1u << (L - len);
+        const uint8_t ent = static_cast<uint8_t>(len | (((g >> 20) & 0xFu) << 4));
+        for (uint32_t i = tid; i < cnt; i += nthreads) t1[lo + i] = ent;
+    }
+    __syncthreads();
+    // Multi-code table, one code position at a time for kPer entries per thread so their
+    // t1 reads overlap: the code after the first ones is read from t1 at the bits after
+    // them (valid while it fits in lmax bits). Entries are visited in a scattered order
+    // (an odd multiplier permutes 0..lsize-1): entries with a common prefix read t1 at
+    // strides of 2^length and would otherwise pile onto one LDS bank.
+    constexpr int kPer = 8;
+    for (uint32_t base = 0; base < lsize; base += kPer * nthreads) {
+        uint32_t idx[kPer], vals[kPer], used[kPer], n[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; u++) {
+            idx[u] = (min(base + u * nthreads + tid, lsize - 1) * 0x9E5u) & (lsize - 1);
+            const uint32_t e1 = t1[idx[u]];
+            used[u] = e1 & 15u;
+            vals[u] = e1 >> 4;
+            n[u] = used[u] ? 1u : 0u;
+        }
+#pragma unroll
+        for (uint32_t step = 1; step < kMaxSyms; step++) {
+            uint32_t e2[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; u++) e2[u] = t1[(idx[u] << used[u]) & (lsize - 1)];
+#pragma unroll
+            for (int u = 0; u < kPer; u++) {
+                const uint32_t l2 = e2[u] & 15u;
+                const bool ok = n[u] == step && l2 != 0 && used[u] + l2 <= L;
+                vals[u] |= ok ? (e2[u] >> 4) << (4 * step) : 0u;
+                used[u] += ok ? l2 : 0u;
+                n[u] += ok ? 1u : 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; u++) {
+            if (base + u * nthreads + tid < lsize)
+                lut[idx[u]] = n[u] ? vals[u] | (used[u] << 24) | (n[u] << 28) : kEntErr | (1u << 28) | (L << 24);
+        }
+    }
+    __syncthreads();
+
+    // ---- tasks
+    const uint32_t stride = gridDim.x * waves;
+    auto load_in = [&](uint32_t task, TaskIn& t) {
+        const uint32_t c0 = task * 64, c = c0 + lane;
+        const uint32_t cl = min(c, a.n_chunks - 1);
+        t.pos0 = a.offs[cl];
+        t.pos1 = a.offs[cl + 1];
+        t.wlo = a.offs[c0];
+        t.whi = a.offs[min(c0 + 64, a.n_chunks)];
+        const uint32_t fg0 = c0 * (a.chunk >> 6);  // the wave's first group (flat)
+        const uint32_t row0 = fg0 / a.Gr, j0 = fg0 - row0 * a.Gr;
+        t.rb = a.row_base[row0];
+        t.pre = lane <= (j0 >> 5) ? a.bitmap[row0 * a.words + lane] : 0u;
+        t.bw = 0;
+        if (a.simple) {
+            const uint32_t fg = cl * (a.chunk >> 6), row = fg / a.Gr, j = fg - row * a.Gr;
+            t.bw = a.bitmap[row * a.words + (j >> 5)];
+        }
+    };
+    auto window_of = [&](const TaskIn& t, uint32_t& wa, uint32_t& pieces) {
+        const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t.wlo)) >> 5;
+        const uint32_t w1 = min((static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t.whi)) >> 5) + 2u, a.n_words);
+        wa = w0 & ~3u;
+        pieces = (w1 - wa + 3) >> 2;
+    };
+    // every lane loads all kWinLoads pieces (clamped to the stream) so the loads are
+    // straight-line code; pieces past the window's end are not stored
+    auto load_window = [&](const TaskIn& t, u32x4* pw) {
+        uint32_t wa, pieces;
+        window_of(t, wa, pieces);
+        const uint32_t last = a.n_words / 4 - 1;
+#pragma unroll
+        for (int q = 0; q < kWinLoads; q++)
+            pw[q] = reinterpret_cast<const u32x4*>(a.stream)[min(wa / 4 + q * 64 + lane, last)];
+    };
+
+    uint32_t task = blockIdx.x * waves + wave;
+    if (task >= a.n_tasks) return;
+    TaskIn cur;
+    u32x4 pw[kWinLoads];
+    load_in(task, cur);
+    load_window(cur, pw);
+    for (; task < a.n_tasks; task += stride) {
+        const uint32_t c0 = task * 64, c = c0 + lane;
+        const bool active = c < a.n_chunks;
+        const uint32_t e0 = active ? c * a.chunk : 0;
+        const uint32_t len = active ? min(a.chunk, a.n_elems - e0) : 0;
+        const uint32_t ng = len >> 6;
+
+        // stream window into LDS
+        uint32_t wa, pieces;
+        window_of(cur, wa, pieces);
+        const bool in_lds = pieces <= static_cast<uint32_t>(kWinWords / 4);
+        if (in_lds) {
+#pragma unroll
+            for (int q = 0; q < kWinLoads; q++) {
+                const uint32_t p = q * 64 + lane;
+                if (p < pieces) *reinterpret_cast<u32x4*>(win + 4 * p) = pw[q];
+            }
+        }
+
+        // raw groups of this lane's chunk (bit q = group q)
+        uint32_t rawmask = 0;
+        if (ng) {
+            const uint32_t fg = e0 >> 6;
+            uint32_t row = fg / a.Gr, j = fg - row * a.Gr;
+            if (a.simple) {
+                rawmask = ng >= 32 ? cur.bw : (cur.bw >> (j & 31)) & ((1u << ng) - 1u);
+            } else {
+                for (uint32_t q = 0; q < ng; q++) {
+                    rawmask |= ((a.bitmap[row * a.words + (j >> 5)] >> (j & 31)) & 1u) << q;
+                    if (++j == a.Gr) {
+                        j = 0;
+                        row++;
+                    }
+                }
+            }
+        }
+        // raw-table index of this lane's first raw group: raw groups before the wave's
+        // first group (its row's base plus the set bits before it in that row) plus those
+        // of the lanes below (the wave's chunks are consecutive in the raw table's order)
+        uint32_t rawbase = 0;
+        if (MODE == DEC_EXP || MODE == DEC_FULL) {
+            const uint32_t fg0 = c0 * (a.chunk >> 6);
+            const uint32_t j0 = fg0 % a.Gr, wj = j0 >> 5;
+            const uint32_t before = lane < wj ? __popc(cur.pre) : lane == wj ? __popc(cur.pre & ((1u << (j0 & 31)) - 1u)) : 0u;
+            rawbase = __builtin_amdgcn_readfirstlane(cur.rb) + wave_sum6(before) + wave_prefix6(__popc(rawmask), lane);
+        }
+        info[lane] = rawmask;
+        info[64 + lane] = rawbase;
+        const uint32_t pos0 = active ? cur.pos0 : 0, pos1 = cur.pos1;
+
+        // the next task's inputs are in flight while this one decodes
+        const uint32_t next = task + stride;
+        TaskIn nx;
+        if (next < a.n_tasks) load_in(next, nx);
+        wave_sync();
+
+        // bit reader: nb valid bits MSB-aligned in buf; wp = next word to load
+        uint32_t wp = pos0 >> 5;
+        uint64_t buf = 0;
+        int nb = 64 - static_cast<int>(pos0 & 31);
+        uint32_t err = 0;
+        auto start = [&](auto lds_tag) {
+            constexpr bool IN_LDS = decltype(lds_tag)::value;
+            buf = ((static_cast<uint64_t>(read_word<IN_LDS>(a, win, wa, wp)) << 32) | read_word<IN_LDS>(a, win, wa, wp + 1))
+                  << (pos0 & 31);
+            wp += 2;
+        };
+        // Decode S symbols into mysym. Lanes that are done step with a null entry (no
+        // bits, no symbols). A refill before every two steps keeps >= lmax bits in buf.
+        auto decode = [&](auto lds_tag, uint32_t S) {
+            constexpr bool IN_LDS = decltype(lds_tag)::value;
+            uint32_t k = 0;
+            uint64_t acc = 0;
+            uint32_t wn = read_word<IN_LDS>(a, win, wa, wp);  // word wp, read a refill ahead
+            auto refill = [&]() {
+                const bool take = nb < 32;
+                buf |= take ? static_cast<uint64_t>(wn) << (32 - nb) : 0ull;
+                wp += take ? 1u : 0u;
+                nb += take ? 32 : 0;
+                wn = read_word<IN_LDS>(a, win, wa, wp);
+            };
+            auto put = [&](uint32_t vals, uint32_t n) {
+                acc |= static_cast<uint64_t>(vals) << (4 * (k & 7));
+                mysym[k >> 3] = static_cast<uint32_t>(acc);
+                const uint32_t kn = k + n;
+                acc >>= ((k ^ kn) & 8) << 2;
+                k = kn;
+            };
+            while (__any(k + kMaxSyms <= S)) {
+                refill();
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    uint32_t e = lut[static_cast<uint32_t>(buf >> (64 - L))];
+                    e = k + kMaxSyms <= S ? e : 0u;
+                    const uint32_t lt = ent_len(e);
+                    buf <<= lt;
+                    nb -= static_cast<int>(lt);
+                    err |= e;
+                    put(e & 0xFFFFFFu, ent_n(e));
+                }
+            }
+            while (__any(k < S)) {
+                refill();
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    const uint32_t e1 = t1[static_cast<uint32_t>(buf >> (64 - L))];
+                    const bool go = k < S;
+                    const uint32_t l1 = e1 & 15u;
+                    const uint32_t lt = go ? (l1 ? l1 : L) : 0u;
+                    buf <<= lt;
+                    nb -= static_cast<int>(lt);
+                    err |= go && l1 == 0 ? kEntErr : 0u;
+                    put(go ? e1 >> 4 : 0u, go ? 1u : 0u);
+                }
+            }
+        };
+        // the task body, instantiated for each word source so that the LDS one never
+        // shares a path with pending global reads
+        auto run_task = [&](auto lds_tag) {
+            start(lds_tag);
+            const uint32_t segs = (a.chunk + kSegElems - 1) / kSegElems;
+            for (uint32_t s = 0; s < segs; s++) {
+                const uint32_t gq = 4 * s;
+                const uint32_t nseg = ng > gq ? min(ng - gq, 4u) : 0u;
+                const uint32_t nonraw = ~(rawmask >> gq) & ((1u << nseg) - 1u);
+                const uint32_t S = 64u * __popc(nonraw);
+                // sign/mantissa bytes of this lane's write-out items, in flight during the decode
+                // (items of 16 weights: chunk l = 4 it + lane / 16, group (lane / 4) % 4, piece lane % 4)
+                constexpr int kSmItems = MODE == DEC_FULL || MODE == DEC_DIRECT ? 16 : 1;
+                u32x4 smv[kSmItems];
+                if (MODE == DEC_FULL || MODE == DEC_DIRECT) {
+    #pragma unroll
+                    for (int it = 0; it < kSmItems; it++) {
+                        const uint32_t l = 4 * it + (lane >> 4), g = (lane >> 2) & 3;
+                        const uint32_t cl = min(c0 + l, a.n_chunks - 1);
+                        const uint32_t el = cl * a.chunk, q = min(gq + g, (min(a.chunk, a.n_elems - el) >> 6) - 1);
+                        smv[it] = *reinterpret_cast<const u32x4*>(a.sm + el + 64 * q + 16 * (lane & 3));
+                    }
+                }
+                decode(lds_tag, S);
+                if (s == 0 && next < a.n_tasks) load_window(nx, pw);
+                wave_sync();
+
+                // ---- cooperative write-out of segment s of the wave's 64 chunks. Item
+                // (chunk l, group g of the segment, piece p); consecutive lanes cover
+                // consecutive output bytes of one chunk.
+                auto item_ok = [&](uint32_t l, uint32_t q, uint32_t& el) {
+                    const uint32_t cl = c0 + l;
+                    if (cl >= a.n_chunks) return false;
+                    el = cl * a.chunk;
+                    return q < (min(a.chunk, a.n_elems - el) >> 6);
+                };
+                // symbols of group q (of this segment) start at nibble 64 * (non-raw groups before it)
+                auto sym_of = [&](uint32_t l, uint32_t rm, uint32_t g) {
+                    return sym + l * kSymPitch + 8u * __popc((~rm >> gq) & ((1u << g) - 1u));
+                };
+                if (MODE == DEC_EXP) {
+    #pragma unroll 4
+                    for (int it = 0; it < 16; it++) {
+                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        uint32_t el;
+                        if (!item_ok(l, q, el)) continue;
+                        const uint32_t rm = info[l];
+                        u32x4 v;
+                        if ((rm >> q) & 1u) {
+                            const uint32_t rb = info[64 + l];
+                            const uint32_t ri = min(rb + __popc(rm & ((1u << q) - 1u)), a.raw_max);
+                            v = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * p);
+                        } else {
+                            const uint32_t* sp = sym_of(l, rm, g) + 2 * p;
+                            const uint32_t n0 = sp[0], n1 = sp[1];
+                            const uint32_t a0 = pal4(n0 & 0x0F0F0F0Fu, a.pal), b0 = pal4((n0 >> 4) & 0x0F0F0F0Fu, a.pal);
+                            const uint32_t a1 = pal4(n1 & 0x0F0F0F0Fu, a.pal), b1 = pal4((n1 >> 4) & 0x0F0F0F0Fu, a.pal);
+                            v = u32x4{__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
+                                      __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
+                        }
+                        *reinterpret_cast<u32x4*>(a.out + el + 64 * q + 16 * p) = v;
+                    }
+                } else if (MODE == DEC_FULL) {
+    #pragma unroll
+                    for (int it = 0; it < 16; it++) {
+                        if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
+                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        uint32_t el;
+                        if (!item_ok(l, q, el)) continue;
+                        const uint32_t e = el + 64 * q + 16 * p;
+                        const uint32_t rm = info[l];
+                        uint32_t ea0, eb0, ea1, eb1;
+                        if ((rm >> q) & 1u) {
+                            const uint32_t rb = info[64 + l];
+                            const uint32_t ri = min(rb + __popc(rm & ((1u << q) - 1u)), a.raw_max);
+                            const u32x4 r = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * p);
+                            split_exps(r.x, r.y, ea0, eb0);
+                            split_exps(r.z, r.w, ea1, eb1);
+                        } else {
+                            const uint32_t* sp = sym_of(l, rm, g) + 2 * p;
+                            const uint32_t n0 = sp[0], n1 = sp[1];
+                            ea0 = pal4(n0 & 0x0F0F0F0Fu, a.pal);
+                            eb0 = pal4((n0 >> 4) & 0x0F0F0F0Fu, a.pal);
+                            ea1 = pal4(n1 & 0x0F0F0F0Fu, a.pal);
+                            eb1 = pal4((n1 >> 4) & 0x0F0F0F0Fu, a.pal);
+                        }
+                        u32x4* o = reinterpret_cast<u32x4*>(a.out + 2 * static_cast<uint64_t>(e));
+                        o[0] = piece_from_split(ea0, eb0, smv[it].x, smv[it].y);
+                        o[1] = piece_from_split(ea1, eb1, smv[it].z, smv[it].w);
+                    }
+                } else if (MODE == DEC_IDX) {
+    #pragma unroll
+                    for (int it = 0; it < 8; it++) {
+                        const uint32_t item = it * 64 + lane, l = item >> 3, g = (item >> 1) & 3, p = item & 1, q = gq + g;
+                        uint32_t el;
+                        if (!item_ok(l, q, el)) continue;
+                        const uint32_t rm = info[l];
+                        u32x4 v = {0, 0, 0, 0};
+                        if (!((rm >> q) & 1u)) {
+                            const uint32_t* sp = sym_of(l, rm, g) + 4 * p;
+                            v = u32x4{sp[0], sp[1], sp[2], sp[3]};
+                        }
+                        *reinterpret_cast<u32x4*>(a.out + (el + 64 * q) / 2 + 16 * p) = v;
+                    }
+                } else {
+                    // direct plane: the 16 weights of lane group p of a group, at MFMA lane
+                    // 16p + (row & 15) of the row tile's block
+    #pragma unroll
+                    for (int it = 0; it < 16; it++) {
+                        if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
+                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        uint32_t el;
+                        if (!item_ok(l, q, el)) continue;
+                        const uint32_t fs = el + 64 * q;
+                        const uint32_t fg = fs >> 6, n = fg / a.Gr, j = fg - n * a.Gr;
+                        uint8_t* blk = a.out + 1536ull * (static_cast<uint64_t>(n >> 4) * a.Gr + j);
+                        const uint32_t ll = 16 * p + (n & 15);
+                        u32x4 v = smv[it];
+                        v = (v & 0x7F7F7F7Fu) << 1 | ((v << 1) & 0x01000100u) | ((v >> 15) & 0x00010001u);
+                        *reinterpret_cast<u32x4*>(blk + 16 * ll) = v;
+                        const uint32_t rm = info[l];
+                        u32x2 d = {0, 0};
+                        if (!((rm >> q) & 1u)) {
+                            const uint32_t* sp = sym_of(l, rm, g) + 2 * p;
+    #pragma unroll
+                            for (int h = 0; h < 2; h++) {
+                                const uint32_t nat = sp[h], lo = nat & 0x0F0F0F0Fu, hi = (nat >> 4) & 0x0F0F0F0Fu;
+                                d[h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u) | (__builtin_amdgcn_perm(hi, lo, 0x07030602u) << 4);
+                            }
+                        }
+                        *reinterpret_cast<u32x2*>(blk + 1024 + 8 * ll) = d;
+                    }
+                }
+                wave_sync();
+            }
+        };
+        if (in_lds)
+            run_task(std::true_type{});
+        else
+            run_task(std::false_type{});
+        if (active) {
+            const uint32_t consumed = (wp - (pos0 >> 5)) * 32 - (pos0 & 31) - static_cast<uint32_t>(nb);
+            uint32_t bits = (err & kEntErr) ? UW_DERR_BADCODE : 0u;
+            if (consumed != pos1 - pos0) bits |= UW_DERR_CHUNKLEN;
+            if (bits && a.err) atomicOr(a.err, bits);
+        }
+        if (next < a.n_tasks) cur = nx;
+    }
+}
+
+}  // namespace lut
+
 }  // namespace
+
+// Compute units of the current device (the persistent decoder runs one workgroup per CU).
+uint32_t cu_count()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;  // benign race: every writer stores the same value
+    }
+    return static_cast<uint32_t>(cached[dev]);
+}
+
+template <int MODE>
+hipError_t launch_lut(const lut::Args& f, uint32_t blocks, uint32_t waves, hipStream_t s)
+{
+    static bool attr_done = false;  // benign race: every writer stores the same value
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lut::decode_lut_kernel<MODE>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lut::lds_bytes(lut::kMaxWaves)));
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL(lut::decode_lut_kernel<MODE>, dim3(blocks), dim3(64 * waves), lut::lds_bytes(waves), s, f);
+    return hipGetLastError();
+}
 
 uint64_t direct_plane_bytes(const uw_header* h)
 {
@@ -370,15 +904,68 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
     } else {
         std::memcpy(a.pal, h->palette, 16);
     }
-    const size_t lds = kStageDwords * 4 + (2u << h->lmax);
-    const dim3 grid((h->n_chunks + 64 * kWaves - 1) / (64 * kWaves));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (mode) {
-    case DEC_FULL: hipLaunchKernelGGL(decode_kernel<DEC_FULL>, grid, dim3(256), lds, s, a); break;
-    case DEC_EXP: hipLaunchKernelGGL(decode_kernel<DEC_EXP>, grid, dim3(256), lds, s, a); break;
-    case DEC_IDX: hipLaunchKernelGGL(decode_kernel<DEC_IDX>, grid, dim3(256), lds, s, a); break;
-    case DEC_DIRECT: hipLaunchKernelGGL(decode_kernel<DEC_DIRECT>, grid, dim3(256), lds, s, a); break;
-    default: return fail(UW_EINVAL, "bad decode mode");
+    const uint64_t n_elems = static_cast<uint64_t>(h->N) * static_cast<uint64_t>(h->K);
+    if (h->lmax <= 12 && h->chunk <= lut::kMaxChunk && n_elems + h->chunk < (1ull << 32) &&
+        h->K <= 131072) {
+        lut::Args f;
+        std::memset(&f, 0, sizeof f);
+        f.sm = a.sm;
+        f.bitmap = a.bitmap;
+        f.row_base = a.row_base;
+        f.raw = a.raw;
+        f.offs = a.offs;
+        f.stream = a.stream;
+        f.out = static_cast<uint8_t*>(d_out);
+        f.err = d_err;
+        f.K = static_cast<uint32_t>(h->K);
+        f.Gr = static_cast<uint32_t>(h->K / 64);
+        f.words = h->bitmap_words;
+        f.chunk = h->chunk;
+        f.n_chunks = h->n_chunks;
+        f.n_tasks = (h->n_chunks + 63) / 64;
+        f.n_elems = static_cast<uint32_t>(n_elems);
+        f.lmax = h->lmax;
+        f.n_words = static_cast<uint32_t>(h->bytes_stream / 4);
+        f.raw_max = a.raw_max;
+        uint8_t vmap[16];
+        for (int i = 0; i < 16; i++) vmap[i] = static_cast<uint8_t>(i);
+        if (mode == DEC_DIRECT) {
+            ValueOrder vo;
+            value_order(h, &vo);
+            std::memcpy(vmap, vo.order, 16);
+        }
+        // the canonical codes in rank order: code of rank first_index[l] + k is first_code[l] + k
+        for (uint32_t l = 1, r = 0; l <= h->lmax; l++)
+            for (uint32_t k = 0; k < t.count[l] && r < 16; k++, r++)
+                f.ranges[r] = ((t.first_code[l] + k) << (h->lmax - l)) | (l << 16) |
+                              (static_cast<uint32_t>(vmap[t.sorted[r] & 15]) << 20);
+        std::memcpy(f.pal, h->palette, 16);
+        f.simple = (h->chunk & (h->chunk - 1)) == 0 && h->K % h->chunk == 0;
+        // equal rounds: every wave of the persistent grid gets the same number of tasks
+        const uint32_t cus = cu_count();
+        const uint32_t rounds = (f.n_tasks + cus * lut::kMaxWaves - 1) / (cus * lut::kMaxWaves);
+        const uint32_t waves = (f.n_tasks + cus * rounds - 1) / (cus * rounds);
+        const uint32_t blocks = (f.n_tasks + waves * rounds - 1) / (waves * rounds);
+        hipError_t e = hipSuccess;
+        switch (mode) {
+        case DEC_FULL: e = launch_lut<DEC_FULL>(f, blocks, waves, s); break;
+        case DEC_EXP: e = launch_lut<DEC_EXP>(f, blocks, waves, s); break;
+        case DEC_IDX: e = launch_lut<DEC_IDX>(f, blocks, waves, s); break;
+        case DEC_DIRECT: e = launch_lut<DEC_DIRECT>(f, blocks, waves, s); break;
+        default: return fail(UW_EINVAL, "bad decode mode");
+        }
+        if (e != hipSuccess) return fail(UW_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    } else {
+        const size_t lds = kStageDwords * 4 + (2u << h->lmax);
+        const dim3 grid((h->n_chunks + 64 * kWaves - 1) / (64 * kWaves));
+        switch (mode) {
+        case DEC_FULL: hipLaunchKernelGGL(decode_kernel<DEC_FULL>, grid, dim3(256), lds, s, a); break;
+        case DEC_EXP: hipLaunchKernelGGL(decode_kernel<DEC_EXP>, grid, dim3(256), lds, s, a); break;
+        case DEC_IDX: hipLaunchKernelGGL(decode_kernel<DEC_IDX>, grid, dim3(256), lds, s, a); break;
+        case DEC_DIRECT: hipLaunchKernelGGL(decode_kernel<DEC_DIRECT>, grid, dim3(256), lds, s, a); break;
+        default: return fail(UW_EINVAL, "bad decode mode");
+        }
     }
     if (mode == DEC_DIRECT) {
         MetaArgs m;
@@ -394,7 +981,7 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
         m.T = static_cast<uint32_t>(T);
         m.words = h->bitmap_words;
         m.raw_max = a.raw_max;
-        hipLaunchKernelGGL(direct_meta_kernel, dim3((m.T + 255) / 256), dim3(256), 0, s, m);
+        hipLaunchKernelGGL(direct_meta_kernel, dim3((m.T + 3) / 4), dim3(256), 0, s, m);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(UW_EHIP, "decode launch failed: %s", hipGetErrorString(e));

@@ -192,3 +192,17 @@ def test_variants_table():
     assert any(uw.variant_supports(v, 4096, 4096, 1, uw.W_IDX) for v in range(n))
     assert any(uw.variant_supports(v, 4096, 4096, 4096, uw.W_IDX) for v in range(n))
     assert not uw.variant_supports(0, 4096, 100, 1, uw.W_IDX)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the binding before PyTorch must not load a second HIP runtime: libuw and
+    the tensors it is given have to share PyTorch's (a second runtime finds no device)."""
+    import subprocess
+    import sys
+
+    code = ("import decode_gemm_amd, torch, os\n"
+            "m = open('/proc/%d/maps' % os.getpid()).read()\n"
+            "print(len({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1", out.stdout
