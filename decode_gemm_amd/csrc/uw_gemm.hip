@@ -654,9 +654,184 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 }
 
 // ------------------------------------------------------------------------- variants
+// ------------------------------------------------------------------------- wide
+// Large-M kernel. Block = 8 waves computing a 256 (W rows) x 256 (X rows) tile; wave
+// (wn, wm) owns 64 x 128 of it = 4 x 8 MFMA tiles of 16x16 (128 accumulators per lane),
+// so two waves share each SIMD and one wave's MFMAs overlap the other's loads and
+// rebuild. Per 64-k step each thread loads 2 W items (16 weights of one row, as
+// compressed bytes) and 2 X items (16 k of one X row), rebuilds the W items to bf16 and
+// stores both into an LDS stage laid out in MFMA operand order, [16-row tile][k half]
+// [lane] of 16 B, so every fragment read is one conflict-free ds_read_b128. Two stages:
+// step j+1 is rebuilt and stored while step j's MFMAs run; its loads are issued as soon
+// as step j's registers are free (before the barrier that publishes step j), so they have
+// the barrier wait and a whole MFMA phase to arrive. Per MFMA a wave reads 3/8 of the
+// LDS bytes a 64 x 64 wave tile needs.
+template <int SRC, bool CONTIG>
+__global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
+{
+    constexpr int BN = 256, BM = 256, ITEMS = 2, NWV = 8;
+    constexpr int TN = 4, TM = 8;  // 16x16 tiles per wave
+    constexpr bool RAW = SRC == UW_W_IDX;
+    constexpr bool DIRECT = SRC == UW_W_DIRECT;
+    constexpr int A_VEC = BN * 64 * 2 / 16, STAGE_VEC = A_VEC + BM * 64 * 2 / 16;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    u32x4* const S = reinterpret_cast<u32x4*>(lds);
+
+    const uint32_t tiles_n = static_cast<uint32_t>((a.N + BN - 1) / BN);
+    const uint32_t tiles_m = static_cast<uint32_t>((a.M + BM - 1) / BM);
+    uint32_t tn, tm;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_n, tiles_m, tn, tm);
+    const int64_t n0 = static_cast<int64_t>(tn) * BN, m0 = static_cast<int64_t>(tm) * BM;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave >> 1, wm = wave & 1;
+    const uint32_t G = static_cast<uint32_t>(a.K >> 6);
+
+    // W item it: row 16 * (wave + 8 it) + r of the tile, weights 16g .. 16g+15 of a group;
+    // X item it: X row 16 * (wave + 8 it) + r, k 16g .. 16g+15 of a group
+    Plane<SRC> wpl[ITEMS];
+    int64_t wrow[ITEMS];
+    const uint8_t* pmeta[ITEMS];
+    uint32_t bword[ITEMS], rbase[ITEMS];
+    u32x2 mnext[ITEMS];
+    const uint16_t* xsrc[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; it++) {
+        const int i = wave + NWV * it;
+        const int64_t rr = n0 + 16 * i + r;
+        wrow[it] = DIRECT ? rr : (rr < a.N ? rr : a.N - 1);
+        wpl[it] = Plane<SRC>(a, wrow[it], g);
+        bword[it] = 0;
+        rbase[it] = RAW ? a.row_base[wrow[it]] : 0u;
+        if (DIRECT) {
+            int64_t t = (n0 >> 4) + i;
+            t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
+            pmeta[it] = a.dmeta + 8 * t * G;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it]);
+        }
+        const int64_t m = m0 + 16 * i + r;
+        xsrc[it] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
+    }
+
+    floatx4 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int c = 0; c < TM; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    W16 wr[ITEMS];
+    u32x4 xr[ITEMS][2];
+    u32x4 rsm[ITEMS], rex[ITEMS];  // raw item: true sign/mantissa (index plane), verbatim exponents
+    bool israw[ITEMS];
+    auto load_step = [&](uint32_t j) {
+#pragma unroll
+        for (int it = 0; it < ITEMS; it++) {
+            if (RAW && (j & 31) == 0) {  // bitmap word of this step, refreshed every 32 steps
+                if (j) rbase[it] += __popc(bword[it]);
+                bword[it] = a.bitmap[wrow[it] * a.words + (j >> 5)];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < ITEMS; it++) {
+            wpl[it].load(j, wr[it]);
+            if (DIRECT) {
+                const u32x2 mcur = mnext[it];
+                israw[it] = (mcur.x >> r) & 1u;
+                rex[it] = *raw_exp_addr(a, mcur, r, g, wpl[it].p0 + 1536 * static_cast<int64_t>(j));
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
+            }
+            if (RAW) {
+                israw[it] = (bword[it] >> (j & 31)) & 1u;
+                if (israw[it]) {
+                    uint32_t ri = rbase[it] + __popc(bword[it] & ((1u << (j & 31)) - 1u));
+                    ri = ri < a.raw_max ? ri : a.raw_max;
+                    rsm[it] = *reinterpret_cast<const u32x4*>(a.sm + wrow[it] * a.K + 64 * static_cast<int64_t>(j) + 16 * g);
+                    rex[it] = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * g);
+                }
+            }
+            const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc[it] + 64 * static_cast<int64_t>(j));
+            xr[it][0] = xp[0];
+            xr[it][1] = xp[1];
+        }
+    };
+    auto store_step = [&](int st) {
+        u32x4* const A = S + st * STAGE_VEC;
+        u32x4* const B = A + A_VEC;
+#pragma unroll
+        for (int it = 0; it < ITEMS; it++) {
+            const int i = wave + NWV * it;
+            u32x4 p0, p1;
+            rebuild16<SRC, CONTIG>(a, wr[it], p0, p1);
+            if (DIRECT && israw[it]) rebuild16_raw(wr[it], rex[it], p0, p1);
+            if (RAW && israw[it]) {
+                uint32_t ea, eb;
+                split_exps(rex[it].x, rex[it].y, ea, eb);
+                p0 = piece_from_split(ea, eb, rsm[it].x, rsm[it].y);
+                split_exps(rex[it].z, rex[it].w, ea, eb);
+                p1 = piece_from_split(ea, eb, rsm[it].z, rsm[it].w);
+            }
+            A[(2 * i) * 64 + lane] = p0;
+            A[(2 * i + 1) * 64 + lane] = p1;
+            B[(2 * i) * 64 + lane] = xr[it][0];
+            B[(2 * i + 1) * 64 + lane] = xr[it][1];
+        }
+    };
+    auto mma_step = [&](int st) {
+        const u32x4* const A = S + st * STAGE_VEC;
+        const u32x4* const B = A + A_VEC;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            u32x4 bf[TM];
+#pragma unroll
+            for (int c = 0; c < TM; c++) bf[c] = B[((TM * wm + c) * 2 + h) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < TN; i++) {
+                const u32x4 af = A[((TN * wn + i) * 2 + h) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < TM; c++) acc[i][c] = mfma16(af, bf[c], acc[i][c]);
+            }
+        }
+    };
+
+    load_step(0);
+    store_step(0);
+    if (G > 1) load_step(1);
+    __syncthreads();
+    for (uint32_t j = 0; j + 1 < G; j++) {
+        const int st = j & 1;
+        // keep the MFMAs after the loads: sunk into the MFMA sequence (to reuse the
+        // fragment registers) the loads would leave too little time to arrive
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(st);
+        store_step(st ^ 1);
+        if (j + 2 < G) load_step(j + 2);
+        __syncthreads();
+    }
+    mma_step((G - 1) & 1);
+
+    // lane holds D[4*(lane/16) + q][lane%16] = Y^T: 4 consecutive n of one Y row
+#pragma unroll
+    for (int i = 0; i < TN; i++) {
+#pragma unroll
+        for (int c = 0; c < TM; c++) {
+            const int64_t n = n0 + (TN * wn + i) * 16 + 4 * (lane >> 4);
+            const int64_t m = m0 + (TM * wm + c) * 16 + (lane & 15);
+            if (m < a.M) {
+                float* yp = a.y + m * a.ldy + n;
+                if (n + 3 < a.N && (a.ldy & 3) == 0) {
+                    *reinterpret_cast<floatx4*>(yp) = acc[i][c];
+                } else {
+                    for (int q = 0; q < 4; q++)
+                        if (n + q < a.N) yp[q] = acc[i][c][q];
+                }
+            }
+        }
+    }
+}
+
 struct Variant {
     const char* name;
-    int kind;  // 0 skinny, 1 tiled
+    int kind;  // 0 skinny, 1 tiled, 2 wide
     int rt, nw, u;
     int bn, bm;
 };
@@ -666,7 +841,7 @@ const Variant kVariants[] = {
     {"skinny rt1 u4 w4", 0, 1, 4, 4, 0, 0},  {"skinny rt2 u4 w4", 0, 2, 4, 4, 0, 0},
     {"skinny rt2 u4 w8", 0, 2, 8, 4, 0, 0},  {"skinny rt4 u2 w4", 0, 4, 4, 2, 0, 0},
     {"tiled 128x128", 1, 0, 0, 0, 128, 128}, {"tiled 128x64", 1, 0, 0, 0, 128, 64},
-    {"tiled 256x128", 1, 0, 0, 0, 256, 128},
+    {"tiled 256x128", 1, 0, 0, 0, 256, 128}, {"wide 256x256", 2, 0, 0, 0, 256, 256},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -716,8 +891,21 @@ hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
 }
 
 template <int SRC, bool CONTIG>
+hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
+{
+    constexpr size_t lds = 2 * (256 + 256) * 64 * 2;
+    static bool attr_done = false;  // benign race: every writer stores the same value
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), lds, attr_done);
+    if (e != hipSuccess) return e;
+    const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
+    hipLaunchKernelGGL((gemm_wide<SRC, CONTIG>), dim3(tiles), dim3(512), lds, s, g);
+    return hipGetLastError();
+}
+
+template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
+    if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
     if (v.kind == 0) {
         if (v.rt == 1 && v.u == 8) return launch_skinny_rt<SRC, CONTIG, 1, 8, 4>(g, s);
         if (v.rt == 1 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 1, 4, 8>(g, s);
@@ -742,6 +930,9 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
         if (M > 16) return tiles >= 1024 ? 3 : 2;
         return tiles >= 2048 ? 0 : tiles >= 512 ? 1 : 2;
     }
+    // the 256 x 256 kernel once its tiles fill most of the CUs
+    const int64_t wide_tiles = ((N + 255) / 256) * ((M + 255) / 256);
+    if (M >= 512 && wide_tiles >= 192) return 9;
     return M <= 128 ? 7 : 6;
 }
 
