@@ -20,7 +20,8 @@ __all__ = [
     "decode_exponent", "transcode_palette", "prepare_direct", "recon_gemm", "run_pipeline", "autotune", "swiglu",
     "workspace_bytes", "direct_plane_bytes", "variant_count", "variant_name", "variant_supports", "version",
     "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT",
-    "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS",
+    "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS", "Proj", "MlpLayer", "proj", "mlp_layers", "mlp_stack_workspace",
+    "mlp_stack_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuw.so")
@@ -70,6 +71,16 @@ class Plan(ctypes.Structure):
 
     def __repr__(self):
         return f"Plan(pipeline={PIPELINE_NAMES.get(self.pipeline, self.pipeline)}, variant={self.variant}, t_ms={self.t_ms:.4f})"
+
+
+class Proj(ctypes.Structure):
+    """uw_proj: one projection of an MLP layer and the pipeline / variant it runs with."""
+    _fields_ = [("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_direct", ctypes.c_void_p),
+                ("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+class MlpLayer(ctypes.Structure):
+    _fields_ = [("gate", Proj), ("up", Proj), ("down", Proj)]
 
 
 class TuneArgs(ctypes.Structure):
@@ -124,6 +135,9 @@ def _load():
         "uw_autotune": ([ctypes.POINTER(TuneArgs), ctypes.POINTER(i64), ctypes.c_int, P, ctypes.POINTER(Plan)],
                         ctypes.c_int),
         "uw_swiglu": ([P, P, i64, P, P], ctypes.c_int),
+        "uw_mlp_stack_workspace": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, ctypes.c_int, ctypes.POINTER(sz)],
+                                   ctypes.c_int),
+        "uw_mlp_stack_forward": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, P, P, P, sz, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -261,3 +275,30 @@ def autotune(h: Header, d_blob, d_x, d_y, Ms, d_direct=None, d_ws=None, ws_bytes
 
 def swiglu(d_g, d_u, d_h, n: int, stream=None) -> None:
     _check(lib.uw_swiglu(_ptr(d_g), _ptr(d_u), n, _ptr(d_h), _stream(stream)))
+
+
+def proj(h: Header, d_blob, pipeline: int, d_direct=None, variant: int = -1) -> Proj:
+    """A uw_proj; keep `h` alive as long as the layer array is used."""
+    return Proj(ctypes.pointer(h), _ptr(d_blob), _ptr(d_direct), pipeline, variant)
+
+
+def mlp_layers(layers) -> ctypes.Array:
+    """uw_mlp_layer array from (gate, up, down) Proj triples."""
+    arr = (MlpLayer * len(layers))()
+    for i, (g, u, d) in enumerate(layers):
+        arr[i] = MlpLayer(g, u, d)
+    return arr
+
+
+def mlp_stack_workspace(layers: ctypes.Array, M: int, two_slots: bool = False) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.uw_mlp_stack_workspace(layers, len(layers), M, int(two_slots), ctypes.byref(out)))
+    return out.value
+
+
+def mlp_stack_forward(layers: ctypes.Array, M: int, d_x, d_y, d_ws, ws_bytes: int, stream=None,
+                      decode_stream=None) -> None:
+    """uw_mlp_stack_forward: every layer's SwiGLU MLP on the same X; d_y ends as the last
+    layer's output. decode_stream (optional) decodes one projection ahead."""
+    _check(lib.uw_mlp_stack_forward(layers, len(layers), M, _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes,
+                                    _stream(stream), None if decode_stream is None else _stream(decode_stream)))

@@ -208,4 +208,183 @@ uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h
     return e == hipSuccess ? UW_OK : fail(UW_EHIP, "swiglu launch failed: %s", hipGetErrorString(e));
 }
 
+namespace {
+
+struct StackLayout {
+    int64_t Nff, K, Nout;
+    size_t g, u, h, slot0, slot1, slot_bytes, total;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, bool two, StackLayout* o)
+{
+    if (!L || n <= 0) return fail(UW_EINVAL, "no layers");
+    if (M < 0) return fail(UW_ESHAPE, "M < 0");
+    const uw_header* g0 = L[0].gate.h;
+    const uw_header* d0 = L[0].down.h;
+    if (!g0 || !d0) return fail(UW_EINVAL, "NULL header");
+    o->Nff = g0->N;
+    o->K = g0->K;
+    o->Nout = d0->N;
+    size_t slot = 0;
+    for (int l = 0; l < n; l++) {
+        const uw_proj* ps[3] = {&L[l].gate, &L[l].up, &L[l].down};
+        for (int q = 0; q < 3; q++) {
+            if (!ps[q]->h || !ps[q]->d_blob) return fail(UW_EINVAL, "layer %d projection %d: NULL header or blob", l, q);
+            if (ps[q]->pipeline == UW_PIPE_DIRECT && !ps[q]->d_direct)
+                return fail(UW_EINVAL, "layer %d projection %d: direct palette needs the direct plane", l, q);
+            size_t need = 0;
+            uw_status st = uw_workspace_bytes(ps[q]->h, ps[q]->pipeline, &need);
+            if (st != UW_OK) return st;
+            slot = need > slot ? need : slot;
+        }
+        const uw_header* g = L[l].gate.h;
+        const uw_header* u = L[l].up.h;
+        const uw_header* d = L[l].down.h;
+        if (g->N != o->Nff || g->K != o->K || u->N != o->Nff || u->K != o->K || d->K != o->Nff || d->N != o->Nout)
+            return fail(UW_ESHAPE, "layer %d: shapes differ from layer 0 or do not chain", l);
+    }
+    const size_t mf = static_cast<size_t>(M) * static_cast<size_t>(o->Nff);
+    o->slot_bytes = align256(slot);
+    o->g = 0;
+    o->u = align256(4 * mf);
+    o->h = o->u + align256(4 * mf);
+    o->slot0 = o->h + align256(2 * mf);
+    o->slot1 = o->slot0 + o->slot_bytes;
+    o->total = o->slot0 + (two ? 2 : 1) * o->slot_bytes;
+    return UW_OK;
+}
+
+// Decode one projection's plane into `slot` (no-op for direct palette).
+uw_status decode_proj(const uw_proj& p, void* slot, void* stream)
+{
+    switch (p.pipeline) {
+    case UW_PIPE_FULL: return uw_decode_full(p.h, p.d_blob, static_cast<uint16_t*>(slot), nullptr, stream);
+    case UW_PIPE_EXP: return uw_decode_exponent(p.h, p.d_blob, static_cast<uint8_t*>(slot), nullptr, stream);
+    case UW_PIPE_TRANSCODE: return uw_transcode_palette(p.h, p.d_blob, static_cast<uint8_t*>(slot), nullptr, stream);
+    case UW_PIPE_DIRECT: return UW_OK;
+    default: return fail(UW_EINVAL, "unknown pipeline %d", p.pipeline);
+    }
+}
+
+// The GEMM of a projection whose plane is ready (in `slot`, or the direct plane).
+uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
+                    void* stream)
+{
+    uw_gemm_args g;
+    std::memset(&g, 0, sizeof g);
+    g.M = M;
+    g.d_x = x;
+    g.ldx = ldx;
+    g.h = p.h;
+    g.d_blob = p.d_blob;
+    g.d_y = y;
+    g.ldy = ldy;
+    g.variant = p.variant;
+    g.src = p.pipeline == UW_PIPE_FULL ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
+          : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
+    g.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
+    return uw_recon_gemm(&g, stream);
+}
+
+}  // namespace
+
+uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64_t M, int two_slots, size_t* out)
+{
+    clear_error();
+    if (!out) return fail(UW_EINVAL, "NULL argument");
+    StackLayout lay;
+    uw_status st = stack_layout(layers, n_layers, M, two_slots != 0, &lay);
+    if (st == UW_OK) *out = lay.total;
+    return st;
+}
+
+uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y,
+                               void* d_ws, size_t ws_bytes, void* stream, void* decode_stream)
+{
+    try {
+        clear_error();
+        const bool two = decode_stream != nullptr;
+        StackLayout lay;
+        uw_status st = stack_layout(layers, n_layers, M, two, &lay);
+        if (st != UW_OK) return st;
+        if (M == 0) return UW_OK;
+        if (!d_x || !d_y || !d_ws) return fail(UW_EINVAL, "NULL device pointer");
+        if (!aligned(d_ws, 256)) return fail(UW_EINVAL, "d_ws must be 256-byte aligned");
+        if (ws_bytes < lay.total) return fail(UW_ENOSPACE, "the stack needs %zu workspace bytes", lay.total);
+        uint8_t* ws = static_cast<uint8_t*>(d_ws);
+        float* g = reinterpret_cast<float*>(ws + lay.g);
+        float* u = reinterpret_cast<float*>(ws + lay.u);
+        uint16_t* h = reinterpret_cast<uint16_t*>(ws + lay.h);
+        void* slot[2] = {ws + lay.slot0, ws + lay.slot1};
+        const int64_t mf = M * lay.Nff;
+
+        if (!two) {
+            for (int l = 0; l < n_layers && st == UW_OK; l++) {
+                const uw_mlp_layer& L = layers[l];
+                if ((st = decode_proj(L.gate, slot[0], stream)) != UW_OK) break;
+                if ((st = gemm_proj(L.gate, slot[0], M, d_x, lay.K, g, lay.Nff, stream)) != UW_OK) break;
+                if ((st = decode_proj(L.up, slot[0], stream)) != UW_OK) break;
+                if ((st = gemm_proj(L.up, slot[0], M, d_x, lay.K, u, lay.Nff, stream)) != UW_OK) break;
+                if ((st = uw_swiglu(g, u, mf, h, stream)) != UW_OK) break;
+                if ((st = decode_proj(L.down, slot[0], stream)) != UW_OK) break;
+                st = gemm_proj(L.down, slot[0], M, h, lay.Nff, d_y, lay.Nout, stream);
+            }
+            return st;
+        }
+
+        // two streams: projection p decodes into slot p & 1 on decode_stream once the GEMM
+        // that last read that slot (projection p - 2) is done; its GEMM waits for the decode
+        hipStream_t ms = static_cast<hipStream_t>(stream), ds = static_cast<hipStream_t>(decode_stream);
+        hipEvent_t decoded[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+        for (int s = 0; s < 2; s++) {
+            if (hipEventCreateWithFlags(&decoded[s], hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&consumed[s], hipEventDisableTiming) != hipSuccess) {
+                for (int q = 0; q < 2; q++) {
+                    if (decoded[q]) (void)hipEventDestroy(decoded[q]);
+                    if (consumed[q]) (void)hipEventDestroy(consumed[q]);
+                }
+                return fail(UW_EHIP, "hipEventCreate failed");
+            }
+        }
+        // the decode stream must also see everything queued on the main stream so far
+        // (the caller's writes of X and of the planes)
+        hipEvent_t start = nullptr;
+        if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess ||
+            hipEventRecord(start, ms) != hipSuccess || hipStreamWaitEvent(ds, start, 0) != hipSuccess)
+            st = fail(UW_EHIP, "stream ordering failed");
+        int64_t p = 0;
+        auto run = [&](const uw_proj& pr, const uint16_t* x, int64_t ldx, float* y, int64_t ldy) -> uw_status {
+            const int s = static_cast<int>(p & 1);
+            uw_status r = UW_OK;
+            if (pr.pipeline != UW_PIPE_DIRECT) {
+                if (p >= 2 && hipStreamWaitEvent(ds, consumed[s], 0) != hipSuccess) return fail(UW_EHIP, "wait failed");
+                if ((r = decode_proj(pr, slot[s], ds)) != UW_OK) return r;
+                if (hipEventRecord(decoded[s], ds) != hipSuccess || hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess)
+                    return fail(UW_EHIP, "event failed");
+            }
+            if ((r = gemm_proj(pr, slot[s], M, x, ldx, y, ldy, ms)) != UW_OK) return r;
+            if (hipEventRecord(consumed[s], ms) != hipSuccess) return fail(UW_EHIP, "event failed");
+            p++;
+            return UW_OK;
+        };
+        for (int l = 0; l < n_layers && st == UW_OK; l++) {
+            const uw_mlp_layer& L = layers[l];
+            if ((st = run(L.gate, d_x, lay.K, g, lay.Nff)) != UW_OK) break;
+            if ((st = run(L.up, d_x, lay.K, u, lay.Nff)) != UW_OK) break;
+            if ((st = uw_swiglu(g, u, mf, h, ms)) != UW_OK) break;
+            st = run(L.down, h, lay.Nff, d_y, lay.Nout);
+        }
+        for (int s = 0; s < 2; s++) {
+            (void)hipEventDestroy(decoded[s]);
+            (void)hipEventDestroy(consumed[s]);
+        }
+        if (start) (void)hipEventDestroy(start);
+        return st;
+    } catch (...) {
+        return fail(UW_EINTERNAL, "unexpected exception in uw_mlp_stack_forward");
+    }
+}
+
 }  // extern "C"

@@ -285,6 +285,44 @@ uw_status uw_autotune(const uw_tune_args* args, const int64_t* Ms, int nM, void*
  */
 uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h, void* stream);
 
+/*
+ * MLP stack (device). One SwiGLU MLP per layer, layers in order: g = X Wg^T, u = X Wu^T,
+ * h = bf16(silu(g) u) (uw_swiglu), Y = h Wd^T, each projection through its own pipeline
+ * and GEMM variant (e.g. from uw_autotune), all launched on `stream` ("Bundles and
+ * results": gate, activation, up and down per layer; "Sharing the GPU between decode and
+ * compute": the next matrix is prepared while the current one multiplies).
+ *
+ * Every layer reads the same X (bf16 [M][K], K = the gate/up input width, 16-byte
+ * aligned; attention between layers is not modelled) and overwrites d_y (fp32
+ * [M][N_out], N_out = down's N); after the call d_y holds the last layer's output.
+ * With decode_stream != NULL the decode-first projections (full / exp / transcode) are
+ * decoded on decode_stream into two alternating workspace slots, each one projection ahead
+ * of its GEMM; events created by the call order the two streams (the caller's streams keep
+ * their own priorities). All layers must have the same shapes: gate and up N_ff x K, down
+ * N_out x N_ff. Buffers are the caller's; nothing is allocated on the device.
+ *
+ * Workspace, uw_mlp_stack_workspace: g and u (fp32 M x N_ff), h (bf16 M x N_ff) and one
+ * decode slot (two when two_slots != 0) of the largest plane the layers' pipelines decode,
+ * each part 256-byte aligned.
+ * Errors: UW_EINVAL (NULL pointers, bad pipeline, direct plane missing), UW_ESHAPE
+ * (shapes differ or do not chain), UW_ENOSPACE (workspace too small), UW_EHIP.
+ */
+typedef struct {
+    const uw_header* h;       /* the projection's header (host) */
+    const void* d_blob;       /* its blob on the device */
+    const uint8_t* d_direct;  /* its direct plane; required when pipeline == UW_PIPE_DIRECT */
+    int32_t pipeline;         /* uw_pipeline */
+    int32_t variant;          /* GEMM variant, -1 = default */
+} uw_proj;
+
+typedef struct {
+    uw_proj gate, up, down;
+} uw_mlp_layer;
+
+uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64_t M, int two_slots, size_t* out);
+uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y,
+                               void* d_ws, size_t ws_bytes, void* stream, void* decode_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -372,3 +372,54 @@ def test_stack_layers_teacher_forced():
         ni = rng.integers(0, 4096, 1024)
         yr, ar = oracle.gemm_pairs(hg, mats["down"].w, mi, ni)
         check_gemm(host(yd)[mi, ni], yr, ar, f"layer {layer} down")
+
+
+def test_mlp_stack_forward_one_and_two_streams():
+    """uw_mlp_stack_forward over 3 layers with mixed pipelines: one stream and a separate
+    decode stream give bit-identical Y; the last layer's g, u, h (left in the workspace)
+    and Y are checked against the oracle on the GPU's own inputs."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(71)
+    K, F, M = 256, 512, 5
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    pipes = [(uw.PIPE_FULL, uw.PIPE_FULL, uw.PIPE_EXP), (uw.PIPE_DIRECT, uw.PIPE_TRANSCODE, uw.PIPE_DIRECT),
+             (uw.PIPE_EXP, uw.PIPE_DIRECT, uw.PIPE_FULL)]
+    mats, keep, layers = [], [], []
+    for l, pp in enumerate(pipes):
+        trip = []
+        for q, (n, k) in enumerate(((F, K), (F, K), (K, F))):
+            w = synth.f32_to_bf16_bits(rng.standard_normal((n, k), dtype=np.float32) * 0.05)
+            m = Mat(w, 256)
+            d = m.decode("direct")[0] if pp[q] == uw.PIPE_DIRECT else None
+            keep.append((m, d))
+            trip.append(uw.proj(m.h, m.d_blob, pp[q], d_direct=d))
+        mats.append([t[0] for t in keep[-3:]])
+        layers.append(trip)
+    arr = uw.mlp_layers(layers)
+    d_x = dev(x)
+    outs = []
+    for two in (False, True):
+        nbytes = uw.mlp_stack_workspace(arr, M, two_slots=two)
+        ws = empty_u8(nbytes + 256)
+        y = empty_f32(M, K)
+        y.fill_(float("nan"))
+        side = torch.cuda.Stream() if two else None
+        log(f"  stack forward, decode stream: {two}, workspace {nbytes} B")
+        uw.mlp_stack_forward(arr, M, d_x, y, ws, nbytes, decode_stream=side)
+        _sync()
+        outs.append((host(y), host(ws)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "one stream and two streams differ"
+    y, wsb = outs[1]
+    gate, up, down = mats[-1]
+    a256 = lambda v: (v + 255) // 256 * 256
+    g = wsb[: 4 * M * F].view(np.float32).reshape(M, F)
+    u = wsb[a256(4 * M * F): a256(4 * M * F) + 4 * M * F].view(np.float32).reshape(M, F)
+    ho = 2 * a256(4 * M * F)
+    hg = wsb[ho: ho + 2 * M * F].view(np.uint16).reshape(M, F)
+    for name, got, wm in (("gate", g, gate), ("up", u, up)):
+        yr, ar = oracle.gemm(x, wm.w)
+        check_gemm(got, yr, ar, f"stack last layer {name}")
+    href = oracle.swiglu(g, u).reshape(M, F)
+    assert (np.abs(hg.astype(np.int32) - href.astype(np.int32)) <= 1).all()
+    yr, ar = oracle.gemm(hg, down.w)
+    check_gemm(y, yr, ar, "stack last layer down")

@@ -206,3 +206,34 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1", out.stdout
+
+
+def test_mlp_stack_host_checks():
+    """Workspace size of the stack forward and its shape / argument checks (host side,
+    no device call: the checks come before any launch)."""
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")  # 512 x 256
+    hg = uw.inspect(uw.encode(w))
+    wd = np.ascontiguousarray(w.reshape(256, 512))
+    hd = uw.inspect(uw.encode(wd))
+    fake = 1 << 20
+    good = uw.mlp_layers([(uw.proj(hg, fake, uw.PIPE_FULL), uw.proj(hg, fake, uw.PIPE_EXP),
+                           uw.proj(hd, fake, uw.PIPE_TRANSCODE))])
+    M = 7
+    a = lambda v: (v + 255) // 256 * 256
+    slot = a(2 * 512 * 256)  # the largest decode plane: full decode of a 512 x 256 matrix
+    base = 2 * a(4 * M * 512) + a(2 * M * 512)
+    assert uw.mlp_stack_workspace(good, M) == base + slot
+    assert uw.mlp_stack_workspace(good, M, two_slots=True) == base + 2 * slot
+    bad = uw.mlp_layers([(uw.proj(hg, fake, uw.PIPE_FULL), uw.proj(hg, fake, uw.PIPE_FULL),
+                          uw.proj(hg, fake, uw.PIPE_FULL))])  # down must be 256 x 512
+    with pytest.raises(uw.UwError) as e:
+        uw.mlp_stack_workspace(bad, M)
+    assert e.value.status == uw.ESHAPE
+    nodirect = uw.mlp_layers([(uw.proj(hg, fake, uw.PIPE_DIRECT), uw.proj(hg, fake, uw.PIPE_FULL),
+                               uw.proj(hd, fake, uw.PIPE_FULL))])
+    with pytest.raises(uw.UwError) as e:
+        uw.mlp_stack_forward(nodirect, M, fake, fake, fake, 1 << 30, stream=0)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.mlp_stack_forward(good, M, fake, fake, fake, 16, stream=0)
+    assert e.value.status == uw.ENOSPACE
