@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-detail", action="store_true", help="skip per-pipeline detail and the large-M line")
     p.add_argument("--copy-probe", action="store_true", help="also launch a plain 256 MiB copy kernel (counter scale)")
+    p.add_argument("--configs", action="store_true",
+                   help="also sweep the down_proj, 70B-layer and 32-layer-stack workloads (a few minutes more)")
     return p.parse_args()
 
 
@@ -226,6 +228,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(synth, cfg, w, Ms, log)
 
+    sweep = configs_sweep(uw, synth, torch, dev, stream, log) if args.configs else None
+
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -248,6 +252,8 @@ def main():
         "detail": detail,
         "large_m": large_m,
     }
+    if sweep is not None:
+        out["configs"] = sweep
     print(json.dumps(out))
 
 
@@ -281,6 +287,153 @@ def decoder_detail(uw, torch, h, blobs, stream, log):
         res[mode] = {"us": round(us, 2), "bytes": int(nbytes), "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     log(f"[bench] decoders: {res}")
     return res
+
+
+def timed(torch, stream, fn, reps=10):
+    """Median of per-launch HIP-event times (ms) of fn(rep)."""
+    ev = []
+    for r in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(r)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def shape_sweep(uw, synth, torch, dev, stream, log, cfg, proj, Ms, copies=2):
+    """One projection shape: the autotuned plan and each pipeline's best per M, timed over
+    rotated copies of the compressed weights."""
+    w = synth.gen_weight(cfg, proj)
+    blob = uw.encode(w)
+    del w
+    h = uw.inspect(blob)
+    N, K = h.N, h.K
+    blobs, planes = [], []
+    for _ in range(copies):
+        b = torch.from_numpy(blob).to(dev)
+        d = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+        uw.prepare_direct(h, b, d)
+        blobs.append(b)
+        planes.append(d)
+    ws_bytes = uw.workspace_bytes(h, uw.PIPE_FULL)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rows = {}
+    for M in Ms:
+        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        per = {}
+        for p in range(4):
+            pl = uw.autotune(h, blobs[0], x, y, [M], d_direct=planes[0], d_ws=ws, ws_bytes=ws_bytes, reps=5, warmup=2,
+                             pipeline_mask=1 << p)[0]
+            ms = timed(torch, stream, lambda r: uw.run_pipeline(p, h, blobs[r % copies], x, y, M, d_direct=planes[r % copies],
+                                                                d_ws=ws, ws_bytes=ws_bytes, variant=pl.variant,
+                                                                stream=stream))
+            alg = algorithmic_bytes(h, M, p)
+            per[uw.PIPELINE_NAMES[p]] = {
+                "variant": uw.variant_name(pl.variant), "us": round(ms * 1e3, 2),
+                "uncompressed_GBs": round(2 * N * K / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac_compressed": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        best = min(per, key=lambda k: per[k]["us"])
+        rows[str(M)] = {"best": best, **per}
+        log(f"[bench] {cfg.name}/{proj} {N}x{K} M={M}: best {best} {per[best]}")
+    return {"shape": [N, K], "blob_bytes_per_weight": round(blob.size / (N * K), 4), "by_M": rows}
+
+
+def stack_sweep(uw, synth, torch, dev, stream, log, Ms):
+    """The 32-layer SwiGLU stack through uw_mlp_stack_forward: per M, plans autotuned on
+    layer 0's gate and down shapes, one forward timed with one stream and with a separate
+    decode stream."""
+    import concurrent.futures as cf
+
+    cfg = synth.CONFIGS["stack"]
+    sig = synth.gen_stack_sigmas(cfg)
+    L = cfg.layers
+    t0 = time.time()
+
+    def make(i):
+        layer, q = divmod(i, 3)
+        proj = ("gate", "up", "down")[q]
+        return uw.encode(synth.gen_weight(cfg, proj, layer, sigma=float(sig[layer])))
+
+    with cf.ThreadPoolExecutor(max(1, min(16, (os.cpu_count() or 8)))) as ex:
+        blobs_h = list(ex.map(make, range(3 * L)))
+    hs = [uw.inspect(b) for b in blobs_h]
+    d_blobs, d_planes = [], []
+    for b, h in zip(blobs_h, hs):
+        db = torch.from_numpy(b).to(dev)
+        dp = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+        uw.prepare_direct(h, db, dp)
+        d_blobs.append(db)
+        d_planes.append(dp)
+    del blobs_h
+    torch.cuda.synchronize()
+    log(f"[bench] stack: {3 * L} matrices encoded and prepared in {time.time() - t0:.1f}s")
+    Nff, K = hs[0].N, hs[0].K
+    weight_bytes = sum(2 * h.N * h.K for h in hs)
+    ws_t = torch.empty(uw.workspace_bytes(hs[0], uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    rows = {}
+    for M in Ms:
+        plans = {}
+        for q, Kin, Nout in ((0, K, Nff), (2, Nff, K)):
+            x = torch.from_numpy(synth.gen_x(cfg, M, Kin).view(np.int16)).to(dev)
+            y = torch.empty(M, Nout, dtype=torch.float32, device=dev)
+            plans[q] = uw.autotune(hs[q], d_blobs[q], x, y, [M], d_direct=d_planes[q], d_ws=ws_t, ws_bytes=ws_t.numel(),
+                                   reps=5, warmup=2)[0]
+        layers = []
+        for layer in range(L):
+            trip = []
+            for q in range(3):
+                i = 3 * layer + q
+                pl = plans[0 if q < 2 else 2]
+                trip.append(uw.proj(hs[i], d_blobs[i], pl.pipeline, d_direct=d_planes[i], variant=pl.variant))
+            layers.append(trip)
+        arr = uw.mlp_layers(layers)
+        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, K, dtype=torch.float32, device=dev)
+        row = {"gate_up_plan": f"{uw.PIPELINE_NAMES[plans[0].pipeline]} / {uw.variant_name(plans[0].variant)}",
+               "down_plan": f"{uw.PIPELINE_NAMES[plans[2].pipeline]} / {uw.variant_name(plans[2].variant)}"}
+        for two in (False, True):
+            nb = uw.mlp_stack_workspace(arr, M, two_slots=two)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            fwd = lambda r: uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream, decode_stream=side if two else None)
+            fwd(0)
+            ms = timed(torch, stream, fwd, reps=3)
+            key = "two_streams" if two else "one_stream"
+            row[key] = {"ms": round(ms, 3), "tokens_per_s": round(M / (ms * 1e-3), 1),
+                        "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+                        "tflops": round(2.0 * M * weight_bytes / 2 / (ms * 1e-3) / 1e12, 1)}
+            del ws
+        rows[str(M)] = row
+        log(f"[bench] stack M={M}: {row}")
+    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows}
+
+
+def configs_sweep(uw, synth, torch, dev, stream, log):
+    """The other workloads: down_proj (M 256..4096), the 70B-shaped layer (gate and down,
+    M 1..2048), the 32-layer stack (M sweep), and PyTorch's bf16 matmul on plain bf16
+    weights of the large-M shapes as a reference point."""
+    out = {}
+    out["down"] = shape_sweep(uw, synth, torch, dev, stream, log, synth.CONFIGS["down"], "down", (256, 1024, 4096))
+    c70 = synth.CONFIGS["70b"]
+    out["70b_gate"] = shape_sweep(uw, synth, torch, dev, stream, log, c70, "gate", c70.Ms)
+    out["70b_down"] = shape_sweep(uw, synth, torch, dev, stream, log, c70, "down", c70.Ms)
+    torch.cuda.empty_cache()
+    out["stack"] = stack_sweep(uw, synth, torch, dev, stream, log, (1, 4, 16, 64, 256, 1024, 4096))
+    ref = {}
+    for (N, K, M) in ((4096, 14336, 4096), (14336, 4096, 4096), (8192, 28672, 2048)):
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        ms = timed(torch, stream, lambda r: torch.matmul(a, b.t()), reps=10)
+        ref[f"M={M} N={N} K={K}"] = {"us": round(ms * 1e3, 1), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        del a, b
+    out["vendor_bf16_matmul_reference"] = ref
+    log(f"[bench] vendor reference: {ref}")
+    return out
 
 
 def large_m_line(uw, synth, torch, dev, stream, log):

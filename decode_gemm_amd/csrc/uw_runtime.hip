@@ -334,8 +334,9 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
             return st;
         }
 
-        // two streams: projection p decodes into slot p & 1 on decode_stream once the GEMM
-        // that last read that slot (projection p - 2) is done; its GEMM waits for the decode
+        // two streams: the p-th decode-first projection decodes into slot p & 1 on
+        // decode_stream once the GEMM that last read that slot is done; its GEMM waits for
+        // the decode
         hipStream_t ms = static_cast<hipStream_t>(stream), ds = static_cast<hipStream_t>(decode_stream);
         hipEvent_t decoded[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
         for (int s = 0; s < 2; s++) {
@@ -355,17 +356,20 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
             hipEventRecord(start, ms) != hipSuccess || hipStreamWaitEvent(ds, start, 0) != hipSuccess)
             st = fail(UW_EHIP, "stream ordering failed");
         int64_t p = 0;
+        // decode-first projections take slots in turn; direct-palette ones use none and
+        // need no events
+        bool used[2] = {false, false};
         auto run = [&](const uw_proj& pr, const uint16_t* x, int64_t ldx, float* y, int64_t ldy) -> uw_status {
+            if (pr.pipeline == UW_PIPE_DIRECT) return gemm_proj(pr, nullptr, M, x, ldx, y, ldy, ms);
             const int s = static_cast<int>(p & 1);
             uw_status r = UW_OK;
-            if (pr.pipeline != UW_PIPE_DIRECT) {
-                if (p >= 2 && hipStreamWaitEvent(ds, consumed[s], 0) != hipSuccess) return fail(UW_EHIP, "wait failed");
-                if ((r = decode_proj(pr, slot[s], ds)) != UW_OK) return r;
-                if (hipEventRecord(decoded[s], ds) != hipSuccess || hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess)
-                    return fail(UW_EHIP, "event failed");
-            }
+            if (used[s] && hipStreamWaitEvent(ds, consumed[s], 0) != hipSuccess) return fail(UW_EHIP, "wait failed");
+            if ((r = decode_proj(pr, slot[s], ds)) != UW_OK) return r;
+            if (hipEventRecord(decoded[s], ds) != hipSuccess || hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess)
+                return fail(UW_EHIP, "event failed");
             if ((r = gemm_proj(pr, slot[s], M, x, ldx, y, ldy, ms)) != UW_OK) return r;
             if (hipEventRecord(consumed[s], ms) != hipSuccess) return fail(UW_EHIP, "event failed");
+            used[s] = true;
             p++;
             return UW_OK;
         };

@@ -92,8 +92,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     NaN inputs are not produced by the generators, so no NaN quieting is done here.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (the largest, -inf, is
+    # 0xFF800000), so 32-bit arithmetic is exact here
+    r = (u >> 16) & 1
+    r += u
+    r += 0x7FFF
+    r >>= 16
     return r.astype(np.uint16)
 
 
