@@ -54,6 +54,7 @@ struct GemmArgs {
     const uint8_t* dmeta;  // direct plane: per (tile, group) raw mask and side-table base
     const uint8_t* dside;  // direct plane: raw exponents, 64 bytes per raw (row, group)
     uint32_t tiles;        // direct plane: ceil(N / 16)
+    uint32_t kgroups;      // tiled / wide kernels: 64-groups per K slice (blockIdx.y); 0 = all
 };
 
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c)
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         }
     }
 
-    auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) {
+    auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < CT; c++) {
             const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[c] + 64 * static_cast<int64_t>(j));
@@ -297,7 +298,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
     u32x4 xr[U][CT][2];
     u32x2 mr[DIRECT ? U : 1][RT];  // direct: raw-row mask and side base of the slot's block
     u32x4 rx[DIRECT ? U : 1][RT];  // direct: this lane's raw exponents for the slot's group
-    auto load_slot = [&](uint32_t j, auto uc) {
+    auto load_slot = [&](uint32_t j, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
 #pragma unroll
         for (int i = 0; i < RT; i++) {
@@ -305,7 +306,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
             if (DIRECT) mr[u % (DIRECT ? U : 1)][i] = *reinterpret_cast<const u32x2*>(pmeta[i] + 8 * static_cast<int64_t>(j));
         }
     };
-    auto load_raw = [&](uint32_t j, auto vc) {
+    auto load_raw = [&](uint32_t j, auto vc) __attribute__((always_inline)) {
         constexpr int v = decltype(vc)::value % (DIRECT ? U : 1);
 #pragma unroll
         for (int i = 0; i < RT; i++)
@@ -313,7 +314,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
     };
     // one group: rebuild ring slot u (group t), refill it with group t + U, request the
     // raw exponents of group t + U/2, multiply, then refill the X pieces
-    auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) {
+    auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         const uint32_t j = wave + NW * t;
         u32x4 A[RT][2];
@@ -429,6 +430,77 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 // 256 threads = 4 waves as 2 x 2; block tile BN (weight rows) x BM (activation rows);
 // wave tile (BN/2) x (BM/2) of 16 x 16 MFMA tiles. LDS per stage: W and X slices of 64 k
 // in operand order: [16-row tile][k-half][lane][8 values].
+// K slice of this block (tiled and wide kernels): 64-groups [j0, j1).
+__device__ __forceinline__ void k_slice(const GemmArgs& a, uint32_t G, uint32_t& j0, uint32_t& j1)
+{
+    const uint32_t kg = a.kgroups ? a.kgroups : G;
+    j0 = blockIdx.y * kg;
+    j1 = j0 + kg < G ? j0 + kg : G;
+}
+
+// Raw-table index of the first raw group at or after group j0 of a row (index plane).
+__device__ __forceinline__ uint32_t raw_base_at(const GemmArgs& a, int64_t row, uint32_t j0)
+{
+    uint32_t base = a.row_base[row];
+    for (uint32_t w = 0; w < (j0 >> 5); w++) base += __popc(a.bitmap[row * a.words + w]);
+    return base;
+}
+
+// Store 4 consecutive n of output row m.
+__device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, const floatx4& v)
+{
+    if (m >= a.M) return;
+    float* yp = a.y + m * a.ldy + n;
+    if (n + 3 < a.N && (a.ldy & 3) == 0) {
+        *reinterpret_cast<floatx4*>(yp) = v;
+    } else {
+        for (int q = 0; q < 4; q++)
+            if (n + q < a.N) yp[q] = v[q];
+    }
+}
+
+// Split-K epilogue of a BN x BM tile held by waves (wn, wm), wave tiles TN x TM of 16x16:
+// add it into Y with fp32 atomics, one m half (the rows of the waves with wm = h) at a
+// time. The half goes through LDS (free once the K loop is done) so that each atomic
+// instruction of a wave covers 64 consecutive floats of one Y row, two cache lines,
+// instead of the 16 rows of an MFMA output fragment. Columns are XOR-swizzled by row so
+// the fragment writes do not collide on LDS banks.
+template <int BN, int BM, int TN, int TM, int NT>
+__device__ __forceinline__ void add_tile(const GemmArgs& a, float* ep, const floatx4 (&acc)[TN][TM], int64_t n0,
+                                         int64_t m0, int wn, int wm, int lane, int tid)
+{
+    constexpr int HR = BM / 2;
+    static_assert(BN % 64 == 0 && TM * 16 == HR, "tile shape");
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        __syncthreads();
+        if (wm == h) {
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+#pragma unroll
+                for (int c = 0; c < TM; c++) {
+                    const int nn = (wn * TN + i) * 16 + 4 * (lane >> 4), mm = c * 16 + (lane & 15);
+                    *reinterpret_cast<floatx4*>(ep + mm * BN + (nn ^ ((mm & 15) << 2))) = acc[i][c];
+                }
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int e = tid; e < HR * BN; e += NT) {
+            const int mm = e / BN, nn = e % BN;
+            const int64_t m = m0 + h * HR + mm, n = n0 + nn;
+            if (m < a.M && n < a.N) unsafeAtomicAdd(a.y + m * a.ldy + n, ep[mm * BN + (nn ^ ((mm & 15) << 2))]);
+        }
+    }
+}
+
+__global__ void zero_rows(float* y, int64_t ldy, int64_t M, int64_t N)
+{
+    const int64_t total = M * N;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        y[(e / N) * ldy + e % N] = 0.f;
+}
+
 template <int BN, int BM>
 struct TiledCfg {
     static constexpr int TN = BN / 32, TM = BM / 32;     // 16x16 tiles per wave
@@ -481,6 +553,8 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave >> 1, wm = wave & 1;
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
+    uint32_t j0, j1;
+    k_slice(a, G, j0, j1);
 
     // item t of a slice: row R = t >> 1 inside the tile, k-half h = t & 1 (32 weights =
     // two 16-weight units, lane groups g = 2h and 2h + 1)
@@ -504,7 +578,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
             int64_t tt = rr >> 4;
             tt = tt < static_cast<int64_t>(a.tiles) ? tt : a.tiles - 1;
             pmeta[it] = a.dmeta + 8 * tt * G;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it]);
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
         }
     }
     const uint16_t* xsrc[C::XITEMS];
@@ -535,8 +609,8 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
     auto load_step = [&](uint32_t j) {
 #pragma unroll
         for (int it = 0; it < C::WITEMS; it++) {
-            if (RAW && (j & 31) == 0) {  // once every 32 steps, before this step's other loads
-                if (j) rbase[it] += __popc(bword[it]);
+            if (RAW && (j == j0 || (j & 31) == 0)) {  // once every 32 steps, before this step's other loads
+                rbase[it] = j == j0 ? raw_base_at(a, wrow[it], j0) : rbase[it] + __popc(bword[it]);
                 bword[it] = a.bitmap[wrow[it] * a.words + (j >> 5)];
             }
         }
@@ -611,12 +685,12 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
                 for (int q = 0; q < 4; q++) Bs[st * B_VEC + xdst[it] + 16 * q] = xr[it][q];
     };
 
-    load_step(0);
+    load_step(j0);
     store_step(0);
     __syncthreads();
-    for (uint32_t j = 0; j < G; j++) {
-        const int st = j & 1;
-        if (j + 1 < G) load_step(j + 1);
+    for (uint32_t j = j0; j < j1; j++) {
+        const int st = (j - j0) & 1;
+        if (j + 1 < j1) load_step(j + 1);
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             u32x4 af[C::TN], bf[C::TM];
@@ -629,28 +703,22 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 #pragma unroll
                 for (int c = 0; c < C::TM; c++) acc[i][c] = mfma16(af[i], bf[c], acc[i][c]);
         }
-        if (j + 1 < G) store_step(st ^ 1);
+        if (j + 1 < j1) store_step(st ^ 1);
         __syncthreads();
     }
 
+    static_assert(BM / 2 * BN * 4 <= C::LDS, "split-K epilogue half tile must fit the LDS");
+    if (gridDim.y > 1) {  // one of several K slices
+        add_tile<BN, BM, C::TN, C::TM, 256>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane, tid);
+        return;
+    }
     // lane holds D[4*(lane/16) + q][lane%16] = Y^T: 4 consecutive n of one Y row
 #pragma unroll
-    for (int i = 0; i < C::TN; i++) {
+    for (int i = 0; i < C::TN; i++)
 #pragma unroll
-        for (int c = 0; c < C::TM; c++) {
-            const int64_t n = n0 + (wn * C::TN + i) * 16 + 4 * (lane >> 4);
-            const int64_t m = m0 + (wm * C::TM + c) * 16 + (lane & 15);
-            if (m < a.M) {
-                float* yp = a.y + m * a.ldy + n;
-                if (n + 3 < a.N && (a.ldy & 3) == 0) {
-                    *reinterpret_cast<floatx4*>(yp) = acc[i][c];
-                } else {
-                    for (int q = 0; q < 4; q++)
-                        if (n + q < a.N) yp[q] = acc[i][c][q];
-                }
-            }
-        }
-    }
+        for (int c = 0; c < C::TM; c++)
+            store_out(a, m0 + (wm * C::TM + c) * 16 + (lane & 15), n0 + (wn * C::TN + i) * 16 + 4 * (lane >> 4),
+                      acc[i][c]);
 }
 
 // ------------------------------------------------------------------------- variants
@@ -686,6 +754,8 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave >> 1, wm = wave & 1;
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
+    uint32_t j0, j1;
+    k_slice(a, G, j0, j1);
 
     // W item it: row 16 * (wave + 8 it) + r of the tile, weights 16g .. 16g+15 of a group;
     // X item it: X row 16 * (wave + 8 it) + r, k 16g .. 16g+15 of a group
@@ -707,7 +777,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
             int64_t t = (n0 >> 4) + i;
             t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
             pmeta[it] = a.dmeta + 8 * t * G;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it]);
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
         }
         const int64_t m = m0 + 16 * i + r;
         xsrc[it] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
@@ -726,8 +796,8 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
     auto load_step = [&](uint32_t j) {
 #pragma unroll
         for (int it = 0; it < ITEMS; it++) {
-            if (RAW && (j & 31) == 0) {  // bitmap word of this step, refreshed every 32 steps
-                if (j) rbase[it] += __popc(bword[it]);
+            if (RAW && (j == j0 || (j & 31) == 0)) {  // bitmap word of this step, refreshed every 32 steps
+                rbase[it] = j == j0 ? raw_base_at(a, wrow[it], j0) : rbase[it] + __popc(bword[it]);
                 bword[it] = a.bitmap[wrow[it] * a.words + (j >> 5)];
             }
         }
@@ -793,40 +863,34 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         }
     };
 
-    load_step(0);
+    load_step(j0);
     store_step(0);
-    if (G > 1) load_step(1);
+    if (j0 + 1 < j1) load_step(j0 + 1);
     __syncthreads();
-    for (uint32_t j = 0; j + 1 < G; j++) {
-        const int st = j & 1;
+    for (uint32_t j = j0; j + 1 < j1; j++) {
+        const int st = (j - j0) & 1;
         // keep the MFMAs after the loads: sunk into the MFMA sequence (to reuse the
         // fragment registers) the loads would leave too little time to arrive
         __builtin_amdgcn_sched_barrier(0);
         mma_step(st);
         store_step(st ^ 1);
-        if (j + 2 < G) load_step(j + 2);
+        if (j + 2 < j1) load_step(j + 2);
         __syncthreads();
     }
-    mma_step((G - 1) & 1);
+    mma_step((j1 - 1 - j0) & 1);
 
+    static_assert(BM / 2 * BN * 4 <= 2 * STAGE_VEC * 16, "split-K epilogue half tile must fit the LDS");
+    if (gridDim.y > 1) {  // one of several K slices
+        add_tile<BN, BM, TN, TM, 512>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
+                                      static_cast<int>(threadIdx.x));
+        return;
+    }
     // lane holds D[4*(lane/16) + q][lane%16] = Y^T: 4 consecutive n of one Y row
 #pragma unroll
-    for (int i = 0; i < TN; i++) {
+    for (int i = 0; i < TN; i++)
 #pragma unroll
-        for (int c = 0; c < TM; c++) {
-            const int64_t n = n0 + (TN * wn + i) * 16 + 4 * (lane >> 4);
-            const int64_t m = m0 + (TM * wm + c) * 16 + (lane & 15);
-            if (m < a.M) {
-                float* yp = a.y + m * a.ldy + n;
-                if (n + 3 < a.N && (a.ldy & 3) == 0) {
-                    *reinterpret_cast<floatx4*>(yp) = acc[i][c];
-                } else {
-                    for (int q = 0; q < 4; q++)
-                        if (n + q < a.N) yp[q] = acc[i][c][q];
-                }
-            }
-        }
-    }
+        for (int c = 0; c < TM; c++)
+            store_out(a, m0 + (TM * wm + c) * 16 + (lane & 15), n0 + (TN * wn + i) * 16 + 4 * (lane >> 4), acc[i][c]);
 }
 
 struct Variant {
@@ -878,16 +942,66 @@ hipError_t launch_skinny_rt(const GemmArgs& g, hipStream_t s)
     }
 }
 
+// Work split of the tiled and wide kernels over K. With few output tiles (down_proj-like
+// shapes: small N, long K) the CUs would idle, so K is cut into ks slices of whole
+// 64-groups, one workgroup each; Y is zeroed first and every slice adds its partial tile
+// into Y with fp32 atomics. ks is the minimum of a small time model fitted to this
+// kernel's own measurements on the 256-CU part: a workgroup of S steps takes
+// c0 + c1 * S microseconds, `cap` workgroups run at once, and each sliced output element
+// costs `atom` microseconds per slice in L2 atomics.
+struct SliceModel {
+    uint32_t per_cu;  // resident workgroups per CU (LDS / register bound)
+    double c0, c1;    // us per workgroup, us per 64-group step
+};
+constexpr SliceModel kTiledModel = {2, 3.2, 1.66};  // 128 x 128 tile, 4 waves
+constexpr SliceModel kWideModel = {1, 22.0, 2.07};   // 256 x 256 tile, 8 waves
+constexpr double kAtomUs = 3.3e-6;
+
+struct SlicePlan {
+    uint32_t ks;
+    double us;
+};
+
+SlicePlan plan_slices(const SliceModel& mdl, int64_t N, int64_t K, int64_t M, int64_t bn, int64_t bm)
+{
+    const uint32_t G = static_cast<uint32_t>(K / 64);
+    const uint64_t tiles = static_cast<uint64_t>(((N + bn - 1) / bn) * ((M + bm - 1) / bm));
+    const uint64_t cap = static_cast<uint64_t>(mdl.per_cu) * cu_count();
+    uint32_t most = G / 8;
+    most = most < 1 ? 1 : most > 64 ? 64 : most;
+    SlicePlan best = {1, 1e300};
+    for (uint32_t ks = 1; ks <= most; ks++) {
+        const uint32_t kg = (G + ks - 1) / ks;
+        if (ks > 1 && (G + kg - 1) / kg != ks) continue;  // same groups per slice as a smaller ks
+        const uint64_t waves = (tiles * ks + cap - 1) / cap;
+        const double us = waves * (mdl.c0 + mdl.c1 * kg) + (ks > 1 ? kAtomUs * ks * M * N : 0.0);
+        if (us < best.us) best = {ks, us};
+    }
+    return best;
+}
+
+hipError_t launch_sliced(const void* fn, GemmArgs g, uint32_t tiles, uint32_t ks, uint32_t threads, size_t lds, hipStream_t s)
+{
+    const uint32_t G = static_cast<uint32_t>(g.K / 64);
+    g.kgroups = (G + ks - 1) / ks;
+    ks = (G + g.kgroups - 1) / g.kgroups;
+    if (ks > 1) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
+    void* args[] = {&g};
+    return hipLaunchKernel(fn, dim3(tiles, ks), dim3(threads), args, lds, s);
+}
+
 template <int SRC, bool CONTIG, int BN, int BM>
 hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
 {
     using C = TiledCfg<BN, BM>;
     static bool attr_done = false;  // benign race: every writer stores the same value
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_tiled<SRC, CONTIG, BN, BM>), C::LDS, attr_done);
+    const void* fn = reinterpret_cast<const void*>(&gemm_tiled<SRC, CONTIG, BN, BM>);
+    hipError_t e = allow_lds(fn, C::LDS, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_tiled<SRC, CONTIG, BN, BM>), dim3(tiles), dim3(256), C::LDS, s, g);
-    return hipGetLastError();
+    const uint32_t ks = BN == 128 && BM == 128 ? plan_slices(kTiledModel, g.N, g.K, g.M, BN, BM).ks : 1;
+    e = launch_sliced(fn, g, tiles, ks, 256, C::LDS, s);
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <int SRC, bool CONTIG>
@@ -898,8 +1012,9 @@ hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), lds, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
-    hipLaunchKernelGGL((gemm_wide<SRC, CONTIG>), dim3(tiles), dim3(512), lds, s, g);
-    return hipGetLastError();
+    e = launch_sliced(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), g, tiles,
+                      plan_slices(kWideModel, g.N, g.K, g.M, 256, 256).ks, 512, lds, s);
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <int SRC, bool CONTIG>
@@ -930,10 +1045,10 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
         if (M > 16) return tiles >= 1024 ? 3 : 2;
         return tiles >= 2048 ? 0 : tiles >= 512 ? 1 : 2;
     }
-    // the 256 x 256 kernel once its tiles fill most of the CUs
-    const int64_t wide_tiles = ((N + 255) / 256) * ((M + 255) / 256);
-    if (M >= 512 && wide_tiles >= 192) return 9;
-    return M <= 128 ? 7 : 6;
+    // the 128 x 128 or the 256 x 256 kernel, each with its best K split
+    const double t_tiled = plan_slices(kTiledModel, N, K, M, 128, 128).us;
+    const double t_wide = plan_slices(kWideModel, N, K, M, 256, 256).us;
+    return t_wide < t_tiled ? 9 : 6;
 }
 
 uw_status launch_gemm(const uw_gemm_args* p, void* stream)
@@ -1020,7 +1135,7 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
     (void)src;
     if (variant < 0 || variant >= uw::kNumVariants || K % 64 || K < 64) return 0;
     const uw::Variant& v = uw::kVariants[variant];
-    if (v.kind == 0) return M >= 1 && M <= 64;
+    if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }
 

@@ -54,6 +54,7 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
                         void* stream);
 uw_status launch_gemm(const uw_gemm_args* a, void* stream);
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
+uint32_t cu_count();  // compute units of the current device
 uint64_t direct_plane_bytes(const uw_header* h);
 
 bool aligned(const void* p, size_t a);

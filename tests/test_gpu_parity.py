@@ -197,6 +197,28 @@ def test_gemm_small_integers_exact():
                 assert np.array_equal(_run_gemm(m, planes, src, x, v), ref), f"M={M} src={src} v={v}"
 
 
+def test_gemm_k_slices_one_hot_exact():
+    """K = 4160 (65 groups of 64) with raw groups: the tiled and wide launches cut K into
+    slices that start inside a bitmap word and end ragged, and add their partial sums
+    into Y. One-hot X rows must still give the weights exactly."""
+    cfg = synth.Config("kslice", 8, (("w", 333, 4160),), 0.02, "normal", 0.002, 0.0, 12, (1,))
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w, 256)
+    assert m.h.n_raw > 0
+    planes = _planes(m)
+    wf = synth.bf16_bits_to_f32(w)
+    rng = np.random.default_rng(7)
+    for M in (17, 130, 300):
+        ks = rng.integers(0, m.K, M)
+        x = np.zeros((M, m.K), np.uint16)
+        x[np.arange(M), ks] = 0x3F80
+        ref = wf[:, ks].T
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX, uw.W_DIRECT):
+            for v in _variants_for(m, M, src):
+                log(f"  k-slices one-hot M={M} src={src} variant={v}")
+                assert np.array_equal(_run_gemm(m, planes, src, x, v), ref), f"M={M} src={src} v={v}"
+
+
 @pytest.mark.parametrize("N,K", [(512, 256), (200, 192), (333, 4160)])
 def test_gemm_parity_ragged(N, K):
     cfg = synth.Config("rag", 7, (("w", N, K),), 0.02, "normal", 0.001, 0.0, 12, (1,))
