@@ -129,6 +129,64 @@ struct Plane {
     }
 };
 
+// The same loads for a wave whose rows all lie in one 16-row tile (the skinny kernel):
+// a wave-uniform base (held in SGPRs and advanced with scalar adds) plus a fixed 32-bit
+// lane offset, so a load costs no vector address arithmetic.
+template <int SRC>
+struct PlaneS {
+    static constexpr int S0 = Plane<SRC>::S0, S1 = Plane<SRC>::S1;
+    const uint8_t* b0;
+    const uint8_t* b1;
+    uint32_t o0, o1;
+
+    PlaneS() = default;
+    // tile rows [r0, r0 + 16) (r0 wave-uniform), this lane's row r0 + r, weights 16g ..
+    __device__ __forceinline__ PlaneS(const GemmArgs& a, int64_t r0, int r, int g)
+    {
+        if (SRC == UW_W_DIRECT) {
+            int64_t t = r0 >> 4;
+            t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
+            b0 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * (a.K >> 6));
+            b1 = b0;
+            const uint32_t l = 16 * g + r;
+            o0 = 16 * l;
+            o1 = 1024 + 8 * l;
+        } else {
+            // rows past N read row N - 1 (their outputs are never stored)
+            const int64_t rc0 = r0 < a.N ? r0 : a.N - 1;
+            const int64_t row = r0 + r < a.N ? r0 + r : a.N - 1;
+            const uint32_t e = static_cast<uint32_t>((row - rc0) * a.K + 16 * g);  // element offset
+            if (SRC == UW_W_BF16) {
+                b0 = static_cast<const uint8_t*>(a.wplane) + 2 * rc0 * a.K;
+                b1 = b0 + 16;
+                o0 = o1 = 2 * e;
+            } else if (SRC == UW_W_EXP) {
+                b0 = a.sm + rc0 * a.K;
+                b1 = static_cast<const uint8_t*>(a.wplane) + rc0 * a.K;
+                o0 = o1 = e;
+            } else {
+                b0 = a.sm + rc0 * a.K;
+                b1 = static_cast<const uint8_t*>(a.wplane) + rc0 * a.K / 2;
+                o0 = e;
+                o1 = e / 2;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load(uint32_t j, W16& w) const
+    {
+        w.a = *reinterpret_cast<const u32x4*>(b0 + static_cast<int64_t>(S0) * j + o0);
+        const uint8_t* q = b1 + static_cast<int64_t>(S1) * j + o1;
+        if (SRC == UW_W_BF16 || SRC == UW_W_EXP) {
+            w.b = *reinterpret_cast<const u32x4*>(q);
+        } else {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(q);
+            w.b.x = v.x;
+            w.b.y = v.y;
+        }
+    }
+};
+
 // Verbatim exponents of a raw group (16 of them, from k0 & 63), natural order.
 __device__ __forceinline__ u32x4 raw_exps16(const GemmArgs& a, int64_t row, int64_t k0, uint32_t j, uint32_t bw)
 {
@@ -225,7 +283,7 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // per-lane select in the rebuild. Index plane: the rebuild yields (sign, palette[0],
 // mantissa) for raw groups and the exact difference to the true weights is added after
 // the loop with extra MFMAs, from metadata fetched when the kernel starts.
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 {
     static_assert(U % 2 == 0, "ring depth must be even");
@@ -245,24 +303,27 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 #pragma unroll
         for (int c = 0; c < CT; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    Plane<SRC> pl[RT];
-    const uint8_t* pmeta[RT];
+    PlaneS<SRC> pl[RT];
 #pragma unroll
-    for (int i = 0; i < RT; i++) {
-        const int64_t rr = nb + 16 * i + r;
-        pl[i] = Plane<SRC>(a, DIRECT ? rr : (rr < a.N ? rr : a.N - 1), g);
-        if (DIRECT) {
-            int64_t t = (nb >> 4) + i;
-            t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-            pmeta[i] = a.dmeta + 8 * t * G;
-        }
+    for (int i = 0; i < RT; i++) pl[i] = PlaneS<SRC>(a, nb + 16 * i, r, g);
+    // direct plane: lane i < RT fetches the meta (raw-row mask, side base) of row tile i,
+    // so a slot's metas are one vector load, retired in order with the slot's other loads
+    // (scalar loads may return out of order and would have to be waited for at once)
+    const uint8_t* pmeta = nullptr;
+    if (DIRECT) {
+        int64_t t = (nb >> 4) + (lane < RT ? lane : 0);
+        t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
+        pmeta = a.dmeta + 8 * t * G;
     }
-    const uint16_t* xrow[CT];
+    // X: uniform base a.x + 64 j, lane offset of row min(16c + r, M - 1), k 16g (bytes;
+    // the host keeps 2 * M * ldx below 2^32 for this kernel)
+    uint32_t xoff[CT];
 #pragma unroll
     for (int c = 0; c < CT; c++) {
         const int64_t m = 16 * c + r;
-        xrow[c] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
+        xoff[c] = static_cast<uint32_t>(2 * ((m < a.M ? m : a.M - 1) * a.ldx + 16 * g));
     }
+    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(a.x);
 
     // Index plane: raw-group metadata of this wave's rows (local rows wave + NW * q),
     // fetched now and consumed after the main loop: lane q holds row_base of row q, and
@@ -289,28 +350,38 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
     auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < CT; c++) {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[c] + 64 * static_cast<int64_t>(j));
+            const u32x4* xp = reinterpret_cast<const u32x4*>(xb + 128 * static_cast<int64_t>(j) + xoff[c]);
             B[c][0] = xp[0];
             B[c][1] = xp[1];
         }
     };
     W16 ring[U][RT];
-    u32x4 xr[U][CT][2];
-    u32x2 mr[DIRECT ? U : 1][RT];  // direct: raw-row mask and side base of the slot's block
+    u32x4 xr[XNEAR ? 1 : U][CT][2];
+    u32x2 mr[DIRECT ? U : 1];  // direct: lane i holds the slot's (raw-row mask, side base) of row tile i
     u32x4 rx[DIRECT ? U : 1][RT];  // direct: this lane's raw exponents for the slot's group
     auto load_slot = [&](uint32_t j, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
+        // the meta goes first: it is read half a ring turn later, and waiting for it must
+        // not wait for the slot's W loads
+        if (DIRECT) mr[u % (DIRECT ? U : 1)] = *reinterpret_cast<const u32x2*>(pmeta + 8 * static_cast<int64_t>(j));
 #pragma unroll
-        for (int i = 0; i < RT; i++) {
-            pl[i].load(j, ring[u][i]);
-            if (DIRECT) mr[u % (DIRECT ? U : 1)][i] = *reinterpret_cast<const u32x2*>(pmeta[i] + 8 * static_cast<int64_t>(j));
-        }
+        for (int i = 0; i < RT; i++) pl[i].load(j, ring[u][i]);
     };
     auto load_raw = [&](uint32_t j, auto vc) __attribute__((always_inline)) {
         constexpr int v = decltype(vc)::value % (DIRECT ? U : 1);
 #pragma unroll
         for (int i = 0; i < RT; i++)
-            rx[v][i] = *raw_exp_addr(a, mr[v][i], r, g, pl[i].p0 + static_cast<int64_t>(Plane<SRC>::S0) * j);
+        {
+            // the block's raw-row mask is the same in every lane, and most blocks have no raw
+            // row: then skip the address arithmetic and read the (always readable) meta
+            // section instead. The load itself is always issued, so every wait in the loop
+            // stays a counted one.
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.dmeta);
+            const u32x2 meta = {static_cast<uint32_t>(__builtin_amdgcn_readlane(mr[v].x, i)),
+                                static_cast<uint32_t>(__builtin_amdgcn_readlane(mr[v].y, i))};
+            if (meta.x) src = raw_exp_addr(a, meta, r, g, a.dmeta);
+            rx[v][i] = *src;
+        }
     };
     // one group: rebuild ring slot u (group t), refill it with group t + U, request the
     // raw exponents of group t + U/2, multiply, then refill the X pieces
@@ -322,29 +393,67 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         for (int i = 0; i < RT; i++) {
             rebuild16<SRC, CONTIG>(a, ring[u][i], A[i][0], A[i][1]);
             if (DIRECT) {
-                if ((mr[u % (DIRECT ? U : 1)][i].x >> r) & 1u) rebuild16_raw(ring[u][i], rx[u % (DIRECT ? U : 1)][i], A[i][0], A[i][1]);
+                const uint32_t mask = __builtin_amdgcn_readlane(mr[u % (DIRECT ? U : 1)].x, i);
+                if (mask && ((mask >> r) & 1u)) rebuild16_raw(ring[u][i], rx[u % (DIRECT ? U : 1)][i], A[i][0], A[i][1]);
             }
         }
-        if (refill) load_slot(j + NW * U, uc);
-        if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+        if (XNEAR) {
+            // X one group ahead, in one register set: multiply, request the next group's X
+            // (before the W refill, so waiting for it never waits for that refill), then
+            // refill the W slot
 #pragma unroll
-        for (int s2 = 0; s2 < 2; s2++)
+            for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-            for (int i = 0; i < RT; i++)
+                for (int i = 0; i < RT; i++)
 #pragma unroll
-                for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[u][c][s2], acc[i][c]);
-        if (refill) load_x(j + NW * U, xr[u]);
+                    for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[0][c][s2], acc[i][c]);
+            if (refill || t + 1 < T) load_x(j + NW, xr[0]);  // unconditional in the steady state
+            if (refill) load_slot(j + NW * U, uc);
+            if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+        } else {
+            // issue order is pinned: the raw exponents consumed half a turn from now, then
+            // the W slot refill (a full turn ahead), the MFMAs, the X refill; waiting for any
+            // of them then never waits for a younger request
+            __builtin_amdgcn_sched_barrier(0);
+            if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+            if (refill) load_slot(j + NW * U, uc);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[u][c][s2], acc[i][c]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (refill) load_x(j + NW * U, xr[u]);
+        }
     };
-    [&]<int... us>(std::integer_sequence<int, us...>) {
-        ((static_cast<uint32_t>(us) < T ? (load_slot(wave + NW * us, std::integral_constant<int, us>{}),
-                                           load_x(wave + NW * us, xr[us]))
-                                        : void()),
-         ...);
-        if (DIRECT)
-            ((us < U / 2 && static_cast<uint32_t>(us) < T ? load_raw(wave + NW * us, std::integral_constant<int, us>{})
-                                                          : void()),
-             ...);
-    }(std::make_integer_sequence<int, U>{});
+    // The ring is filled with no conditions (slots past the wave's last group reload that
+    // group): the compiler's wait counts at the loop head are the minimum over every path
+    // into it, so a skipped load on any path would make it wait for nearly all loads in
+    // flight, once per ring turn.
+    if (T > 0) {
+        const auto jc = [&](int k) __attribute__((always_inline)) {
+            return wave + NW * (static_cast<uint32_t>(k) < T ? static_cast<uint32_t>(k) : T - 1);
+        };
+        [&]<int... us>(std::integer_sequence<int, us...>) {
+            if (XNEAR) {
+                (load_slot(jc(us), std::integral_constant<int, us>{}), ...);
+                if (DIRECT) ((us < U / 2 ? load_raw(jc(us), std::integral_constant<int, us>{}) : void()), ...);
+                load_x(wave, xr[0]);
+            } else {
+                // the steady state's issue order: the raw exponents of slot k - U/2, slot k's
+                // meta and W, slot k's X
+                auto first = [&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    if (DIRECT && k >= U / 2) load_raw(jc(k - U / 2), std::integral_constant<int, (k + U / 2) % U>{});
+                    load_slot(jc(k), kc);
+                    load_x(jc(k), xr[XNEAR ? 0 : k]);
+                };
+                (first(std::integral_constant<int, us>{}), ...);
+            }
+        }(std::make_integer_sequence<int, U>{});
+    }
     uint32_t t0 = 0;
     // steady state: every slot is consumed and refilled, no guards, so the compiler waits
     // for exactly the slot it needs
@@ -898,6 +1007,7 @@ struct Variant {
     int kind;  // 0 skinny, 1 tiled, 2 wide
     int rt, nw, u;
     int bn, bm;
+    int xnear;  // skinny: X one group ahead in one register set instead of with the ring
 };
 
 const Variant kVariants[] = {
@@ -906,6 +1016,8 @@ const Variant kVariants[] = {
     {"skinny rt2 u4 w8", 0, 2, 8, 4, 0, 0},  {"skinny rt4 u2 w4", 0, 4, 4, 2, 0, 0},
     {"tiled 128x128", 1, 0, 0, 0, 128, 128}, {"tiled 128x64", 1, 0, 0, 0, 128, 64},
     {"tiled 256x128", 1, 0, 0, 0, 256, 128}, {"wide 256x256", 2, 0, 0, 0, 256, 256},
+    {"skinny rt4 u4 w4", 0, 4, 4, 4, 0, 0},  {"skinny rt4 u2 w8 x1", 0, 4, 8, 2, 0, 0, 1},
+    {"skinny rt4 u2 w4 x1", 0, 4, 4, 2, 0, 0, 1}, {"skinny rt2 u4 w8 x1", 0, 2, 8, 4, 0, 0, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -919,26 +1031,26 @@ hipError_t allow_lds(const void* fn, size_t bytes, bool& done)
     return e;
 }
 
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR>
 hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
     constexpr size_t lds = static_cast<size_t>(NW) * RT * CT * 256 * 4;
     static bool attr_done = false;  // benign race: every writer stores the same value
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW>), lds, attr_done);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR>), lds, attr_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW>), grid, dim3(64 * NW), lds, s, g);
+    hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR>), grid, dim3(64 * NW), lds, s, g);
     return hipGetLastError();
 }
 
-template <int SRC, bool CONTIG, int RT, int U, int NW>
+template <int SRC, bool CONTIG, int RT, int U, int NW, bool XNEAR = false>
 hipError_t launch_skinny_rt(const GemmArgs& g, hipStream_t s)
 {
     const int ct = static_cast<int>((g.M + 15) / 16);
     switch (ct) {
-    case 1: return launch_skinny_ct<SRC, CONTIG, 1, RT, U, NW>(g, s);
-    case 2: return launch_skinny_ct<SRC, CONTIG, 2, RT, U, NW>(g, s);
-    default: return launch_skinny_ct<SRC, CONTIG, 4, RT, U, NW>(g, s);
+    case 1: return launch_skinny_ct<SRC, CONTIG, 1, RT, U, NW, XNEAR>(g, s);
+    case 2: return launch_skinny_ct<SRC, CONTIG, 2, RT, U, NW, XNEAR>(g, s);
+    default: return launch_skinny_ct<SRC, CONTIG, 4, RT, U, NW, XNEAR>(g, s);
     }
 }
 
@@ -1027,6 +1139,10 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
         if (v.rt == 1) return launch_skinny_rt<SRC, CONTIG, 1, 4, 4>(g, s);
         if (v.rt == 2 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8>(g, s);
         if (v.rt == 2) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4>(g, s);
+        if (v.xnear && v.rt == 4 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 4, 2, 8, true>(g, s);
+        if (v.xnear && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, true>(g, s);
+        if (v.xnear) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8, true>(g, s);
+        if (v.rt == 4 && v.u == 4) return launch_skinny_rt<SRC, CONTIG, 4, 4, 4>(g, s);
         return launch_skinny_rt<SRC, CONTIG, 4, 2, 4>(g, s);
     }
     if (v.bn == 128 && v.bm == 128) return launch_tiled_t<SRC, CONTIG, 128, 128>(g, s);
@@ -1041,9 +1157,12 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
     (void)K;
     (void)src;
     if (M <= 64) {
+        // the most rows per workgroup (X reused across more weight rows) that still gives
+        // ~200 workgroups of 16 * rt rows
         const int64_t tiles = (N + 15) / 16;  // 16-row tiles
-        if (M > 16) return tiles >= 1024 ? 3 : 2;
-        return tiles >= 2048 ? 0 : tiles >= 512 ? 1 : 2;
+        if (tiles >= 4 * 200) return 5;       // rt4 u2 w4
+        if (tiles >= 2 * 200) return 3;       // rt2 u4 w4
+        return M > 16 ? 2 : 1;                // rt1 u4 w4 / rt1 u4 w8
     }
     // the 128 x 128 or the 256 x 256 kernel, each with its best K split
     const double t_tiled = plan_slices(kTiledModel, N, K, M, 128, 128).us;
@@ -1068,6 +1187,8 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     int v = p->variant < 0 ? default_variant(h->N, h->K, p->M, p->src) : p->variant;
     if (v >= kNumVariants) return fail(UW_EINVAL, "variant %d out of range", v);
     if (!uw_variant_supports(v, h->N, h->K, p->M, p->src)) return fail(UW_EUNSUPPORTED, "variant %d does not support this problem", v);
+    if (kVariants[v].kind == 0 && 2 * p->M * p->ldx + 32 * h->K >= (int64_t{1} << 32))
+        return fail(UW_EUNSUPPORTED, "variant %d addresses X and W with 32-bit offsets: ldx or K too large", v);
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
     g.x = p->d_x;
@@ -1135,7 +1256,7 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
     (void)src;
     if (variant < 0 || variant >= uw::kNumVariants || K % 64 || K < 64) return 0;
     const uw::Variant& v = uw::kVariants[variant];
-    if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
+    if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }
 

@@ -445,3 +445,10 @@ def test_mlp_stack_forward_one_and_two_streams():
     assert (np.abs(hg.astype(np.int32) - href.astype(np.int32)) <= 1).all()
     yr, ar = oracle.gemm(hg, down.w)
     check_gemm(y, yr, ar, "stack last layer down")
+
+
+def test_graft_smoke_entry():
+    """The packaged smoke check (one tiny decode + direct-palette GEMM against the oracle)."""
+    import __graft_entry__
+
+    __graft_entry__.smoke()
