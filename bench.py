@@ -444,7 +444,43 @@ def stack_sweep(uw, synth, torch, dev, stream, log, Ms):
             del ws
         rows[str(M)] = row
         log(f"[bench] stack M={M}: {row}")
-    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows}
+
+    # decode-first plans (the best of full / exponent / transcode per shape) with the
+    # preprocessing on one stream, on a second stream, and on CU-split stream pairs
+    split = {}
+    for M in (1, 16, 64):
+        plans = {}
+        for q, Kin, Nout in ((0, K, Nff), (2, Nff, K)):
+            xq = torch.from_numpy(synth.gen_x(cfg, M, Kin).view(np.int16)).to(dev)
+            yq = torch.empty(M, Nout, dtype=torch.float32, device=dev)
+            plans[q] = uw.autotune(hs[q], d_blobs[q], xq, yq, [M], d_ws=ws_t, ws_bytes=ws_t.numel(), reps=5,
+                                   warmup=2, pipeline_mask=0b0111)[0]
+        arr = uw.mlp_layers([[uw.proj(hs[3 * l + q], d_blobs[3 * l + q], plans[0 if q < 2 else 2].pipeline,
+                                      variant=plans[0 if q < 2 else 2].variant) for q in range(3)] for l in range(L)])
+        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, K, dtype=torch.float32, device=dev)
+        row = {"gate_up_plan": f"{uw.PIPELINE_NAMES[plans[0].pipeline]} / {uw.variant_name(plans[0].variant)}",
+               "down_plan": f"{uw.PIPELINE_NAMES[plans[2].pipeline]} / {uw.variant_name(plans[2].variant)}"}
+        for mode in ("one_stream", "two_streams", "cu_split_32", "cu_split_64", "cu_split_128"):
+            two = mode != "one_stream"
+            nb = uw.mlp_stack_workspace(arr, M, two_slots=two)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            pair = uw.stream_pair_create(int(mode.rsplit("_", 1)[1])) if mode.startswith("cu_split") else None
+            main = torch.cuda.ExternalStream(pair[0]) if pair else stream
+            dec = pair[1] if pair else (side if two else None)
+            torch.cuda.synchronize()
+            fwd = lambda r: uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=main, decode_stream=dec)
+            fwd(0)
+            ms = timed(torch, main, fwd, reps=3)
+            torch.cuda.synchronize()
+            if pair:
+                uw.stream_destroy(pair[0])
+                uw.stream_destroy(pair[1])
+            row[mode] = {"ms": round(ms, 3), "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+            del ws
+        split[str(M)] = row
+        log(f"[bench] stack decode-first M={M}: {row}")
+    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows, "decode_first": split}
 
 
 def configs_sweep(uw, synth, torch, dev, stream, log):

@@ -109,7 +109,8 @@ def _preload_torch_hip():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libuw.so not built at {LIB_PATH}; run `python -m decode_gemm_amd.build`")
+        raise ImportError(f"libuw.so not built at {LIB_PATH}; run `python decode_gemm_amd/build.py` "
+                          "or __graft_entry__.build()")
     _preload_torch_hip()
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
@@ -138,6 +139,9 @@ def _load():
         "uw_mlp_stack_workspace": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, ctypes.c_int, ctypes.POINTER(sz)],
                                    ctypes.c_int),
         "uw_mlp_stack_forward": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, P, P, P, sz, P, P], ctypes.c_int),
+        "uw_stream_pair_create": ([ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)], ctypes.c_int),
+        "uw_stream_destroy": ([P], ctypes.c_int),
+        "uw_stream_cu_count": ([P, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -302,3 +306,22 @@ def mlp_stack_forward(layers: ctypes.Array, M: int, d_x, d_y, d_ws, ws_bytes: in
     layer's output. decode_stream (optional) decodes one projection ahead."""
     _check(lib.uw_mlp_stack_forward(layers, len(layers), M, _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes,
                                     _stream(stream), None if decode_stream is None else _stream(decode_stream)))
+
+
+def stream_pair_create(decode_cus: int):
+    """uw_stream_pair_create: (gemm_stream, decode_stream) handles on disjoint compute units,
+    decode_cus of them for the decode stream. Wrap with torch.cuda.ExternalStream to use them
+    from torch; release with stream_destroy."""
+    g, d = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib.uw_stream_pair_create(decode_cus, ctypes.byref(g), ctypes.byref(d)))
+    return g.value, d.value
+
+
+def stream_destroy(handle: int) -> None:
+    _check(lib.uw_stream_destroy(handle))
+
+
+def stream_cu_count(stream=None) -> int:
+    out = ctypes.c_int(0)
+    _check(lib.uw_stream_cu_count(_stream(stream), ctypes.byref(out)))
+    return out.value

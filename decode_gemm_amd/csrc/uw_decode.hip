@@ -839,6 +839,23 @@ uint32_t cu_count()
     return static_cast<uint32_t>(cached[dev]);
 }
 
+// Compute units a stream's work may run on: its CU mask's population (all of the device
+// for the null stream or when the mask cannot be read).
+uint32_t stream_cu_count(void* stream)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t cus = cu_count();
+    if (!s) return cus;
+    uint32_t mask[32] = {};
+    if (hipExtStreamGetCUMask(s, 32, mask) != hipSuccess) {
+        (void)hipGetLastError();
+        return cus;
+    }
+    uint32_t n = 0;
+    for (uint32_t w : mask) n += static_cast<uint32_t>(__builtin_popcount(w));
+    return n == 0 || n > cus ? cus : n;
+}
+
 template <int MODE>
 hipError_t launch_lut(const lut::Args& f, uint32_t blocks, uint32_t waves, hipStream_t s)
 {
@@ -942,8 +959,10 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
                               (static_cast<uint32_t>(vmap[t.sorted[r] & 15]) << 20);
         std::memcpy(f.pal, h->palette, 16);
         f.simple = (h->chunk & (h->chunk - 1)) == 0 && h->K % h->chunk == 0;
-        // equal rounds: every wave of the persistent grid gets the same number of tasks
-        const uint32_t cus = cu_count();
+        // equal rounds: every wave of the persistent grid gets the same number of tasks; the
+        // grid is one workgroup per compute unit the stream may use (a CU-masked stream of
+        // uw_stream_pair_create runs the decoder on a slice of the device)
+        const uint32_t cus = stream_cu_count(s);
         const uint32_t rounds = (f.n_tasks + cus * lut::kMaxWaves - 1) / (cus * lut::kMaxWaves);
         const uint32_t waves = (f.n_tasks + cus * rounds - 1) / (cus * rounds);
         const uint32_t blocks = (f.n_tasks + waves * rounds - 1) / (waves * rounds);

@@ -55,6 +55,7 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
 uw_status launch_gemm(const uw_gemm_args* a, void* stream);
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
 uint32_t cu_count();  // compute units of the current device
+uint32_t stream_cu_count(void* stream);  // compute units a hipStream_t may use (its CU mask)
 uint64_t direct_plane_bytes(const uw_header* h);
 
 bool aligned(const void* p, size_t a);

@@ -391,4 +391,61 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
     }
 }
 
+// ---------------------------------------------------------------- CU-split streams
+// Decode next to the GEMM ("Sharing the GPU between decode and compute"): two streams on
+// disjoint compute units, so a projection's preprocessing can run beside another's
+// reconstructive GEMM without either queueing behind the other's workgroups.
+uw_status uw_stream_pair_create(int decode_cus, void** gemm_stream, void** decode_stream)
+{
+    using namespace uw;
+    clear_error();
+    if (!gemm_stream || !decode_stream) return fail(UW_EINVAL, "NULL output");
+    if (decode_cus < 1) return fail(UW_EINVAL, "decode_cus must be >= 1");
+    const uint32_t T = cu_count();
+    if (static_cast<uint32_t>(decode_cus) >= T) return fail(UW_EINVAL, "decode_cus must be < %u", T);
+    // The decoder's compute units are spread over the XCDs (T / 8 CUs each when T % 8 == 0):
+    // XCD x gives its share at positions k * P / n + x (mod P), so whether the mask bits
+    // number the CUs XCD by XCD or round-robin over the XCDs, every XCD keeps both kinds.
+    const uint32_t X = T % 8 == 0 ? 8 : 1, P = T / X, d = static_cast<uint32_t>(decode_cus);
+    const uint32_t words = (T + 31) / 32;
+    std::vector<uint32_t> dm(words, 0u), gm(words, 0u);
+    for (uint32_t i = 0; i < T; i++) gm[i / 32] |= 1u << (i % 32);
+    for (uint32_t x = 0; x < X; x++) {
+        const uint32_t n = d / X + (x < d % X ? 1u : 0u);
+        for (uint32_t k = 0; k < n; k++) {
+            const uint32_t i = x * P + (k * P / n + x) % P;
+            dm[i / 32] |= 1u << (i % 32);
+            gm[i / 32] &= ~(1u << (i % 32));
+        }
+    }
+    hipStream_t g = nullptr, dd = nullptr;
+    if (hipExtStreamCreateWithCUMask(&g, words, gm.data()) != hipSuccess)
+        return fail(UW_EHIP, "hipExtStreamCreateWithCUMask failed");
+    if (hipExtStreamCreateWithCUMask(&dd, words, dm.data()) != hipSuccess) {
+        (void)hipStreamDestroy(g);
+        return fail(UW_EHIP, "hipExtStreamCreateWithCUMask failed");
+    }
+    *gemm_stream = g;
+    *decode_stream = dd;
+    return UW_OK;
+}
+
+uw_status uw_stream_destroy(void* stream)
+{
+    using namespace uw;
+    clear_error();
+    if (!stream) return fail(UW_EINVAL, "NULL stream");
+    if (hipStreamDestroy(static_cast<hipStream_t>(stream)) != hipSuccess) return fail(UW_EHIP, "hipStreamDestroy failed");
+    return UW_OK;
+}
+
+uw_status uw_stream_cu_count(void* stream, int* out)
+{
+    using namespace uw;
+    clear_error();
+    if (!out) return fail(UW_EINVAL, "NULL output");
+    *out = static_cast<int>(stream_cu_count(stream));
+    return UW_OK;
+}
+
 }  // extern "C"

@@ -328,6 +328,25 @@ uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64
 uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y,
                                void* d_ws, size_t ws_bytes, void* stream, void* decode_stream);
 
+/*
+ * CU-split streams ("Sharing the GPU between decode and compute": the preprocessing of one
+ * projection runs on a slice of the compute units while the reconstructive GEMM of another
+ * runs on the rest, so neither waits behind the other's workgroups).
+ *
+ * uw_stream_pair_create (host): two new HIP streams, both at the default priority, on
+ * disjoint compute units: decode_cus of the device's CUs (spread evenly over its XCDs) for
+ * *decode_stream, all the others for *gemm_stream. Pass them to uw_mlp_stack_forward as
+ * (stream, decode_stream), or use them with any entry point; the persistent decoders size
+ * their grids to the stream's CUs. The caller owns both and releases them with
+ * uw_stream_destroy. Errors: UW_EINVAL (NULL outputs, decode_cus < 1 or >= the device's
+ * CUs), UW_EHIP.
+ * uw_stream_cu_count (host): the compute units a stream may use (its CU mask; the whole
+ * device for the null stream).
+ */
+uw_status uw_stream_pair_create(int decode_cus, void** gemm_stream, void** decode_stream);
+uw_status uw_stream_destroy(void* stream);
+uw_status uw_stream_cu_count(void* stream, int* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -447,6 +447,61 @@ def test_mlp_stack_forward_one_and_two_streams():
     check_gemm(y, yr, ar, "stack last layer down")
 
 
+def test_cu_split_streams_decode_and_stack_forward():
+    """Streams on disjoint compute units: their CU counts add up to the device's, the
+    persistent decoder on the decode slice is still bit-exact, and the stack forward with
+    its preprocessing on the decode slice gives the same Y as on one stream."""
+    torch = torch_cuda()
+    total = uw.stream_cu_count(0)
+    gs, ds = uw.stream_pair_create(48)
+    try:
+        assert uw.stream_cu_count(ds) == 48
+        assert uw.stream_cu_count(gs) == total - 48
+        w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+        m = Mat(w, 256)
+        ref = m.ref()
+        out = empty_u8(m.N * m.K // 2)
+        err = zeros_u32()
+        uw.transcode_palette(m.h, m.d_blob, out, err, stream=ds)
+        _sync()
+        assert int(host(err)[0]) == 0 and (host(out) == ref["idx"]).all()
+        rng = np.random.default_rng(73)
+        K, F, M = 256, 512, 9
+        x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+        keep, layers = [], []
+        for l in range(3):
+            trip = []
+            for q, (n, k) in enumerate(((F, K), (F, K), (K, F))):
+                wl = synth.f32_to_bf16_bits(rng.standard_normal((n, k), dtype=np.float32) * 0.05)
+                ml = Mat(wl, 256)
+                keep.append(ml)
+                trip.append(uw.proj(ml.h, ml.d_blob, (uw.PIPE_TRANSCODE, uw.PIPE_EXP, uw.PIPE_FULL)[(l + q) % 3]))
+            layers.append(trip)
+        arr = uw.mlp_layers(layers)
+        d_x = dev(x)
+        ys = []
+        for split in (False, True):
+            nbytes = uw.mlp_stack_workspace(arr, M, two_slots=split)
+            ws = empty_u8(nbytes + 256)
+            y = empty_f32(M, K)
+            y.fill_(float("nan"))
+            _sync()
+            log(f"  stack forward on CU-split streams: {split}")
+            if split:
+                uw.mlp_stack_forward(arr, M, d_x, y, ws, nbytes, stream=gs, decode_stream=ds)
+            else:
+                uw.mlp_stack_forward(arr, M, d_x, y, ws, nbytes)
+            _sync()
+            ys.append(host(y))
+        assert np.isfinite(ys[0]).all()
+        assert np.array_equal(ys[0], ys[1])
+        del torch
+    finally:
+        _sync()
+        uw.stream_destroy(gs)
+        uw.stream_destroy(ds)
+
+
 def test_graft_smoke_entry():
     """The packaged smoke check (one tiny decode + direct-palette GEMM against the oracle)."""
     import __graft_entry__

@@ -237,3 +237,20 @@ def test_mlp_stack_host_checks():
     with pytest.raises(uw.UwError) as e:
         uw.mlp_stack_forward(good, M, fake, fake, fake, 16, stream=0)
     assert e.value.status == uw.ENOSPACE
+
+
+def test_stream_pair_argument_checks():
+    """uw_stream_pair_create rejects NULL outputs and an empty decode share before it
+    touches the device."""
+    P = ctypes.c_void_p
+    g, d = P(), P()
+    assert uw.lib.uw_stream_pair_create(8, None, ctypes.byref(d)) == uw.EINVAL
+    assert uw.lib.uw_stream_pair_create(8, ctypes.byref(g), None) == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.stream_pair_create(0)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.stream_pair_create(-3)
+    assert e.value.status == uw.EINVAL
+    assert uw.lib.uw_stream_destroy(None) == uw.EINVAL
+    assert uw.lib.uw_stream_cu_count(None, None) == uw.EINVAL
