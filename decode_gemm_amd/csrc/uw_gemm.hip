@@ -283,10 +283,11 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // per-lane select in the rebuild. Index plane: the rebuild yields (sign, palette[0],
 // mantissa) for raw groups and the exact difference to the true weights is added after
 // the loop with extra MFMAs, from metadata fetched when the kernel starts.
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 {
     static_assert(U % 2 == 0, "ring depth must be even");
+    static_assert(!(XNEAR && XT), "one X scheme");
     constexpr bool DIRECT = SRC == UW_W_DIRECT;
     constexpr bool POSTRAW = SRC == UW_W_IDX;
     extern __shared__ float red[];
@@ -323,6 +324,21 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         const int64_t m = 16 * c + r;
         xoff[c] = static_cast<uint32_t>(2 * ((m < a.M ? m : a.M - 1) * a.ldx + 16 * g));
     }
+    // XT: X is read as whole 128-byte row segments instead (load q: rows 8q .. 8q+7 of the
+    // group, lane l = row 8q + l / 8, 16 bytes l % 8) and put into operand order through a
+    // wave-private LDS tile, rows 144 bytes apart so the fragment reads hit distinct banks.
+    // A fragment load otherwise touches 16 rows at 64 bytes each and costs the address
+    // unit twice the lines per byte.
+    constexpr int XS_PITCH = 9;  // 16-byte units per LDS row
+    uint32_t xofft[XT ? 2 * CT : 1];
+    if (XT) {
+#pragma unroll
+        for (int q = 0; q < 2 * CT; q++) {
+            const int64_t m = 8 * q + (lane >> 3);
+            xofft[q] = static_cast<uint32_t>(2 * ((m < a.M ? m : a.M - 1) * a.ldx + 8 * (lane & 7)));
+        }
+    }
+    u32x4* const xs = reinterpret_cast<u32x4*>(red) + wave * (16 * CT * XS_PITCH);
     const uint8_t* const xb = reinterpret_cast<const uint8_t*>(a.x);
 
     // Index plane: raw-group metadata of this wave's rows (local rows wave + NW * q),
@@ -347,12 +363,27 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         }
     }
 
-    auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) __attribute__((always_inline)) {
+    // X pieces of group j in MFMA operand order (the post-loop raw correction)
+    auto load_x_frag = [&](uint32_t j, u32x4 (&B)[CT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < CT; c++) {
             const u32x4* xp = reinterpret_cast<const u32x4*>(xb + 128 * static_cast<int64_t>(j) + xoff[c]);
             B[c][0] = xp[0];
             B[c][1] = xp[1];
+        }
+    };
+    // X of group j for the ring: operand order, or row segments for XT
+    auto load_x = [&](uint32_t j, u32x4 (&B)[CT][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CT; c++) {
+            if (XT) {
+                B[c][0] = *reinterpret_cast<const u32x4*>(xb + 128 * static_cast<int64_t>(j) + xofft[XT ? 2 * c : 0]);
+                B[c][1] = *reinterpret_cast<const u32x4*>(xb + 128 * static_cast<int64_t>(j) + xofft[XT ? 2 * c + 1 : 0]);
+            } else {
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xb + 128 * static_cast<int64_t>(j) + xoff[c]);
+                B[c][0] = xp[0];
+                B[c][1] = xp[1];
+            }
         }
     };
     W16 ring[U][RT];
@@ -388,6 +419,18 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
     auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         const uint32_t j = wave + NW * t;
+        u32x4 XF[XT ? CT : 1][2];  // XT: this step's X fragments, back from the LDS tile
+        if (XT) {
+#pragma unroll
+            for (int q = 0; q < 2 * CT; q++) xs[(8 * q + (lane >> 3)) * XS_PITCH + (lane & 7)] = xr[XNEAR ? 0 : u][q >> 1][q & 1];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int c = 0; c < CT; c++)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; s2++) XF[XT ? c : 0][s2] = xs[(16 * c + r) * XS_PITCH + 2 * g + s2];
+        }
         u32x4 A[RT][2];
 #pragma unroll
         for (int i = 0; i < RT; i++) {
@@ -423,7 +466,8 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 #pragma unroll
                 for (int i = 0; i < RT; i++)
 #pragma unroll
-                    for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[u][c][s2], acc[i][c]);
+                    for (int c = 0; c < CT; c++)
+                        acc[i][c] = mfma16(A[i][s2], XT ? XF[XT ? c : 0][s2] : xr[u][c][s2], acc[i][c]);
             __builtin_amdgcn_sched_barrier(0);
             if (refill) load_x(j + NW * U, xr[u]);
         }
@@ -494,7 +538,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
                     if (r == (li & 15)) raw_pieces<SRC>(a, row, j, ri, g, t0v, t1v, u0v, u1v);
                     ri++;
                     u32x4 B[CT][2];
-                    load_x(j, B);
+                    load_x_frag(j, B);
 #pragma unroll
                     for (int i = 0; i < RT; i++) {
                         if (i == (li >> 4)) {
@@ -512,7 +556,9 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         }
     }
 
-    // cross-wave reduction: red[w][i][c][q][lane]
+    // cross-wave reduction: red[w][i][c][q][lane] (XT: over the X tiles, once every wave
+    // is done with its own)
+    if (XT) __syncthreads();
     constexpr int TILES = RT * CT;
 #pragma unroll
     for (int i = 0; i < RT; i++)
@@ -1008,6 +1054,7 @@ struct Variant {
     int rt, nw, u;
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
+    int xt;     // skinny: X read as whole row segments and put in operand order through LDS
 };
 
 const Variant kVariants[] = {
@@ -1018,6 +1065,8 @@ const Variant kVariants[] = {
     {"tiled 256x128", 1, 0, 0, 0, 256, 128}, {"wide 256x256", 2, 0, 0, 0, 256, 256},
     {"skinny rt4 u4 w4", 0, 4, 4, 4, 0, 0},  {"skinny rt4 u2 w8 x1", 0, 4, 8, 2, 0, 0, 1},
     {"skinny rt4 u2 w4 x1", 0, 4, 4, 2, 0, 0, 1}, {"skinny rt2 u4 w8 x1", 0, 2, 8, 4, 0, 0, 1},
+    {"skinny rt4 u2 w4 xt", 0, 4, 4, 2, 0, 0, 0, 1}, {"skinny rt4 u4 w4 xt", 0, 4, 4, 4, 0, 0, 0, 1},
+    {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1031,26 +1080,28 @@ hipError_t allow_lds(const void* fn, size_t bytes, bool& done)
     return e;
 }
 
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
 hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
-    constexpr size_t lds = static_cast<size_t>(NW) * RT * CT * 256 * 4;
+    constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
+    constexpr size_t xt_bytes = XT ? static_cast<size_t>(NW) * 16 * CT * 9 * 16 : 0;
+    constexpr size_t lds = red_bytes > xt_bytes ? red_bytes : xt_bytes;
     static bool attr_done = false;  // benign race: every writer stores the same value
-    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR>), lds, attr_done);
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), lds, attr_done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR>), grid, dim3(64 * NW), lds, s, g);
+    hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, g);
     return hipGetLastError();
 }
 
-template <int SRC, bool CONTIG, int RT, int U, int NW, bool XNEAR = false>
+template <int SRC, bool CONTIG, int RT, int U, int NW, bool XNEAR = false, bool XT = false>
 hipError_t launch_skinny_rt(const GemmArgs& g, hipStream_t s)
 {
     const int ct = static_cast<int>((g.M + 15) / 16);
     switch (ct) {
-    case 1: return launch_skinny_ct<SRC, CONTIG, 1, RT, U, NW, XNEAR>(g, s);
-    case 2: return launch_skinny_ct<SRC, CONTIG, 2, RT, U, NW, XNEAR>(g, s);
-    default: return launch_skinny_ct<SRC, CONTIG, 4, RT, U, NW, XNEAR>(g, s);
+    case 1: return launch_skinny_ct<SRC, CONTIG, 1, RT, U, NW, XNEAR, XT>(g, s);
+    case 2: return launch_skinny_ct<SRC, CONTIG, 2, RT, U, NW, XNEAR, XT>(g, s);
+    default: return launch_skinny_ct<SRC, CONTIG, 4, RT, U, NW, XNEAR, XT>(g, s);
     }
 }
 
@@ -1139,6 +1190,9 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
         if (v.rt == 1) return launch_skinny_rt<SRC, CONTIG, 1, 4, 4>(g, s);
         if (v.rt == 2 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8>(g, s);
         if (v.rt == 2) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4>(g, s);
+        if (v.xt && v.rt == 4 && v.u == 4) return launch_skinny_rt<SRC, CONTIG, 4, 4, 4, false, true>(g, s);
+        if (v.xt && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, true>(g, s);
+        if (v.xt) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4, false, true>(g, s);
         if (v.xnear && v.rt == 4 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 4, 2, 8, true>(g, s);
         if (v.xnear && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, true>(g, s);
         if (v.xnear) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8, true>(g, s);
@@ -1160,8 +1214,8 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
         // the most rows per workgroup (X reused across more weight rows) that still gives
         // ~200 workgroups of 16 * rt rows
         const int64_t tiles = (N + 15) / 16;  // 16-row tiles
-        if (tiles >= 4 * 200) return 5;       // rt4 u2 w4
-        if (tiles >= 2 * 200) return 3;       // rt2 u4 w4
+        if (tiles >= 4 * 200) return M > 16 ? 14 : 5;  // rt4 u2 w4 (xt: X through LDS)
+        if (tiles >= 2 * 200) return 3;                // rt2 u4 w4
         return M > 16 ? 2 : 1;                // rt1 u4 w4 / rt1 u4 w8
     }
     // the 128 x 128 or the 256 x 256 kernel, each with its best K split
