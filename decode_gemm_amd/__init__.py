@@ -128,6 +128,7 @@ def _load():
         "uw_prepare_direct": ([H, P, P, P, P], ctypes.c_int),
         "uw_direct_plane_bytes": ([H, ctypes.POINTER(sz)], ctypes.c_int),
         "uw_recon_gemm": ([ctypes.POINTER(GemmArgs), P], ctypes.c_int),
+        "uw_recon_gemm_gate_up": ([ctypes.POINTER(GemmArgs), ctypes.POINTER(GemmArgs), P, i64, P], ctypes.c_int),
         "uw_variant_count": ([], ctypes.c_int),
         "uw_variant_name": ([ctypes.c_int], ctypes.c_char_p),
         "uw_variant_supports": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
@@ -257,6 +258,20 @@ def recon_gemm(h: Header, d_blob, src: int, d_wplane, d_x, d_y, M: int, ldx: int
     a = GemmArgs(M, _ptr(d_x), h.K if ldx is None else ldx, ctypes.pointer(h), _ptr(d_blob), src, _ptr(d_wplane),
                  _ptr(d_y), h.N if ldy is None else ldy, variant)
     _check(lib.uw_recon_gemm(ctypes.byref(a), _stream(stream)))
+
+
+def recon_gemm_gate_up(hg: Header, d_blob_g, d_direct_g, hu: Header, d_blob_u, d_direct_u, d_x, d_yg, d_yu, d_h,
+                       M: int, ldx: int | None = None, ldf: int | None = None, variant: int = -1,
+                       stream=None) -> None:
+    """uw_recon_gemm_gate_up: gate and up (direct planes, same X) and h = bf16(silu(g) * u)
+    in one launch; raises UwError(EUNSUPPORTED) where the fused form does not apply."""
+    lx = hg.K if ldx is None else ldx
+    lf = hg.N if ldf is None else ldf
+    ag = GemmArgs(M, _ptr(d_x), lx, ctypes.pointer(hg), _ptr(d_blob_g), W_DIRECT, _ptr(d_direct_g), _ptr(d_yg), lf,
+                  variant)
+    au = GemmArgs(M, _ptr(d_x), lx, ctypes.pointer(hu), _ptr(d_blob_u), W_DIRECT, _ptr(d_direct_u), _ptr(d_yu), lf,
+                  variant)
+    _check(lib.uw_recon_gemm_gate_up(ctypes.byref(ag), ctypes.byref(au), _ptr(d_h), lf, _stream(stream)))
 
 
 def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_direct=None, d_ws=None, ws_bytes: int = 0,

@@ -283,14 +283,16 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // per-lane select in the rebuild. Index plane: the rebuild yields (sign, palette[0],
 // mantissa) for raw groups and the exact difference to the true weights is added after
 // the loop with extra MFMAs, from metadata fetched when the kernel starts.
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
-__global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
+// The block's tile: everything up to its reduced outputs, which go to sink(o, n, m, y) for
+// each Y element (o = the element's index in the block tile) inside [0, N) x [0, M).
+// red: the block's LDS (the cross-wave reduction, and the X tiles with XT).
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT, class Sink>
+__device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&& sink)
 {
     static_assert(U % 2 == 0, "ring depth must be even");
     static_assert(!(XNEAR && XT), "one X scheme");
     constexpr bool DIRECT = SRC == UW_W_DIRECT;
     constexpr bool POSTRAW = SRC == UW_W_IDX;
-    extern __shared__ float red[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
                 if (mask && ((mask >> r) & 1u)) rebuild16_raw(ring[u][i], rx[u % (DIRECT ? U : 1)][i], A[i][0], A[i][1]);
             }
         }
-        if (XNEAR) {
+        if constexpr (XNEAR) {
             // X one group ahead, in one register set: multiply, request the next group's X
             // (before the W refill, so waiting for it never waits for that refill), then
             // refill the W slot
@@ -481,7 +483,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
             return wave + NW * (static_cast<uint32_t>(k) < T ? static_cast<uint32_t>(k) : T - 1);
         };
         [&]<int... us>(std::integer_sequence<int, us...>) {
-            if (XNEAR) {
+            if constexpr (XNEAR) {
                 (load_slot(jc(us), std::integral_constant<int, us>{}), ...);
                 if (DIRECT) ((us < U / 2 ? load_raw(jc(us), std::integral_constant<int, us>{}) : void()), ...);
                 load_x(wave, xr[0]);
@@ -577,8 +579,52 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 #pragma unroll
         for (int w = 0; w < NW; w++) sum += red[((w * TILES + tile) * 4 + q) * 64 + src_lane];
         const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
-        if (n < a.N && m < a.M) a.y[m * a.ldy + n] = sum;
+        if (n < a.N && m < a.M) sink(o, n, m, sum);
     }
+}
+
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+__global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
+{
+    extern __shared__ float red[];
+    skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>(a, red, [&](int, int64_t n, int64_t m, float v) {
+        a.y[m * a.ldy + n] = v;
+    });
+}
+
+// LDS of a skinny block: the cross-wave reduction, or the X tiles with XT (aliased).
+template <int CT, int RT, int NW, bool XT>
+constexpr size_t skinny_lds()
+{
+    constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
+    constexpr size_t xt_bytes = XT ? static_cast<size_t>(NW) * 16 * CT * 9 * 16 : 0;
+    return red_bytes > xt_bytes ? red_bytes : xt_bytes;
+}
+
+// gate and up of a SwiGLU MLP in one launch (direct planes, same X, same shape): each
+// block computes its rows of gate, keeps them in LDS, computes the same rows of up, and
+// writes g, u (fp32) and h = bf16(silu(g) * u). One ramp and one tail instead of three
+// launches, and no separate SwiGLU pass over g and u.
+struct GateUpArgs {
+    GemmArgs gate, up;
+    uint16_t* h;
+    int64_t ldh;
+};
+
+template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+__global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
+{
+    extern __shared__ float red[];
+    float* const gbuf = red + skinny_lds<CT, RT, NW, XT>() / 4;  // RT * CT * 256 gate outputs
+    skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT>(ga.gate, red, [&](int o, int64_t n, int64_t m, float v) {
+        ga.gate.y[m * ga.gate.ldy + n] = v;
+        gbuf[o] = v;
+    });
+    __syncthreads();  // the up pass reuses the reduction / X-tile LDS
+    skinny_tile<UW_W_DIRECT, CU, CT, RT, U, NW, XNEAR, XT>(ga.up, red, [&](int o, int64_t n, int64_t m, float v) {
+        ga.up.y[m * ga.up.ldy + n] = v;
+        ga.h[m * ga.ldh + n] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(gbuf[o], v)));
+    });
 }
 
 // ------------------------------------------------------------------------- tiled
@@ -1084,9 +1130,7 @@ template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool 
 hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
-    constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
-    constexpr size_t xt_bytes = XT ? static_cast<size_t>(NW) * 16 * CT * 9 * 16 : 0;
-    constexpr size_t lds = red_bytes > xt_bytes ? red_bytes : xt_bytes;
+    constexpr size_t lds = skinny_lds<CT, RT, NW, XT>();
     static bool attr_done = false;  // benign race: every writer stores the same value
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), lds, attr_done);
     if (e != hipSuccess) return e;
@@ -1204,7 +1248,78 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
     return launch_tiled_t<SRC, CONTIG, 256, 128>(g, s);
 }
 
+template <int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>((ga.gate.N + 16 * RT - 1) / (16 * RT)));
+    constexpr size_t lds = skinny_lds<CT, RT, NW, XT>() + static_cast<size_t>(RT) * CT * 256 * 4;
+    const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
+    static bool attr_done = false;  // benign race: every writer stores the same value
+    hipError_t e = allow_lds(fn, lds, attr_done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, ga);
+    return hipGetLastError();
+}
+
+template <int RT, int U, int NW, bool XNEAR = false, bool XT = false>
+hipError_t launch_gate_up_rt(const GateUpArgs& ga, hipStream_t s)
+{
+    const int ct = static_cast<int>((ga.gate.M + 15) / 16);
+    switch (ct) {
+    case 1: return launch_gate_up_ct<1, RT, U, NW, XNEAR, XT>(ga, s);
+    case 2: return launch_gate_up_ct<2, RT, U, NW, XNEAR, XT>(ga, s);
+    default: return launch_gate_up_ct<4, RT, U, NW, XNEAR, XT>(ga, s);
+    }
+}
+
+// The skinny variants with a fused gate/up form (the defaults for M <= 64 and their
+// neighbours); the others return hipErrorNotSupported.
+hipError_t launch_gate_up(const GateUpArgs& ga, const Variant& v, hipStream_t s)
+{
+    if (v.kind != 0) return hipErrorNotSupported;
+    if (v.xt && v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4, false, true>(ga, s);
+    if (v.xt || v.xnear) return hipErrorNotSupported;
+    if (v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4>(ga, s);
+    if (v.rt == 2 && v.u == 4 && v.nw == 4) return launch_gate_up_rt<2, 4, 4>(ga, s);
+    if (v.rt == 1 && v.u == 4 && v.nw == 4) return launch_gate_up_rt<1, 4, 4>(ga, s);
+    if (v.rt == 1 && v.u == 4 && v.nw == 8) return launch_gate_up_rt<1, 4, 8>(ga, s);
+    return hipErrorNotSupported;
+}
+
 }  // namespace
+
+uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v);
+
+uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
+                              void* stream)
+{
+    clear_error();
+    if (!gate || !up || !gate->h || !up->h) return fail(UW_EINVAL, "NULL argument");
+    if (gate->src != UW_W_DIRECT || up->src != UW_W_DIRECT)
+        return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM takes direct planes only");
+    if (gate->M != up->M || gate->h->N != up->h->N || gate->h->K != up->h->K)
+        return fail(UW_ESHAPE, "gate and up must have the same M, N and K");
+    if (gate->M < 0) return fail(UW_ESHAPE, "M < 0");
+    if (gate->M == 0) return UW_OK;
+    if (gate->M > 64) return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM takes M <= 64");
+    if (!d_h || !aligned(d_h, 2)) return fail(UW_EINVAL, "NULL or misaligned d_h");
+    if (ldh < gate->h->N) return fail(UW_EINVAL, "ldh must be >= N");
+    GateUpArgs ga;
+    bool cg = false, cu = false;
+    int vg = 0, vu = 0;
+    uw_gemm_args upv = *up;
+    upv.variant = gate->variant;  // one launch, one variant: the gate's
+    uw_status st = make_args(gate, ga.gate, cg, vg);
+    if (st == UW_OK) st = make_args(&upv, ga.up, cu, vu);
+    if (st != UW_OK) return st;
+    if (!cg || !cu) return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM needs palettes of consecutive exponents");
+    ga.h = d_h;
+    ga.ldh = ldh;
+    const hipError_t e = launch_gate_up(ga, kVariants[vg], static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(UW_EUNSUPPORTED, "variant %d has no fused gate/up form", vg);
+    if (e != hipSuccess) return fail(UW_EHIP, "gate/up launch failed: %s", hipGetErrorString(e));
+    return UW_OK;
+}
 
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
 {
@@ -1224,26 +1339,24 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
     return t_wide < t_tiled ? 9 : 6;
 }
 
-uw_status launch_gemm(const uw_gemm_args* p, void* stream)
+// Validate one GEMM's arguments and fill its kernel arguments; v = the variant to run.
+uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
 {
-    clear_error();
     if (!p || !p->h) return fail(UW_EINVAL, "NULL argument");
     const uw_header* h = p->h;
     if (p->M < 0) return fail(UW_ESHAPE, "M < 0");
     if (h->N < 1 || h->K < 1 || h->K % 64) return fail(UW_ESHAPE, "bad W shape");
-    if (p->M == 0) return UW_OK;
     if (!p->d_x || !p->d_y || !p->d_wplane) return fail(UW_EINVAL, "NULL device pointer");
     if (p->ldx < h->K || p->ldx % 8) return fail(UW_EINVAL, "ldx must be >= K and a multiple of 8");
     if (p->ldy < h->N) return fail(UW_EINVAL, "ldy must be >= N");
     if (!aligned(p->d_x, 16) || !aligned(p->d_y, 16) || !aligned(p->d_wplane, 16))
         return fail(UW_EINVAL, "device pointers must be 16-byte aligned");
     if (p->src < UW_W_BF16 || p->src > UW_W_DIRECT) return fail(UW_EINVAL, "bad src %d", p->src);
-    int v = p->variant < 0 ? default_variant(h->N, h->K, p->M, p->src) : p->variant;
+    v = p->variant < 0 ? default_variant(h->N, h->K, p->M, p->src) : p->variant;
     if (v >= kNumVariants) return fail(UW_EINVAL, "variant %d out of range", v);
     if (!uw_variant_supports(v, h->N, h->K, p->M, p->src)) return fail(UW_EUNSUPPORTED, "variant %d does not support this problem", v);
     if (kVariants[v].kind == 0 && 2 * p->M * p->ldx + 32 * h->K >= (int64_t{1} << 32))
         return fail(UW_EUNSUPPORTED, "variant %d addresses X and W with 32-bit offsets: ldx or K too large", v);
-    GemmArgs g;
     std::memset(&g, 0, sizeof g);
     g.x = p->d_x;
     g.wplane = p->d_wplane;
@@ -1253,7 +1366,7 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     g.M = p->M;
     g.N = h->N;
     g.K = h->K;
-    bool contig = false;
+    contig = false;
     if (p->src != UW_W_BF16) {
         if (!p->d_blob) return fail(UW_EINVAL, "d_blob needed for this src");
         uw_status st = check_header(h, h->total_bytes);
@@ -1277,6 +1390,20 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
         g.dmeta = static_cast<const uint8_t*>(p->d_wplane) + 1536 * T * G;
         g.dside = g.dmeta + (8 * T * G + 63) / 64 * 64;
     }
+    return UW_OK;
+}
+
+uw_status launch_gemm(const uw_gemm_args* p, void* stream)
+{
+    clear_error();
+    if (!p || !p->h) return fail(UW_EINVAL, "NULL argument");
+    if (p->M < 0) return fail(UW_ESHAPE, "M < 0");
+    if (p->M == 0) return UW_OK;
+    GemmArgs g;
+    bool contig = false;
+    int v = 0;
+    uw_status st = make_args(p, g, contig, v);
+    if (st != UW_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const Variant& var = kVariants[v];
@@ -1295,6 +1422,12 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
 extern "C" {
 
 uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream) { return uw::launch_gemm(args, stream); }
+
+uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
+                                void* stream)
+{
+    return uw::launch_gate_up_gemm(gate, up, d_h, ldh, stream);
+}
 
 int uw_variant_count(void) { return uw::kNumVariants; }
 

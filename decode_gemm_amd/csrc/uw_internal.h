@@ -53,6 +53,8 @@ enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2, DEC_DIRECT = 3 };
 uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err,
                         void* stream);
 uw_status launch_gemm(const uw_gemm_args* a, void* stream);
+uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
+                              void* stream);
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
 uint32_t cu_count();  // compute units of the current device
 uint32_t stream_cu_count(void* stream);  // compute units a hipStream_t may use (its CU mask)

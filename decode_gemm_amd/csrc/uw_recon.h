@@ -112,4 +112,16 @@ __device__ __forceinline__ u32x4 unit_piece(uint32_t e_lo, uint32_t e_hi, uint32
     return r;
 }
 
+// ---- SwiGLU (the glue between gate/up and down in the MLP): h = bf16(silu(g) * u), one
+// rounding to nearest even from fp32. Shared by the stand-alone kernel and the fused
+// gate/up epilogue so that both give the same bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN -> quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 }  // namespace uw

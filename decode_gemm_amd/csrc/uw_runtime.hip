@@ -13,12 +13,12 @@
 #include <vector>
 
 #include "uw_internal.h"
+#include "uw_recon.h"
 
 namespace uw {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __global__ void fill_kernel(u32x4* p, size_t n16, uint32_t v)
@@ -27,15 +27,6 @@ __global__ void fill_kernel(u32x4* p, size_t n16, uint32_t v)
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
         p[i] = u32x4{v, v, v, v};
 }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN -> quiet NaN
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // h = bf16(silu(g) * u); eight elements per thread, 16-byte loads and stores.
 __global__ void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u, uint16_t* __restrict__ h,
@@ -288,6 +279,31 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     return uw_recon_gemm(&g, stream);
 }
 
+// gate, up and SwiGLU of a layer in one launch when both projections are direct planes
+// and the fused form applies; UW_EUNSUPPORTED otherwise (the caller runs them one by one).
+uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const uint16_t* x, int64_t ldx, float* g,
+                        float* u, uint16_t* h, int64_t ldf, void* stream)
+{
+    if (gp.pipeline != UW_PIPE_DIRECT || up.pipeline != UW_PIPE_DIRECT || M > 64) return UW_EUNSUPPORTED;
+    uw_gemm_args a[2];
+    const uw_proj* pr[2] = {&gp, &up};
+    float* y[2] = {g, u};
+    for (int q = 0; q < 2; q++) {
+        std::memset(&a[q], 0, sizeof a[q]);
+        a[q].M = M;
+        a[q].d_x = x;
+        a[q].ldx = ldx;
+        a[q].h = pr[q]->h;
+        a[q].d_blob = pr[q]->d_blob;
+        a[q].src = UW_W_DIRECT;
+        a[q].d_wplane = pr[q]->d_direct;
+        a[q].d_y = y[q];
+        a[q].ldy = ldf;
+        a[q].variant = pr[q]->variant;
+    }
+    return uw_recon_gemm_gate_up(&a[0], &a[1], h, ldf, stream);
+}
+
 }  // namespace
 
 uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64_t M, int two_slots, size_t* out)
@@ -323,11 +339,16 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
         if (!two) {
             for (int l = 0; l < n_layers && st == UW_OK; l++) {
                 const uw_mlp_layer& L = layers[l];
-                if ((st = decode_proj(L.gate, slot[0], stream)) != UW_OK) break;
-                if ((st = gemm_proj(L.gate, slot[0], M, d_x, lay.K, g, lay.Nff, stream)) != UW_OK) break;
-                if ((st = decode_proj(L.up, slot[0], stream)) != UW_OK) break;
-                if ((st = gemm_proj(L.up, slot[0], M, d_x, lay.K, u, lay.Nff, stream)) != UW_OK) break;
-                if ((st = uw_swiglu(g, u, mf, h, stream)) != UW_OK) break;
+                st = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, stream);
+                if (st == UW_EUNSUPPORTED) {
+                    clear_error();
+                    if ((st = decode_proj(L.gate, slot[0], stream)) != UW_OK) break;
+                    if ((st = gemm_proj(L.gate, slot[0], M, d_x, lay.K, g, lay.Nff, stream)) != UW_OK) break;
+                    if ((st = decode_proj(L.up, slot[0], stream)) != UW_OK) break;
+                    if ((st = gemm_proj(L.up, slot[0], M, d_x, lay.K, u, lay.Nff, stream)) != UW_OK) break;
+                    st = uw_swiglu(g, u, mf, h, stream);
+                }
+                if (st != UW_OK) break;
                 if ((st = decode_proj(L.down, slot[0], stream)) != UW_OK) break;
                 st = gemm_proj(L.down, slot[0], M, h, lay.Nff, d_y, lay.Nout, stream);
             }
@@ -375,9 +396,14 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
         };
         for (int l = 0; l < n_layers && st == UW_OK; l++) {
             const uw_mlp_layer& L = layers[l];
-            if ((st = run(L.gate, d_x, lay.K, g, lay.Nff)) != UW_OK) break;
-            if ((st = run(L.up, d_x, lay.K, u, lay.Nff)) != UW_OK) break;
-            if ((st = uw_swiglu(g, u, mf, h, ms)) != UW_OK) break;
+            st = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, ms);
+            if (st == UW_EUNSUPPORTED) {
+                clear_error();
+                if ((st = run(L.gate, d_x, lay.K, g, lay.Nff)) != UW_OK) break;
+                if ((st = run(L.up, d_x, lay.K, u, lay.Nff)) != UW_OK) break;
+                st = uw_swiglu(g, u, mf, h, ms);
+            }
+            if (st != UW_OK) break;
             st = run(L.down, h, lay.Nff, d_y, lay.Nout);
         }
         for (int s = 0; s < 2; s++) {

@@ -215,6 +215,23 @@ typedef struct {
 
 uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream);
 
+/*
+ * uw_recon_gemm_gate_up (device). The gate and up projections of a SwiGLU MLP and the
+ * SwiGLU itself in one launch (the small-batch fixed cost the post lists among the
+ * reconstructive matmul's overheads, "Bundles and results" / "Trade-offs": one launch for
+ * gate and up). gate and up are two uw_gemm_args as for uw_recon_gemm, both on the
+ * direct plane (src UW_W_DIRECT) with the same M (1..64), N and K; each block computes its
+ * rows of gate, then the same rows of up, with gate's GEMM variant. Writes gate->d_y and
+ * up->d_y (fp32, exactly what uw_recon_gemm gives with that variant) and
+ * d_h[M][ldh] = bf16(silu(gate) * up), the same bits as uw_swiglu on those outputs.
+ * Errors: UW_EINVAL / UW_ESHAPE as for uw_recon_gemm, and UW_EUNSUPPORTED when the fused
+ * form does not apply (not both direct planes, M > 64, a palette whose exponents are not
+ * consecutive, or a variant without a fused form); the caller then runs the two GEMMs and
+ * uw_swiglu.
+ */
+uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
+                                void* stream);
+
 /* Kernel variants of uw_recon_gemm (tile shape per CU and pipelining depth, "How the
  * reconstructive matmul works": wider tiles for large batches, deeper buffers for small
  * ones). uw_variant_count() variants exist; uw_variant_name() describes one;

@@ -447,6 +447,80 @@ def test_mlp_stack_forward_one_and_two_streams():
     check_gemm(y, yr, ar, "stack last layer down")
 
 
+def test_gate_up_fused_matches_separate_launches():
+    """uw_recon_gemm_gate_up gives the same bits as the two GEMMs (same variant) and
+    uw_swiglu, for every variant with a fused form, ragged N, raw rows, M = 1..64; the
+    stack forward takes the fused path for direct gate/up and still equals the projection-
+    by-projection result; unsupported cases are refused."""
+    torch = torch_cuda()
+    cfg = synth.Config("gu", 9, (("gate", 700, 4160), ("up", 700, 4160)), 0.02, "normal", 0.0005, 0.0, 12, (1,))
+    mg, mu = Mat(synth.gen_weight(cfg, "gate")), Mat(synth.gen_weight(cfg, "up"))
+    assert mg.h.n_raw > 0 and mu.h.n_raw > 0
+    for m in (mg, mu):  # the fused form needs palettes of consecutive exponents
+        pal = sorted(np.frombuffer(bytes(m.h.palette), np.uint8)[: m.h.n_pal])
+        assert pal == list(range(pal[0], pal[0] + len(pal)))
+    dg, du = mg.decode("direct")[0], mu.decode("direct")[0]
+    N, K = mg.N, mg.K
+    fused = ["skinny rt4 u2 w4", "skinny rt4 u2 w4 xt", "skinny rt2 u4 w4", "skinny rt1 u4 w4", "skinny rt1 u4 w8"]
+    names = {uw.variant_name(v): v for v in range(uw.variant_count())}
+    for M in (1, 5, 16, 17, 33, 64):
+        x = dev(synth.gen_x(cfg, M, K))
+        for v in [-1] + [names[n] for n in fused]:
+            log(f"  gate/up fused M={M} variant={v}")
+            yg, yu, yg2, yu2 = (empty_f32(M, N) for _ in range(4))
+            h = torch.empty(M, N, dtype=torch.int16, device="cuda")
+            h2 = torch.empty(M, N, dtype=torch.int16, device="cuda")
+            for t in (yg, yu, yg2, yu2):
+                t.fill_(float("nan"))
+            uw.recon_gemm_gate_up(mg.h, mg.d_blob, dg, mu.h, mu.d_blob, du, x, yg, yu, h, M, variant=v)
+            uw.recon_gemm(mg.h, mg.d_blob, uw.W_DIRECT, dg, x, yg2, M, variant=v)
+            uw.recon_gemm(mu.h, mu.d_blob, uw.W_DIRECT, du, x, yu2, M, variant=v)
+            uw.swiglu(yg2, yu2, h2, M * N)
+            _sync()
+            assert np.array_equal(host(yg), host(yg2)) and np.array_equal(host(yu), host(yu2)), f"M={M} v={v}"
+            assert np.array_equal(host(h, np.uint16), host(h2, np.uint16)), f"M={M} v={v}: h"
+        yr, ar = oracle.gemm(synth.gen_x(cfg, M, K), mg.w)
+        check_gemm(host(yg), yr, ar, f"fused gate M={M}")
+    x = dev(synth.gen_x(cfg, 65, K))
+    y = empty_f32(65, N)
+    hh = torch.empty(65, N, dtype=torch.int16, device="cuda")
+    with pytest.raises(uw.UwError) as e:
+        uw.recon_gemm_gate_up(mg.h, mg.d_blob, dg, mu.h, mu.d_blob, du, x, y, y, hh, 65)
+    assert e.value.status == uw.EUNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        uw.recon_gemm_gate_up(mg.h, mg.d_blob, dg, mu.h, mu.d_blob, du, x, y, y, hh, 8, variant=names["tiled 128x128"])
+    assert e.value.status == uw.EUNSUPPORTED
+
+    # stack forward: direct gate/up (fused) with a down projection, vs the same kernels one by one
+    cs = synth.Config("gus", 10, (("gate", 704, 512), ("up", 704, 512)), 0.02, "normal", 0.0, 0.0, 0, (1,))
+    mg, mu = Mat(synth.gen_weight(cs, "gate")), Mat(synth.gen_weight(cs, "up"))
+    dg, du = mg.decode("direct")[0], mu.decode("direct")[0]
+    N, K = mg.N, mg.K
+    wd = synth.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((K, N), dtype=np.float32) * 0.02)
+    md = Mat(wd)
+    ddn = md.decode("direct")[0]
+    cfg = cs
+    for M, v in ((3, -1), (40, names["skinny rt4 u2 w4 xt"])):
+        layer = [uw.proj(mg.h, mg.d_blob, uw.PIPE_DIRECT, d_direct=dg, variant=v),
+                 uw.proj(mu.h, mu.d_blob, uw.PIPE_DIRECT, d_direct=du, variant=v),
+                 uw.proj(md.h, md.d_blob, uw.PIPE_DIRECT, d_direct=ddn)]
+        arr = uw.mlp_layers([layer, layer])
+        x = dev(synth.gen_x(cfg, M, K))
+        nbytes = uw.mlp_stack_workspace(arr, M)
+        ws = empty_u8(nbytes + 256)
+        y = empty_f32(M, K)
+        uw.mlp_stack_forward(arr, M, x, y, ws, nbytes)
+        yg2, yu2 = empty_f32(M, N), empty_f32(M, N)
+        h2 = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        y2 = empty_f32(M, K)
+        uw.recon_gemm(mg.h, mg.d_blob, uw.W_DIRECT, dg, x, yg2, M, variant=v)
+        uw.recon_gemm(mu.h, mu.d_blob, uw.W_DIRECT, du, x, yu2, M, variant=v)
+        uw.swiglu(yg2, yu2, h2, M * N)
+        uw.recon_gemm(md.h, md.d_blob, uw.W_DIRECT, ddn, h2, y2, M)
+        _sync()
+        assert np.array_equal(host(y), host(y2)), f"stack M={M}"
+
+
 def test_cu_split_streams_decode_and_stack_forward():
     """Streams on disjoint compute units: their CU counts add up to the device's, the
     persistent decoder on the decode slice is still bit-exact, and the stack forward with
