@@ -859,13 +859,16 @@ uint32_t stream_cu_count(void* stream)
 template <int MODE>
 hipError_t launch_lut(const lut::Args& f, uint32_t blocks, uint32_t waves, hipStream_t s)
 {
-    static bool attr_done = false;  // benign race: every writer stores the same value
-    if (!attr_done) {
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on (bit per device; a
+                                    // lost update between racing threads only repeats the call)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!((attr_done >> dev) & 1u)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lut::decode_lut_kernel<MODE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lut::lds_bytes(lut::kMaxWaves)));
         if (e != hipSuccess) return e;
-        attr_done = true;
+        attr_done |= uint64_t{1} << dev;
     }
     hipLaunchKernelGGL(lut::decode_lut_kernel<MODE>, dim3(blocks), dim3(64 * waves), lut::lds_bytes(waves), s, f);
     return hipGetLastError();

@@ -983,6 +983,22 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         const int64_t m = m0 + 16 * i + r;
         xsrc[it] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
     }
+    // X (and bf16 W) slices are read as whole 128-byte row segments: load q of this wave
+    // covers tile rows 8 (4 wave + q) .. +7, lane l takes row + l % 8 and 16 bytes l / 8, so
+    // eight consecutive lanes store eight rows of one column of the operand-order LDS
+    // stage (distinct banks). A row-sliced operand load would touch twice the cache lines.
+    const uint8_t* xseg[4];
+    const uint8_t* wseg[4];
+    int sdst[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int rho = 8 * (4 * wave + q) + (lane & 7), kap = lane >> 3;
+        const int64_t m = m0 + rho, n = n0 + rho;
+        xseg[q] = reinterpret_cast<const uint8_t*>(a.x + (m < a.M ? m : a.M - 1) * a.ldx) + 16 * kap;
+        wseg[q] = static_cast<const uint8_t*>(a.wplane) + 2 * (n < a.N ? n : a.N - 1) * a.K + 16 * kap;
+        sdst[q] = (2 * (rho >> 4) + (kap & 1)) * 64 + 16 * (kap >> 1) + (rho & 15);
+    }
+    constexpr bool WSEG = SRC == UW_W_BF16;
 
     floatx4 acc[TN][TM];
 #pragma unroll
@@ -991,7 +1007,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         for (int c = 0; c < TM; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     W16 wr[ITEMS];
-    u32x4 xr[ITEMS][2];
+    u32x4 xr[4], ws[WSEG ? 4 : 1];
     u32x4 rsm[ITEMS], rex[ITEMS];  // raw item: true sign/mantissa (index plane), verbatim exponents
     bool israw[ITEMS];
     auto load_step = [&](uint32_t j) {
@@ -1004,7 +1020,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         }
 #pragma unroll
         for (int it = 0; it < ITEMS; it++) {
-            wpl[it].load(j, wr[it]);
+            if (!WSEG) wpl[it].load(j, wr[it]);
             if (DIRECT) {
                 const u32x2 mcur = mnext[it];
                 israw[it] = (mcur.x >> r) & 1u;
@@ -1020,9 +1036,11 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
                     rex[it] = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * g);
                 }
             }
-            const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc[it] + 64 * static_cast<int64_t>(j));
-            xr[it][0] = xp[0];
-            xr[it][1] = xp[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            xr[q] = *reinterpret_cast<const u32x4*>(xseg[q] + 128 * static_cast<int64_t>(j));
+            if (WSEG) ws[WSEG ? q : 0] = *reinterpret_cast<const u32x4*>(wseg[q] + 128 * static_cast<int64_t>(j));
         }
     };
     auto store_step = [&](int st) {
@@ -1030,6 +1048,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         u32x4* const B = A + A_VEC;
 #pragma unroll
         for (int it = 0; it < ITEMS; it++) {
+            if (WSEG) break;
             const int i = wave + NWV * it;
             u32x4 p0, p1;
             rebuild16<SRC, CONTIG>(a, wr[it], p0, p1);
@@ -1043,8 +1062,11 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
             }
             A[(2 * i) * 64 + lane] = p0;
             A[(2 * i + 1) * 64 + lane] = p1;
-            B[(2 * i) * 64 + lane] = xr[it][0];
-            B[(2 * i + 1) * 64 + lane] = xr[it][1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            B[sdst[q]] = xr[q];
+            if (WSEG) A[sdst[q]] = ws[WSEG ? q : 0];
         }
     };
     auto mma_step = [&](int st) {
@@ -1118,11 +1140,16 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Raise a kernel's dynamic-LDS limit above the 64 KB default once per process (gfx950
 // has 160 KB of LDS per CU).
-hipError_t allow_lds(const void* fn, size_t bytes, bool& done)
+// Raise a kernel's dynamic LDS limit past 64 KB, once per device (bit d of `done`; a
+// lost update between racing threads only repeats the call).
+hipError_t allow_lds(const void* fn, size_t bytes, uint64_t& done)
 {
-    if (bytes <= 64 * 1024 || done) return hipSuccess;
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if ((done >> dev) & 1u) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-    if (e == hipSuccess) done = true;
+    if (e == hipSuccess) done |= uint64_t{1} << dev;
     return e;
 }
 
@@ -1131,7 +1158,7 @@ hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
     constexpr size_t lds = skinny_lds<CT, RT, NW, XT>();
-    static bool attr_done = false;  // benign race: every writer stores the same value
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), lds, attr_done);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, g);
@@ -1201,7 +1228,7 @@ template <int SRC, bool CONTIG, int BN, int BM>
 hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
 {
     using C = TiledCfg<BN, BM>;
-    static bool attr_done = false;  // benign race: every writer stores the same value
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     const void* fn = reinterpret_cast<const void*>(&gemm_tiled<SRC, CONTIG, BN, BM>);
     hipError_t e = allow_lds(fn, C::LDS, attr_done);
     if (e != hipSuccess) return e;
@@ -1215,7 +1242,7 @@ template <int SRC, bool CONTIG>
 hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
 {
     constexpr size_t lds = 2 * (256 + 256) * 64 * 2;
-    static bool attr_done = false;  // benign race: every writer stores the same value
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), lds, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
@@ -1254,7 +1281,7 @@ hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
     const dim3 grid(static_cast<uint32_t>((ga.gate.N + 16 * RT - 1) / (16 * RT)));
     constexpr size_t lds = skinny_lds<CT, RT, NW, XT>() + static_cast<size_t>(RT) * CT * 256 * 4;
     const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
-    static bool attr_done = false;  // benign race: every writer stores the same value
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(fn, lds, attr_done);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, ga);
