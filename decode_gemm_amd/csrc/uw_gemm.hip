@@ -432,6 +432,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
             for (int c = 0; c < CT; c++)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; s2++) XF[XT ? c : 0][s2] = xs[(16 * c + r) * XS_PITCH + 2 * g + s2];
+            // the slot's X registers are free once stored: refill them first, so the X of
+            // group t + U has U whole steps to arrive and is never queued behind W
+            if (!XNEAR && refill) load_x(j + NW * U, xr[XNEAR ? 0 : u]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         u32x4 A[RT][2];
 #pragma unroll
@@ -456,9 +460,9 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
             if (refill) load_slot(j + NW * U, uc);
             if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
         } else {
-            // issue order is pinned: the raw exponents consumed half a turn from now, then
-            // the W slot refill (a full turn ahead), the MFMAs, the X refill; waiting for any
-            // of them then never waits for a younger request
+            // issue order is pinned: (XT: the X refill,) the raw exponents consumed half a
+            // turn from now, the W slot refill (a full turn ahead), the MFMAs, the X refill;
+            // waiting for any of them then never waits for a younger request
             __builtin_amdgcn_sched_barrier(0);
             if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
             if (refill) load_slot(j + NW * U, uc);
@@ -471,7 +475,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                     for (int c = 0; c < CT; c++)
                         acc[i][c] = mfma16(A[i][s2], XT ? XF[XT ? c : 0][s2] : xr[u][c][s2], acc[i][c]);
             __builtin_amdgcn_sched_barrier(0);
-            if (refill) load_x(j + NW * U, xr[u]);
+            if (!XT && refill) load_x(j + NW * U, xr[u]);
         }
     };
     // The ring is filled with no conditions (slots past the wave's last group reload that
@@ -488,13 +492,21 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                 if (DIRECT) ((us < U / 2 ? load_raw(jc(us), std::integral_constant<int, us>{}) : void()), ...);
                 load_x(wave, xr[0]);
             } else {
-                // the steady state's issue order: the raw exponents of slot k - U/2, slot k's
-                // meta and W, slot k's X
+                // the steady state's issue order: (XT: slot k's X,) the raw exponents of slot
+                // k - U/2, slot k's meta and W, (otherwise: slot k's X)
                 auto first = [&](auto kc) __attribute__((always_inline)) {
                     constexpr int k = decltype(kc)::value;
+                    // (pinned: the loop head's wait counts are the minimum over this path
+                    // and the loop's own, so a reordered prologue would weaken them)
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (XT) load_x(jc(k), xr[XNEAR ? 0 : k]);
+                    __builtin_amdgcn_sched_barrier(0);
                     if (DIRECT && k >= U / 2) load_raw(jc(k - U / 2), std::integral_constant<int, (k + U / 2) % U>{});
+                    __builtin_amdgcn_sched_barrier(0);
                     load_slot(jc(k), kc);
-                    load_x(jc(k), xr[XNEAR ? 0 : k]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (!XT) load_x(jc(k), xr[XNEAR ? 0 : k]);
+                    __builtin_amdgcn_sched_barrier(0);
                 };
                 (first(std::integral_constant<int, us>{}), ...);
             }
