@@ -83,6 +83,21 @@ class MlpLayer(ctypes.Structure):
     _fields_ = [("gate", Proj), ("up", Proj), ("down", Proj)]
 
 
+class StackOpts(ctypes.Structure):
+    """uw_stack_opts: decode slots and decode order of a stack forward."""
+    _fields_ = [("slots", ctypes.c_int32), ("down_first", ctypes.c_int32)]
+
+
+class StackTuneArgs(ctypes.Structure):
+    _fields_ = [
+        ("layers", ctypes.POINTER(MlpLayer)), ("n_layers", ctypes.c_int32), ("M", ctypes.c_int64),
+        ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p), ("d_ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+        ("decode_stream", ctypes.c_void_p), ("opts", StackOpts), ("pipeline_mask", ctypes.c_uint32),
+        ("reps", ctypes.c_int32), ("warmup", ctypes.c_int32), ("max_passes", ctypes.c_int32),
+        ("t_start_ms", ctypes.c_float), ("t_ms", ctypes.c_float), ("passes", ctypes.c_int32), ("trials", ctypes.c_int32),
+    ]
+
+
 class TuneArgs(ctypes.Structure):
     _fields_ = [
         ("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_direct", ctypes.c_void_p),
@@ -140,6 +155,11 @@ def _load():
         "uw_mlp_stack_workspace": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, ctypes.c_int, ctypes.POINTER(sz)],
                                    ctypes.c_int),
         "uw_mlp_stack_forward": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, P, P, P, sz, P, P], ctypes.c_int),
+        "uw_mlp_stack_workspace_ex": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, ctypes.POINTER(StackOpts),
+                                       ctypes.POINTER(sz)], ctypes.c_int),
+        "uw_mlp_stack_forward_ex": ([ctypes.POINTER(MlpLayer), ctypes.c_int, i64, P, P, P, sz, P, P,
+                                     ctypes.POINTER(StackOpts)], ctypes.c_int),
+        "uw_mlp_stack_autotune": ([ctypes.POINTER(StackTuneArgs), P], ctypes.c_int),
         "uw_stream_pair_create": ([ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)], ctypes.c_int),
         "uw_stream_destroy": ([P], ctypes.c_int),
         "uw_stream_cu_count": ([P, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
@@ -321,6 +341,35 @@ def mlp_stack_forward(layers: ctypes.Array, M: int, d_x, d_y, d_ws, ws_bytes: in
     layer's output. decode_stream (optional) decodes one projection ahead."""
     _check(lib.uw_mlp_stack_forward(layers, len(layers), M, _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes,
                                     _stream(stream), None if decode_stream is None else _stream(decode_stream)))
+
+
+def mlp_stack_workspace_ex(layers: ctypes.Array, M: int, slots: int = 2, down_first: bool = False) -> int:
+    out = ctypes.c_size_t(0)
+    opts = StackOpts(slots, int(down_first))
+    _check(lib.uw_mlp_stack_workspace_ex(layers, len(layers), M, ctypes.byref(opts), ctypes.byref(out)))
+    return out.value
+
+
+def mlp_stack_forward_ex(layers: ctypes.Array, M: int, d_x, d_y, d_ws, ws_bytes: int, stream=None, decode_stream=None,
+                         slots: int = 2, down_first: bool = False) -> None:
+    """uw_mlp_stack_forward_ex: the stack forward with `slots` decode slots and, optionally,
+    each layer's down projection decoded before its gate and up."""
+    opts = StackOpts(slots, int(down_first))
+    _check(lib.uw_mlp_stack_forward_ex(layers, len(layers), M, _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes,
+                                       _stream(stream), None if decode_stream is None else _stream(decode_stream),
+                                       ctypes.byref(opts)))
+
+
+def mlp_stack_autotune(layers: ctypes.Array, M: int, d_x, d_y, d_ws, ws_bytes: int, stream=None, decode_stream=None,
+                       slots: int = 2, down_first: bool = False, pipeline_mask: int = 0, reps: int = 0,
+                       warmup: int = 0, max_passes: int = 0) -> StackTuneArgs:
+    """uw_mlp_stack_autotune: coordinate descent over the layers' plans (written back into
+    `layers`); returns the argument struct with opts, t_start_ms, t_ms, passes and trials."""
+    a = StackTuneArgs(ctypes.cast(layers, ctypes.POINTER(MlpLayer)), len(layers), M, _ptr(d_x), _ptr(d_y), _ptr(d_ws),
+                      ws_bytes, None if decode_stream is None else _stream(decode_stream),
+                      StackOpts(slots, int(down_first)), pipeline_mask, reps, warmup, max_passes, 0.0, 0.0, 0, 0)
+    _check(lib.uw_mlp_stack_autotune(ctypes.byref(a), _stream(stream)))
+    return a
 
 
 def stream_pair_create(decode_cus: int):

@@ -203,15 +203,21 @@ namespace {
 
 struct StackLayout {
     int64_t Nff, K, Nout;
-    size_t g, u, h, slot0, slot1, slot_bytes, total;
+    size_t g, u, h, slot0, slot_bytes, total;
+    int slots;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, bool two, StackLayout* o)
+const uw_proj& role_of(const uw_mlp_layer& L, int r) { return r == 0 ? L.gate : r == 1 ? L.up : L.down; }
+
+// Workspace of a stack forward: g, u (fp32 M x N_ff), h (bf16 M x N_ff), then `slots` decode
+// slots of the largest plane any projection's pipeline decodes.
+uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, int slots, StackLayout* o)
 {
     if (!L || n <= 0) return fail(UW_EINVAL, "no layers");
     if (M < 0) return fail(UW_ESHAPE, "M < 0");
+    if (slots < 1 || slots > 8) return fail(UW_EINVAL, "decode slots must be 1..8, not %d", slots);
     const uw_header* g0 = L[0].gate.h;
     const uw_header* d0 = L[0].down.h;
     if (!g0 || !d0) return fail(UW_EINVAL, "NULL header");
@@ -220,13 +226,13 @@ uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, bool two, StackL
     o->Nout = d0->N;
     size_t slot = 0;
     for (int l = 0; l < n; l++) {
-        const uw_proj* ps[3] = {&L[l].gate, &L[l].up, &L[l].down};
         for (int q = 0; q < 3; q++) {
-            if (!ps[q]->h || !ps[q]->d_blob) return fail(UW_EINVAL, "layer %d projection %d: NULL header or blob", l, q);
-            if (ps[q]->pipeline == UW_PIPE_DIRECT && !ps[q]->d_direct)
+            const uw_proj& pr = role_of(L[l], q);
+            if (!pr.h || !pr.d_blob) return fail(UW_EINVAL, "layer %d projection %d: NULL header or blob", l, q);
+            if (pr.pipeline == UW_PIPE_DIRECT && !pr.d_direct)
                 return fail(UW_EINVAL, "layer %d projection %d: direct palette needs the direct plane", l, q);
             size_t need = 0;
-            uw_status st = uw_workspace_bytes(ps[q]->h, ps[q]->pipeline, &need);
+            uw_status st = uw_workspace_bytes(pr.h, pr.pipeline, &need);
             if (st != UW_OK) return st;
             slot = need > slot ? need : slot;
         }
@@ -237,13 +243,13 @@ uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, bool two, StackL
             return fail(UW_ESHAPE, "layer %d: shapes differ from layer 0 or do not chain", l);
     }
     const size_t mf = static_cast<size_t>(M) * static_cast<size_t>(o->Nff);
+    o->slots = slots;
     o->slot_bytes = align256(slot);
     o->g = 0;
     o->u = align256(4 * mf);
     o->h = o->u + align256(4 * mf);
     o->slot0 = o->h + align256(2 * mf);
-    o->slot1 = o->slot0 + o->slot_bytes;
-    o->total = o->slot0 + (two ? 2 : 1) * o->slot_bytes;
+    o->total = o->slot0 + static_cast<size_t>(slots) * o->slot_bytes;
     return UW_OK;
 }
 
@@ -304,6 +310,195 @@ uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const u
     return uw_recon_gemm_gate_up(&a[0], &a[1], h, ldf, stream);
 }
 
+// ---- the schedule of a forward with a decode stream
+//
+// A layer whose projections all read direct planes needs no preprocessing (an "easy"
+// layer); any other is "hard" ("Sharing the GPU between decode and compute": the
+// preprocessing of the next hard layer runs on a side stream while easy layers compute,
+// through double-buffered slots; down is consumed last in a layer, so its decode can be
+// issued first). Every decode-first projection gets a decode index q in decode order (per
+// layer gate, up, down, or down first) and slot q mod S. The plan is built on the host
+// before anything is launched: after each GEMM that frees a slot, every decode whose slot
+// is free is issued at once, so decodes run as far ahead of their GEMMs as the slots
+// allow. A decode order that would need a slot still held by a later GEMM is rejected.
+struct Action {
+    enum Kind { DECODE, GEMM, FUSED, SWIGLU } kind;
+    int layer, role, q;  // role 0 gate, 1 up, 2 down; q = decode index or -1
+};
+
+bool both_direct(const uw_mlp_layer& L, int64_t M)
+{
+    return L.gate.pipeline == UW_PIPE_DIRECT && L.up.pipeline == UW_PIPE_DIRECT && M <= 64;
+}
+
+uw_status build_plan(const uw_mlp_layer* layers, int n, int64_t M, int S, bool down_first, std::vector<Action>& plan)
+{
+    plan.clear();
+    std::vector<std::pair<int, int>> dec;
+    std::vector<int> qof(static_cast<size_t>(3) * n, -1);
+    static const int kInOrder[3] = {0, 1, 2}, kDownFirst[3] = {2, 0, 1};
+    for (int l = 0; l < n; l++) {
+        const int* order = down_first ? kDownFirst : kInOrder;
+        for (int k = 0; k < 3; k++) {
+            const int r = order[k];
+            if (role_of(layers[l], r).pipeline == UW_PIPE_DIRECT) continue;
+            qof[3 * l + r] = static_cast<int>(dec.size());
+            dec.push_back({l, r});
+        }
+    }
+    std::vector<char> consumed(dec.size(), 0);
+    size_t next = 0;
+    auto pump = [&]() {
+        while (next < dec.size() && (next < static_cast<size_t>(S) || consumed[next - S])) {
+            plan.push_back({Action::DECODE, dec[next].first, dec[next].second, static_cast<int>(next)});
+            next++;
+        }
+    };
+    pump();
+    for (int l = 0; l < n; l++) {
+        auto gemm = [&](int r) -> bool {
+            const int q = qof[3 * l + r];
+            if (q >= 0 && static_cast<size_t>(q) >= next) return false;
+            plan.push_back({Action::GEMM, l, r, q});
+            if (q >= 0) {
+                consumed[q] = 1;
+                pump();
+            }
+            return true;
+        };
+        if (both_direct(layers[l], M)) {
+            plan.push_back({Action::FUSED, l, -1, -1});
+        } else {
+            if (!gemm(0) || !gemm(1))
+                return fail(UW_EINVAL, "layer %d: this decode order needs more than %d decode slots", l, S);
+            plan.push_back({Action::SWIGLU, l, -1, -1});
+        }
+        if (!gemm(2)) return fail(UW_EINVAL, "layer %d: this decode order needs more than %d decode slots", l, S);
+    }
+    return UW_OK;
+}
+
+uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y, void* d_ws,
+                        size_t ws_bytes, void* stream, void* decode_stream, int slots, bool down_first)
+{
+    StackLayout lay;
+    uw_status st = stack_layout(layers, n_layers, M, slots, &lay);
+    if (st != UW_OK) return st;
+    if (M == 0) return UW_OK;
+    if (!d_x || !d_y || !d_ws) return fail(UW_EINVAL, "NULL device pointer");
+    if (!aligned(d_ws, 256)) return fail(UW_EINVAL, "d_ws must be 256-byte aligned");
+    if (ws_bytes < lay.total) return fail(UW_ENOSPACE, "the stack needs %zu workspace bytes", lay.total);
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    float* g = reinterpret_cast<float*>(ws + lay.g);
+    float* u = reinterpret_cast<float*>(ws + lay.u);
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws + lay.h);
+    auto slot = [&](int s) -> void* { return ws + lay.slot0 + static_cast<size_t>(s) * lay.slot_bytes; };
+    const int64_t mf = M * lay.Nff;
+    // operands of a projection's GEMM
+    auto gemm_io = [&](int r, const uint16_t*& x, int64_t& ldx, float*& y, int64_t& ldy) {
+        if (r == 2) {
+            x = h;
+            ldx = lay.Nff;
+            y = d_y;
+            ldy = lay.Nout;
+        } else {
+            x = d_x;
+            ldx = lay.K;
+            y = r == 0 ? g : u;
+            ldy = lay.Nff;
+        }
+    };
+    // gate, up and SwiGLU of a layer whose gate and up are direct planes
+    auto direct_pair = [&](const uw_mlp_layer& L, void* s) -> uw_status {
+        uw_status r = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, s);
+        if (r != UW_EUNSUPPORTED) return r;
+        clear_error();
+        if ((r = gemm_proj(L.gate, nullptr, M, d_x, lay.K, g, lay.Nff, s)) != UW_OK) return r;
+        if ((r = gemm_proj(L.up, nullptr, M, d_x, lay.K, u, lay.Nff, s)) != UW_OK) return r;
+        return uw_swiglu(g, u, mf, h, s);
+    };
+
+    if (!decode_stream) {
+        for (int l = 0; l < n_layers && st == UW_OK; l++) {
+            const uw_mlp_layer& L = layers[l];
+            if (both_direct(L, M)) {
+                st = direct_pair(L, stream);
+            } else {
+                for (int r = 0; r < 2 && st == UW_OK; r++) {
+                    const uint16_t* x;
+                    int64_t ldx, ldy;
+                    float* y;
+                    gemm_io(r, x, ldx, y, ldy);
+                    if ((st = decode_proj(role_of(L, r), slot(0), stream)) == UW_OK)
+                        st = gemm_proj(role_of(L, r), slot(0), M, x, ldx, y, ldy, stream);
+                }
+                if (st == UW_OK) st = uw_swiglu(g, u, mf, h, stream);
+            }
+            if (st != UW_OK) break;
+            if ((st = decode_proj(L.down, slot(0), stream)) != UW_OK) break;
+            st = gemm_proj(L.down, slot(0), M, h, lay.Nff, d_y, lay.Nout, stream);
+        }
+        return st;
+    }
+
+    std::vector<Action> plan;
+    if ((st = build_plan(layers, n_layers, M, slots, down_first, plan)) != UW_OK) return st;
+    hipStream_t ms = static_cast<hipStream_t>(stream), ds = static_cast<hipStream_t>(decode_stream);
+    std::vector<hipEvent_t> decoded(slots, nullptr), freed(slots, nullptr);
+    hipEvent_t start = nullptr;
+    auto release = [&]() {
+        for (int s = 0; s < slots; s++) {
+            if (decoded[s]) (void)hipEventDestroy(decoded[s]);
+            if (freed[s]) (void)hipEventDestroy(freed[s]);
+        }
+        if (start) (void)hipEventDestroy(start);
+    };
+    for (int s = 0; s < slots; s++) {
+        if (hipEventCreateWithFlags(&decoded[s], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&freed[s], hipEventDisableTiming) != hipSuccess) {
+            release();
+            return fail(UW_EHIP, "hipEventCreate failed");
+        }
+    }
+    // the decode stream must also see everything queued on the main stream so far (the
+    // caller's writes of X and of the planes)
+    if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess || hipEventRecord(start, ms) != hipSuccess ||
+        hipStreamWaitEvent(ds, start, 0) != hipSuccess) {
+        release();
+        return fail(UW_EHIP, "stream ordering failed");
+    }
+    for (const Action& a : plan) {
+        const uw_mlp_layer& L = layers[a.layer];
+        if (a.kind == Action::DECODE) {
+            const int s = a.q % slots;
+            if (a.q >= slots && hipStreamWaitEvent(ds, freed[s], 0) != hipSuccess) { st = fail(UW_EHIP, "wait failed"); break; }
+            if ((st = decode_proj(role_of(L, a.role), slot(s), ds)) != UW_OK) break;
+            if (hipEventRecord(decoded[s], ds) != hipSuccess) { st = fail(UW_EHIP, "event record failed"); break; }
+        } else if (a.kind == Action::GEMM) {
+            const uint16_t* x;
+            int64_t ldx, ldy;
+            float* y;
+            gemm_io(a.role, x, ldx, y, ldy);
+            if (a.q < 0) {
+                if ((st = gemm_proj(role_of(L, a.role), nullptr, M, x, ldx, y, ldy, ms)) != UW_OK) break;
+                continue;
+            }
+            const int s = a.q % slots;
+            if (hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess) { st = fail(UW_EHIP, "wait failed"); break; }
+            if ((st = gemm_proj(role_of(L, a.role), slot(s), M, x, ldx, y, ldy, ms)) != UW_OK) break;
+            if (hipEventRecord(freed[s], ms) != hipSuccess) { st = fail(UW_EHIP, "event record failed"); break; }
+        } else if (a.kind == Action::FUSED) {
+            if ((st = direct_pair(L, ms)) != UW_OK) break;
+        } else {
+            if ((st = uw_swiglu(g, u, mf, h, ms)) != UW_OK) break;
+        }
+    }
+    release();
+    return st;
+}
+
+int opt_slots(const uw_stack_opts* o) { return o && o->slots != 0 ? o->slots : 2; }  // 0 = 2; out of range: EINVAL
+
 }  // namespace
 
 uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64_t M, int two_slots, size_t* out)
@@ -311,7 +506,18 @@ uw_status uw_mlp_stack_workspace(const uw_mlp_layer* layers, int n_layers, int64
     clear_error();
     if (!out) return fail(UW_EINVAL, "NULL argument");
     StackLayout lay;
-    uw_status st = stack_layout(layers, n_layers, M, two_slots != 0, &lay);
+    uw_status st = stack_layout(layers, n_layers, M, two_slots ? 2 : 1, &lay);
+    if (st == UW_OK) *out = lay.total;
+    return st;
+}
+
+uw_status uw_mlp_stack_workspace_ex(const uw_mlp_layer* layers, int n_layers, int64_t M, const uw_stack_opts* opts,
+                                    size_t* out)
+{
+    clear_error();
+    if (!out) return fail(UW_EINVAL, "NULL argument");
+    StackLayout lay;
+    uw_status st = stack_layout(layers, n_layers, M, opt_slots(opts), &lay);
     if (st == UW_OK) *out = lay.total;
     return st;
 }
@@ -321,99 +527,163 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
 {
     try {
         clear_error();
-        const bool two = decode_stream != nullptr;
-        StackLayout lay;
-        uw_status st = stack_layout(layers, n_layers, M, two, &lay);
-        if (st != UW_OK) return st;
-        if (M == 0) return UW_OK;
-        if (!d_x || !d_y || !d_ws) return fail(UW_EINVAL, "NULL device pointer");
-        if (!aligned(d_ws, 256)) return fail(UW_EINVAL, "d_ws must be 256-byte aligned");
-        if (ws_bytes < lay.total) return fail(UW_ENOSPACE, "the stack needs %zu workspace bytes", lay.total);
-        uint8_t* ws = static_cast<uint8_t*>(d_ws);
-        float* g = reinterpret_cast<float*>(ws + lay.g);
-        float* u = reinterpret_cast<float*>(ws + lay.u);
-        uint16_t* h = reinterpret_cast<uint16_t*>(ws + lay.h);
-        void* slot[2] = {ws + lay.slot0, ws + lay.slot1};
-        const int64_t mf = M * lay.Nff;
-
-        if (!two) {
-            for (int l = 0; l < n_layers && st == UW_OK; l++) {
-                const uw_mlp_layer& L = layers[l];
-                st = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, stream);
-                if (st == UW_EUNSUPPORTED) {
-                    clear_error();
-                    if ((st = decode_proj(L.gate, slot[0], stream)) != UW_OK) break;
-                    if ((st = gemm_proj(L.gate, slot[0], M, d_x, lay.K, g, lay.Nff, stream)) != UW_OK) break;
-                    if ((st = decode_proj(L.up, slot[0], stream)) != UW_OK) break;
-                    if ((st = gemm_proj(L.up, slot[0], M, d_x, lay.K, u, lay.Nff, stream)) != UW_OK) break;
-                    st = uw_swiglu(g, u, mf, h, stream);
-                }
-                if (st != UW_OK) break;
-                if ((st = decode_proj(L.down, slot[0], stream)) != UW_OK) break;
-                st = gemm_proj(L.down, slot[0], M, h, lay.Nff, d_y, lay.Nout, stream);
-            }
-            return st;
-        }
-
-        // two streams: the p-th decode-first projection decodes into slot p & 1 on
-        // decode_stream once the GEMM that last read that slot is done; its GEMM waits for
-        // the decode
-        hipStream_t ms = static_cast<hipStream_t>(stream), ds = static_cast<hipStream_t>(decode_stream);
-        hipEvent_t decoded[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
-        for (int s = 0; s < 2; s++) {
-            if (hipEventCreateWithFlags(&decoded[s], hipEventDisableTiming) != hipSuccess ||
-                hipEventCreateWithFlags(&consumed[s], hipEventDisableTiming) != hipSuccess) {
-                for (int q = 0; q < 2; q++) {
-                    if (decoded[q]) (void)hipEventDestroy(decoded[q]);
-                    if (consumed[q]) (void)hipEventDestroy(consumed[q]);
-                }
-                return fail(UW_EHIP, "hipEventCreate failed");
-            }
-        }
-        // the decode stream must also see everything queued on the main stream so far
-        // (the caller's writes of X and of the planes)
-        hipEvent_t start = nullptr;
-        if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess ||
-            hipEventRecord(start, ms) != hipSuccess || hipStreamWaitEvent(ds, start, 0) != hipSuccess)
-            st = fail(UW_EHIP, "stream ordering failed");
-        int64_t p = 0;
-        // decode-first projections take slots in turn; direct-palette ones use none and
-        // need no events
-        bool used[2] = {false, false};
-        auto run = [&](const uw_proj& pr, const uint16_t* x, int64_t ldx, float* y, int64_t ldy) -> uw_status {
-            if (pr.pipeline == UW_PIPE_DIRECT) return gemm_proj(pr, nullptr, M, x, ldx, y, ldy, ms);
-            const int s = static_cast<int>(p & 1);
-            uw_status r = UW_OK;
-            if (used[s] && hipStreamWaitEvent(ds, consumed[s], 0) != hipSuccess) return fail(UW_EHIP, "wait failed");
-            if ((r = decode_proj(pr, slot[s], ds)) != UW_OK) return r;
-            if (hipEventRecord(decoded[s], ds) != hipSuccess || hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess)
-                return fail(UW_EHIP, "event failed");
-            if ((r = gemm_proj(pr, slot[s], M, x, ldx, y, ldy, ms)) != UW_OK) return r;
-            if (hipEventRecord(consumed[s], ms) != hipSuccess) return fail(UW_EHIP, "event failed");
-            used[s] = true;
-            p++;
-            return UW_OK;
-        };
-        for (int l = 0; l < n_layers && st == UW_OK; l++) {
-            const uw_mlp_layer& L = layers[l];
-            st = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, ms);
-            if (st == UW_EUNSUPPORTED) {
-                clear_error();
-                if ((st = run(L.gate, d_x, lay.K, g, lay.Nff)) != UW_OK) break;
-                if ((st = run(L.up, d_x, lay.K, u, lay.Nff)) != UW_OK) break;
-                st = uw_swiglu(g, u, mf, h, ms);
-            }
-            if (st != UW_OK) break;
-            st = run(L.down, h, lay.Nff, d_y, lay.Nout);
-        }
-        for (int s = 0; s < 2; s++) {
-            (void)hipEventDestroy(decoded[s]);
-            (void)hipEventDestroy(consumed[s]);
-        }
-        if (start) (void)hipEventDestroy(start);
-        return st;
+        return stack_forward(layers, n_layers, M, d_x, d_y, d_ws, ws_bytes, stream, decode_stream, decode_stream ? 2 : 1,
+                             false);
     } catch (...) {
         return fail(UW_EINTERNAL, "unexpected exception in uw_mlp_stack_forward");
+    }
+}
+
+uw_status uw_mlp_stack_forward_ex(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y,
+                                  void* d_ws, size_t ws_bytes, void* stream, void* decode_stream, const uw_stack_opts* opts)
+{
+    try {
+        clear_error();
+        return stack_forward(layers, n_layers, M, d_x, d_y, d_ws, ws_bytes, stream, decode_stream, opt_slots(opts),
+                             opts && opts->down_first);
+    } catch (...) {
+        return fail(UW_EINTERNAL, "unexpected exception in uw_mlp_stack_forward_ex");
+    }
+}
+
+// ---- coordinate-descent tuning of a whole stack ("Why no single pipeline wins" and
+// "Sharing the GPU between decode and compute": the runtime's per-projection choices are
+// measured end to end, one coordinate at a time, until a pass changes nothing)
+uw_status uw_mlp_stack_autotune(uw_stack_tune_args* a, void* stream)
+{
+    try {
+        clear_error();
+        if (!a || !a->layers || a->n_layers <= 0) return fail(UW_EINVAL, "NULL argument or no layers");
+        const int n = a->n_layers;
+        uw_mlp_layer* L = a->layers;
+        const int reps = a->reps > 0 ? a->reps : 5, warmup = a->warmup > 0 ? a->warmup : 1;
+        const int max_passes = a->max_passes > 0 ? a->max_passes : 4;
+        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0xFu;
+        const int slots = opt_slots(&a->opts);
+        // layer class: 0 when all three projections have direct planes ("easy" once they
+        // use them), 1 otherwise (a "hard" layer, which always needs preprocessing)
+        std::vector<int> cls(n);
+        bool present[2] = {false, false};
+        for (int l = 0; l < n; l++) {
+            cls[l] = L[l].gate.d_direct && L[l].up.d_direct && L[l].down.d_direct ? 0 : 1;
+            present[cls[l]] = true;
+        }
+        uw_stack_opts opts = a->opts;
+        opts.slots = slots;
+        auto fits = [&]() -> bool {
+            StackLayout lay;
+            if (stack_layout(L, n, a->M, a->decode_stream ? slots : 1, &lay) != UW_OK) {
+                clear_error();
+                return false;
+            }
+            if (lay.total > a->ws_bytes) return false;
+            if (!a->decode_stream) return true;
+            std::vector<Action> plan;
+            if (build_plan(L, n, a->M, slots, opts.down_first != 0, plan) != UW_OK) {
+                clear_error();
+                return false;
+            }
+            return true;
+        };
+        if (!fits()) return fail(UW_EINVAL, "the starting plan does not run in this workspace / slot count");
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+            if (e0) (void)hipEventDestroy(e0);
+            return fail(UW_EHIP, "hipEventCreate failed");
+        }
+        int trials = 0;
+        auto measure = [&](float& med) -> uw_status {
+            std::vector<float> t;
+            for (int r = 0; r < warmup + reps; r++) {
+                if (r >= warmup && hipEventRecord(e0, s) != hipSuccess) return fail(UW_EHIP, "event record failed");
+                uw_status st = stack_forward(L, n, a->M, a->d_x, a->d_y, a->d_ws, a->ws_bytes, stream, a->decode_stream,
+                                             a->decode_stream ? slots : 1, opts.down_first != 0);
+                if (st != UW_OK) return st;
+                if (r >= warmup) {
+                    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+                        return fail(UW_EHIP, "event synchronize failed");
+                    float ms = 0.f;
+                    (void)hipEventElapsedTime(&ms, e0, e1);
+                    t.push_back(ms);
+                }
+            }
+            std::sort(t.begin(), t.end());
+            med = t[t.size() / 2];
+            trials++;
+            return UW_OK;
+        };
+        // coordinate (class, role): set every layer of the class to pipeline p (default variant)
+        auto get = [&](int c, int r) -> int {
+            for (int l = 0; l < n; l++)
+                if (cls[l] == c) return role_of(L[l], r).pipeline;
+            return -1;
+        };
+        std::vector<uw_mlp_layer> saved(L, L + n);
+        auto set = [&](int c, int r, int p) {
+            for (int l = 0; l < n; l++) {
+                if (cls[l] != c) continue;
+                uw_proj& pr = r == 0 ? L[l].gate : r == 1 ? L[l].up : L[l].down;
+                pr.pipeline = p;
+                pr.variant = -1;
+            }
+        };
+        float best = 0.f;
+        uw_status st = measure(best);
+        a->t_start_ms = best;
+        int pass = 0;
+        for (; st == UW_OK && pass < max_passes; pass++) {
+            bool changed = false;
+            for (int c = 0; c < 2 && st == UW_OK; c++) {
+                if (!present[c]) continue;
+                for (int r = 0; r < 3 && st == UW_OK; r++) {
+                    for (int p = 0; p < 4 && st == UW_OK; p++) {
+                        const int cur = get(c, r);
+                        if (p == cur || !(pmask >> p & 1u)) continue;
+                        if (p == UW_PIPE_DIRECT && c == 1) {
+                            // a hard layer may still hold a direct plane for this projection
+                            bool all = true;
+                            for (int l = 0; l < n; l++)
+                                if (cls[l] == 1 && !role_of(L[l], r).d_direct) all = false;
+                            if (!all) continue;
+                        }
+                        saved.assign(L, L + n);
+                        set(c, r, p);
+                        float t = 0.f;
+                        if (fits() && (st = measure(t)) == UW_OK && t < best * 0.99f) {
+                            best = t;
+                            changed = true;
+                        } else {
+                            std::copy(saved.begin(), saved.end(), L);
+                        }
+                    }
+                }
+            }
+            // the decode order, where a decode stream with room for a whole layer is given
+            if (st == UW_OK && a->decode_stream && slots >= 3) {
+                opts.down_first = !opts.down_first;
+                float t = 0.f;
+                if (fits() && (st = measure(t)) == UW_OK && t < best * 0.99f) {
+                    best = t;
+                    changed = true;
+                } else {
+                    opts.down_first = !opts.down_first;
+                }
+            }
+            if (!changed) {
+                pass++;
+                break;
+            }
+        }
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        a->opts.down_first = opts.down_first;
+        a->t_ms = best;
+        a->passes = pass;
+        a->trials = trials;
+        return st;
+    } catch (...) {
+        return fail(UW_EINTERNAL, "unexpected exception in uw_mlp_stack_autotune");
     }
 }
 

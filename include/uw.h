@@ -346,6 +346,83 @@ uw_status uw_mlp_stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t
                                void* d_ws, size_t ws_bytes, void* stream, void* decode_stream);
 
 /*
+ * Stack schedule options ("Sharing the GPU between decode and compute": hard layers, whose
+ * projections need preprocessing, are decoded on a side stream while the layers before them
+ * compute, through preprocessing slots; down is consumed last in a layer, so its decode may
+ * be issued first).
+ *
+ * uw_mlp_stack_forward_ex is uw_mlp_stack_forward with:
+ *   slots      decode slots in the workspace (1..8; 0 = 2). With decode_stream != NULL the
+ *              decode-first projections of all layers, taken in decode order, use slot
+ *              q mod slots; after every GEMM that frees a slot, each decode whose slot is free
+ *              is issued on decode_stream, so a hard layer is decoded while the easy layers
+ *              (all projections direct palette) before it compute. Without a decode stream
+ *              only slot 0 is used.
+ *   down_first per layer, decode down before gate and up (decode order down, gate, up) instead
+ *              of gate, up, down. An order that would need a slot still held by a later GEMM
+ *              (down_first with fewer slots than a layer's decode-first projections) is
+ *              rejected with UW_EINVAL before anything is launched.
+ * Results are bit-identical to uw_mlp_stack_forward for every slot count and order (the
+ * same kernels on the same planes). uw_mlp_stack_workspace_ex sizes the workspace for
+ * opts->slots slots (uw_mlp_stack_workspace(two_slots) = slots 2 or 1).
+ */
+typedef struct {
+    int32_t slots;
+    int32_t down_first;
+} uw_stack_opts;
+
+uw_status uw_mlp_stack_workspace_ex(const uw_mlp_layer* layers, int n_layers, int64_t M, const uw_stack_opts* opts,
+                                    size_t* out);
+uw_status uw_mlp_stack_forward_ex(const uw_mlp_layer* layers, int n_layers, int64_t M, const uint16_t* d_x, float* d_y,
+                                  void* d_ws, size_t ws_bytes, void* stream, void* decode_stream,
+                                  const uw_stack_opts* opts);
+
+/*
+ * uw_mlp_stack_autotune (device, synchronous): coordinate descent over a stack's plan,
+ * measured end to end ("Why no single pipeline wins": the configuration space is searched by
+ * timing, not by heuristics). Layers fall into two classes: those whose three projections
+ * all have direct planes, and the others ("hard" layers, which keep only the Huffman blob
+ * for some projection and always need preprocessing). The coordinates are (class, role)
+ * for role gate, up, down of each class present, and, with a decode stream and at least 3
+ * slots, the decode order. Each pass tries every other pipeline (in pipeline_mask; direct
+ * palette only where every layer of the class has that projection's direct plane) for one
+ * coordinate at a time, applied to all layers of the class with the default GEMM variant,
+ * times the whole forward (warmup untimed runs, then the median of reps, HIP events on
+ * `stream`) and keeps a change only if it is at least 1% faster; passes repeat, gate, up,
+ * down, until one changes nothing or max_passes is reached.
+ *
+ * In: layers with blobs, direct planes (or NULL) and a starting plan that runs in the
+ * workspace; d_x (M x K bf16), d_y (M x N_out fp32), d_ws / ws_bytes (256-byte aligned,
+ * e.g. uw_mlp_stack_workspace_ex with every projection set to UW_PIPE_FULL so that every
+ * candidate fits; candidates that do not fit are skipped), decode_stream (or NULL), opts
+ * (slots; down_first = the starting order). Out: the layers' pipeline and variant fields,
+ * opts.down_first, t_start_ms and t_ms (medians of the starting and the final plan), passes
+ * and trials (forwards timed per candidate set). Y and the workspace are overwritten.
+ * Errors: UW_EINVAL (arguments, a starting plan that does not fit), any error of the forward.
+ */
+typedef struct {
+    uw_mlp_layer* layers;
+    int32_t n_layers;
+    int64_t M;
+    const uint16_t* d_x;
+    float* d_y;
+    void* d_ws;
+    size_t ws_bytes;
+    void* decode_stream;
+    uw_stack_opts opts;
+    uint32_t pipeline_mask; /* 0 = all four */
+    int32_t reps;           /* 0 = 5 */
+    int32_t warmup;         /* 0 = 1 */
+    int32_t max_passes;     /* 0 = 4 */
+    float t_start_ms;
+    float t_ms;
+    int32_t passes;
+    int32_t trials;
+} uw_stack_tune_args;
+
+uw_status uw_mlp_stack_autotune(uw_stack_tune_args* args, void* stream);
+
+/*
  * CU-split streams ("Sharing the GPU between decode and compute": the preprocessing of one
  * projection runs on a slice of the compute units while the reconstructive GEMM of another
  * runs on the rest, so neither waits behind the other's workgroups).

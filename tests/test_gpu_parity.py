@@ -447,6 +447,117 @@ def test_mlp_stack_forward_one_and_two_streams():
     check_gemm(y, yr, ar, "stack last layer down")
 
 
+def _hard_easy_stack(rng, K, F, hard_pipes):
+    """A stack whose layers alternate easy (three projections with direct planes, run on
+    them) and hard (Huffman blobs only; decode-first pipelines from hard_pipes in turn).
+    Returns (layer array, per-layer Mat triples, objects to keep alive)."""
+    keep, mats, layers = [], [], []
+    for l in range(2 * len(hard_pipes)):
+        easy = l % 2 == 0
+        trip, tm = [], []
+        for q, (n, k) in enumerate(((F, K), (F, K), (K, F))):
+            w = synth.f32_to_bf16_bits(rng.standard_normal((n, k), dtype=np.float32) * 0.05)
+            m = Mat(w, 256)
+            d = m.decode("direct")[0] if easy else None
+            keep.append((m, d))
+            tm.append(m)
+            trip.append(uw.proj(m.h, m.d_blob, uw.PIPE_DIRECT if easy else hard_pipes[l // 2][q], d_direct=d))
+        mats.append(tm)
+        layers.append(trip)
+    return uw.mlp_layers(layers), mats, keep
+
+
+def _check_last_layer(x, y, wsb, mats, M, F, what):
+    """Teacher-forced check of the last layer: g, u, h (left in the workspace) and Y."""
+    gate, up, down = mats[-1]
+    a256 = lambda v: (v + 255) // 256 * 256
+    g = wsb[: 4 * M * F].view(np.float32).reshape(M, F)
+    u = wsb[a256(4 * M * F): a256(4 * M * F) + 4 * M * F].view(np.float32).reshape(M, F)
+    ho = 2 * a256(4 * M * F)
+    hg = wsb[ho: ho + 2 * M * F].view(np.uint16).reshape(M, F)
+    for name, got, wm in (("gate", g, gate), ("up", u, up)):
+        yr, ar = oracle.gemm(x, wm.w)
+        check_gemm(got, yr, ar, f"{what}: last layer {name}")
+    href = oracle.swiglu(g, u).reshape(M, F)
+    assert (np.abs(hg.astype(np.int32) - href.astype(np.int32)) <= 1).all()
+    yr, ar = oracle.gemm(hg, down.w)
+    check_gemm(y, yr, ar, f"{what}: last layer down")
+
+
+def test_stack_schedules_hard_easy_bit_identical():
+    """Hard layers (decode-first only) between easy ones (direct planes): every decode
+    schedule (one stream; a decode stream with 1..4 slots, in order or down first) gives
+    bit-identical Y, equal to uw_mlp_stack_forward's, and the last layer matches the
+    oracle."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(83)
+    K, F, M = 256, 512, 5
+    arr, mats, keep = _hard_easy_stack(rng, K, F, [(uw.PIPE_FULL, uw.PIPE_EXP, uw.PIPE_TRANSCODE),
+                                                  (uw.PIPE_TRANSCODE, uw.PIPE_FULL, uw.PIPE_EXP)])
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    d_x = dev(x)
+    side = torch.cuda.Stream()
+    ys = {}
+    last_ws = None
+    for slots, down_first, two in ((1, False, False), (1, False, True), (2, False, True), (3, False, True),
+                                   (3, True, True), (4, True, True), (4, False, True)):
+        nbytes = uw.mlp_stack_workspace_ex(arr, M, slots=slots)
+        ws = empty_u8(nbytes + 256)
+        y = empty_f32(M, K)
+        y.fill_(float("nan"))
+        log(f"  stack forward_ex: slots {slots}, down first {down_first}, decode stream {two}")
+        uw.mlp_stack_forward_ex(arr, M, d_x, y, ws, nbytes, decode_stream=side if two else None, slots=slots,
+                                down_first=down_first)
+        _sync()
+        ys[(slots, down_first, two)] = host(y)
+        last_ws = host(ws)
+    nbytes = uw.mlp_stack_workspace(arr, M, two_slots=True)
+    ws = empty_u8(nbytes + 256)
+    y = empty_f32(M, K)
+    uw.mlp_stack_forward(arr, M, d_x, y, ws, nbytes, decode_stream=side)
+    _sync()
+    ref = host(y)
+    for k, v in ys.items():
+        assert np.array_equal(v, ref), f"schedule {k} differs from uw_mlp_stack_forward"
+    _check_last_layer(x, ref, last_ws, mats, M, F, "hard/easy stack")
+
+
+def test_stack_autotune_coordinate_descent():
+    """uw_mlp_stack_autotune on a hard/easy stack from an all-full-decode start: the
+    tuned plan is never slower than the start, keeps direct palette off the hard layers
+    (they have no direct planes), and its forward matches the oracle."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(89)
+    K, F, M = 256, 512, 4
+    arr, mats, keep = _hard_easy_stack(rng, K, F, [(uw.PIPE_FULL,) * 3, (uw.PIPE_FULL,) * 3])
+    for l in range(len(arr)):
+        for r in ("gate", "up", "down"):
+            getattr(arr[l], r).pipeline = uw.PIPE_FULL  # start: full decode everywhere
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    d_x = dev(x)
+    side = torch.cuda.Stream()
+    nbytes = uw.mlp_stack_workspace_ex(arr, M, slots=3)  # all-full plan: every candidate fits
+    ws = empty_u8(nbytes + 256)
+    y = empty_f32(M, K)
+    log("  stack autotune: 4 layers, decode stream, 3 slots")
+    a = uw.mlp_stack_autotune(arr, M, d_x, y, ws, nbytes, decode_stream=side, slots=3, reps=3, warmup=1,
+                              max_passes=3)
+    _sync()
+    plan = [[getattr(arr[l], r).pipeline for r in ("gate", "up", "down")] for l in range(len(arr))]
+    log(f"  tuned: {plan}, down first {a.opts.down_first}, {a.t_start_ms:.3f} -> {a.t_ms:.3f} ms, "
+        f"{a.passes} passes, {a.trials} trials")
+    assert a.t_ms <= a.t_start_ms
+    assert 1 <= a.passes <= 3 and a.trials >= 2
+    for l, pp in enumerate(plan):
+        assert all(0 <= p <= 3 for p in pp)
+        if l % 2 == 1:
+            assert uw.PIPE_DIRECT not in pp, f"hard layer {l} given direct palette"
+    y.fill_(float("nan"))
+    uw.mlp_stack_forward_ex(arr, M, d_x, y, ws, nbytes, decode_stream=side, slots=3, down_first=bool(a.opts.down_first))
+    _sync()
+    _check_last_layer(x, host(y), host(ws), mats, M, F, "tuned stack")
+
+
 def test_gate_up_fused_matches_separate_launches():
     """uw_recon_gemm_gate_up gives the same bits as the two GEMMs (same variant) and
     uw_swiglu, for every variant with a fused form, ragged N, raw rows, M = 1..64; the

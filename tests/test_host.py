@@ -239,6 +239,38 @@ def test_mlp_stack_host_checks():
     assert e.value.status == uw.ENOSPACE
 
 
+def test_mlp_stack_schedule_options_host():
+    """Slot count and decode order of the stack forward: workspace sizes, the slot range,
+    a down-first order that would need a slot still held by a later GEMM (rejected before
+    any launch), and the tuner's check of its starting plan (also before any launch)."""
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")  # 512 x 256
+    hg = uw.inspect(uw.encode(w))
+    hd = uw.inspect(uw.encode(np.ascontiguousarray(w.reshape(256, 512))))
+    fake = 1 << 20
+    hard = (uw.proj(hg, fake, uw.PIPE_FULL), uw.proj(hg, fake, uw.PIPE_EXP), uw.proj(hd, fake, uw.PIPE_TRANSCODE))
+    layers = uw.mlp_layers([hard, hard])
+    M = 3
+    a = lambda v: (v + 255) // 256 * 256
+    slot = a(2 * 512 * 256)
+    base = 2 * a(4 * M * 512) + a(2 * M * 512)
+    assert uw.mlp_stack_workspace_ex(layers, M, slots=3) == base + 3 * slot
+    assert uw.mlp_stack_workspace_ex(layers, M, slots=0) == base + 2 * slot  # 0 = the default, 2
+    assert uw.mlp_stack_workspace_ex(layers, M, slots=1) == uw.mlp_stack_workspace(layers, M)
+    for bad in (9, -1):
+        with pytest.raises(uw.UwError) as e:
+            uw.mlp_stack_workspace_ex(layers, M, slots=bad)
+        assert e.value.status == uw.EINVAL
+    # down first: decode order down0, gate0, up0, ... with two slots, up0 would need the
+    # slot of down0, which is freed only after up0's own GEMM
+    with pytest.raises(uw.UwError) as e:
+        uw.mlp_stack_forward_ex(layers, M, fake, fake, fake, 1 << 30, stream=0, decode_stream=fake, slots=2,
+                                down_first=True)
+    assert e.value.status == uw.EINVAL and "decode slots" in str(e.value)
+    with pytest.raises(uw.UwError) as e:
+        uw.mlp_stack_autotune(layers, M, fake, fake, fake, 64, stream=0)
+    assert e.value.status == uw.EINVAL
+
+
 def test_stream_pair_argument_checks():
     """uw_stream_pair_create rejects NULL outputs and an empty decode share before it
     touches the device."""
