@@ -480,7 +480,45 @@ def stack_sweep(uw, synth, torch, dev, stream, log, Ms):
             del ws
         split[str(M)] = row
         log(f"[bench] stack decode-first M={M}: {row}")
-    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows, "decode_first": split}
+
+    # hard / easy layers: every 4th layer keeps only its Huffman blobs (no direct planes, so
+    # it always needs preprocessing); the others hold direct planes. Start: direct palette on
+    # the easy layers, full decode on the hard ones; uw_mlp_stack_autotune then tunes the
+    # per-class, per-role pipelines and the decode order end to end (decode stream, 3 slots).
+    hard = {}
+    for M in (1, 16, 64, 256):
+        layers = []
+        for l in range(L):
+            is_hard = l % 4 == 3
+            layers.append([uw.proj(hs[3 * l + q], d_blobs[3 * l + q], uw.PIPE_FULL if is_hard else uw.PIPE_DIRECT,
+                                   d_direct=None if is_hard else d_planes[3 * l + q]) for q in range(3)])
+        arr = uw.mlp_layers(layers)
+        full = uw.mlp_layers([[uw.proj(hs[3 * l + q], d_blobs[3 * l + q], uw.PIPE_FULL) for q in range(3)]
+                              for l in range(L)])
+        nb = uw.mlp_stack_workspace_ex(full, M, slots=3)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, K, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        a = uw.mlp_stack_autotune(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3, reps=3, warmup=1)
+        torch.cuda.synchronize()
+        tune_s = time.time() - t0
+        plan = {}
+        for cls, l in (("easy", 0), ("hard", 3)):
+            plan[cls] = {r: uw.PIPELINE_NAMES[getattr(arr[l], r).pipeline] for r in ("gate", "up", "down")}
+        fwd = lambda r: uw.mlp_stack_forward_ex(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3,
+                                                down_first=bool(a.opts.down_first))
+        fwd(0)
+        ms = timed(torch, stream, fwd, reps=3)
+        hard[str(M)] = {"hard_layers": L // 4, "plan": plan, "down_first": bool(a.opts.down_first),
+                        "start_ms": round(a.t_start_ms, 3), "tuned_ms": round(ms, 3), "passes": a.passes,
+                        "trials": a.trials, "tune_seconds": round(tune_s, 1),
+                        "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+        del ws
+        log(f"[bench] stack hard/easy M={M}: {hard[str(M)]}")
+    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows, "decode_first": split,
+            "hard_easy_tuned": hard}
 
 
 def configs_sweep(uw, synth, torch, dev, stream, log):
