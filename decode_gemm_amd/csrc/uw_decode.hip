@@ -361,6 +361,10 @@ __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
 // tasks (the last round would otherwise run on a fraction of the waves).
 namespace lut {
 
+#ifndef KSM_EARLY
+#define KSM_EARLY 16
+#endif
+
 constexpr uint32_t kMaxWaves = 8;          // waves per workgroup at most
 constexpr int kWinWords = 1792;            // stream window per wave (7 KB)
 constexpr int kWinLoads = kWinWords / 256; // 16-byte loads per lane to fill it
@@ -684,20 +688,38 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 // sign/mantissa bytes of this lane's write-out items, in flight during the decode
                 // (items of 16 weights: chunk l = 4 it + lane / 16, group (lane / 4) % 4, piece lane % 4)
                 constexpr int kSmItems = MODE == DEC_FULL || MODE == DEC_DIRECT ? 16 : 1;
+                constexpr int kSmEarly = kSmItems > 1 ? KSM_EARLY : 1;  // prefetched before the decode
                 u32x4 smv[kSmItems];
+                auto load_sm = [&](int it) {
+                    const uint32_t l = 4 * it + (lane >> 4), g = (lane >> 2) & 3;
+                    const uint32_t cl = min(c0 + l, a.n_chunks - 1);
+                    const uint32_t el = cl * a.chunk, q = min(gq + g, (min(a.chunk, a.n_elems - el) >> 6) - 1);
+                    smv[it] = *reinterpret_cast<const u32x4*>(a.sm + el + 64 * q + 16 * (lane & 3));
+                };
                 if (MODE == DEC_FULL || MODE == DEC_DIRECT) {
     #pragma unroll
-                    for (int it = 0; it < kSmItems; it++) {
-                        const uint32_t l = 4 * it + (lane >> 4), g = (lane >> 2) & 3;
-                        const uint32_t cl = min(c0 + l, a.n_chunks - 1);
-                        const uint32_t el = cl * a.chunk, q = min(gq + g, (min(a.chunk, a.n_elems - el) >> 6) - 1);
-                        smv[it] = *reinterpret_cast<const u32x4*>(a.sm + el + 64 * q + 16 * (lane & 3));
-                    }
+                    for (int it = 0; it < kSmEarly; it++) load_sm(it);
                 }
                 decode(lds_tag, S);
-                if (s == 0 && next < a.n_tasks) load_window(nx, pw);
+                if (MODE == DEC_FULL || MODE == DEC_DIRECT) {
+    #pragma unroll
+                    for (int it = kSmEarly; it < kSmItems; it++) load_sm(it);
+                }
+                // the next task's stream window: right away, or (full and direct outputs) halfway
+                // through the write-out, once half of the prefetched sign/mantissa registers are
+                // free (holding both sets across the write-out made these modes spill)
+                constexpr bool kLateWindow = MODE == DEC_FULL || MODE == DEC_DIRECT;
+                constexpr int kWindowAt = 0;
+                auto prefetch_window = [&]() {
+                    if (s == 0 && next < a.n_tasks) load_window(nx, pw);
+                };
+                if (!kLateWindow) prefetch_window();
                 wave_sync();
 
+                // the lane index as an opaque value: the per-item lane constants below are then
+                // computed here, not hoisted out of every loop and held (spilled) for the whole task
+                uint32_t lw = lane;
+                asm volatile("" : "+v"(lw));
                 // ---- cooperative write-out of segment s of the wave's 64 chunks. Item
                 // (chunk l, group g of the segment, piece p); consecutive lanes cover
                 // consecutive output bytes of one chunk.
@@ -714,7 +736,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 if (MODE == DEC_EXP) {
     #pragma unroll 4
                     for (int it = 0; it < 16; it++) {
-                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t rm = info[l];
@@ -737,7 +759,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
     #pragma unroll
                     for (int it = 0; it < 16; it++) {
                         if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
-                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        if (it == kSmItems - 1 + kWindowAt) {
+                            prefetch_window();
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t e = el + 64 * q + 16 * p;
@@ -764,7 +790,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 } else if (MODE == DEC_IDX) {
     #pragma unroll
                     for (int it = 0; it < 8; it++) {
-                        const uint32_t item = it * 64 + lane, l = item >> 3, g = (item >> 1) & 3, p = item & 1, q = gq + g;
+                        const uint32_t item = it * 64 + lw, l = item >> 3, g = (item >> 1) & 3, p = item & 1, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t rm = info[l];
@@ -781,7 +807,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
     #pragma unroll
                     for (int it = 0; it < 16; it++) {
                         if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
-                        const uint32_t item = it * 64 + lane, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        if (it == kSmItems - 1 + kWindowAt) {
+                            prefetch_window();
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t fs = el + 64 * q;
