@@ -165,11 +165,39 @@ def main():
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    # autotune every M (cold-cache timing: the scrub buffer is overwritten before each rep)
-    plans = {}
+    # plans: uw_autotune per M (single launches, cold caches: the scrub buffer is
+    # overwritten before each rep), then the timed step's own conditions decide between
+    # its pick and every direct-palette variant: launches back to back over the rotated
+    # copies, X resident, as in the timed region
+    tuned = {}
     for M in Ms:
-        plans[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
+        tuned[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
                                warmup=2, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
+    log("[bench] autotune: " + ", ".join(f"M={M}: {tuned[M]!r} ({uw.variant_name(tuned[M].variant)})" for M in Ms))
+
+    def back_to_back_us(pipeline, variant, M, n):
+        for r in range(R):
+            uw.run_pipeline(pipeline, h, blobs[r], xs[M], ys[M], M, d_direct=idxs[r], d_ws=ws, ws_bytes=ws_bytes,
+                            variant=variant, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(n):
+            uw.run_pipeline(pipeline, h, blobs[r % R], xs[M], ys[M], M, d_direct=idxs[r % R], d_ws=ws,
+                            ws_bytes=ws_bytes, variant=variant, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    plans, choice = {}, {}
+    for M in Ms:
+        cands = [(tuned[M].pipeline, tuned[M].variant)]
+        cands += [(uw.PIPE_DIRECT, v) for v in range(uw.variant_count())
+                  if uw.variant_supports(v, N, K, M, uw.W_DIRECT) and (uw.PIPE_DIRECT, v) != cands[0]]
+        times = {c: back_to_back_us(c[0], c[1], M, 4 * R) for c in cands}
+        best = min(times, key=times.get)
+        plans[M] = uw.Plan(best[0], best[1], times[best] / 1e3, 0)
+        choice[M] = {"autotune": f"{uw.PIPELINE_NAMES[cands[0][0]]} / {uw.variant_name(cands[0][1])}",
+                     "autotune_back_to_back_us": round(times[cands[0]], 2), "candidates": len(cands)}
     log("[bench] plans: " + ", ".join(f"M={M}: {plans[M]!r} ({uw.variant_name(plans[M].variant)})" for M in Ms))
 
     seq = [0]
@@ -226,7 +254,7 @@ def main():
         + ", ".join(f"{M}: {mean_ms[M] * 1e3:.1f}" for M in Ms))
 
     detail = {"plans": {str(M): {"pipeline": uw.PIPELINE_NAMES[plans[M].pipeline], "variant": uw.variant_name(plans[M].variant),
-                                 "us": round(mean_ms[M] * 1e3, 2),
+                                 "us": round(mean_ms[M] * 1e3, 2), "selection": choice[M],
                                  "hbm_frac_compressed": round(algorithmic_bytes(h, M, plans[M].pipeline) / (mean_ms[M] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                         for M in Ms},
               "blob_bytes_per_weight": round(blob.size / (N * K), 4),
