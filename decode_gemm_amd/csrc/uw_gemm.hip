@@ -1150,10 +1150,9 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Raise a kernel's dynamic-LDS limit above the 64 KB default once per process (gfx950
-// has 160 KB of LDS per CU).
-// Raise a kernel's dynamic LDS limit past 64 KB, once per device (bit d of `done`; a
-// lost update between racing threads only repeats the call).
+// Raise a kernel's dynamic LDS limit past the 64 KB default (gfx950 has 160 KB per CU),
+// once per device (bit d of `done`; a lost update between racing threads only repeats the
+// call).
 hipError_t allow_lds(const void* fn, size_t bytes, uint64_t& done)
 {
     if (bytes <= 64 * 1024) return hipSuccess;
