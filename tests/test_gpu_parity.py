@@ -180,6 +180,46 @@ def test_gemm_one_hot_rows_give_weights_exactly():
                 assert np.array_equal(y, ref), f"one-hot M={M} src={src} variant={v}"
 
 
+def test_gemm_direct_raw_heavy_blocks():
+    """Direct plane with blocks of very different raw density: a few raw groups in some
+    16-row tiles, rows 64..95 raw in every group (hundreds of side-table rows per
+    workgroup). One-hot X rows give the weights exactly through every direct variant and
+    the fused gate/up launch."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(97)
+    N, K = 160, 1152
+    e = rng.integers(110, 126, size=(N, K)).astype(np.uint16)
+    e[64:96, ::64] = 200 + (np.arange(32) % 20)[:, None]  # rows 64..95: raw in all 18 groups
+    e[5, 64 * 3 + 7] = 221
+    e[40, 64 * 10] = 222
+    e[130, 64 * 17 + 63] = 223
+    w = (((e << 7) | (rng.integers(0, 256, size=e.shape).astype(np.uint16) & 0x807F)) & 0xFFFF).astype(np.uint16)
+    m = Mat(w, 256)
+    assert m.h.n_raw == 32 * 18 + 3
+    direct = m.decode("direct")[0]
+    planes = {uw.W_DIRECT: direct}
+    wf = synth.bf16_bits_to_f32(w)
+    ks = np.array([0, 7, 63, 64 * 3 + 7, 64 * 10, 64 * 17 + 63, 640, 1151])
+    for M in (1, 16, 64):
+        x = np.zeros((M, K), np.uint16)
+        for r in range(M):
+            x[r, ks[r % len(ks)]] = 0x3F80
+        ref = np.stack([wf[:, ks[r % len(ks)]] for r in range(M)])
+        for v in _variants_for(m, M, uw.W_DIRECT):
+            log(f"  raw rows M={M} variant={v}")
+            assert np.array_equal(_run_gemm(m, planes, uw.W_DIRECT, x, v), ref), f"M={M} variant={v}"
+        d_x = dev(x)
+        yg, yu = empty_f32(M, N), empty_f32(M, N)
+        h = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        for v in (-1, 5, 14, 3, 2):
+            log(f"  raw rows fused M={M} variant={v}")
+            yg.fill_(float("nan"))
+            yu.fill_(float("nan"))
+            uw.recon_gemm_gate_up(m.h, m.d_blob, direct, m.h, m.d_blob, direct, d_x, yg, yu, h, M, variant=v)
+            _sync()
+            assert np.array_equal(host(yg), ref) and np.array_equal(host(yu), ref), f"fused M={M} variant={v}"
+
+
 def test_gemm_small_integers_exact():
     rng = np.random.default_rng(41)
     N, K = 200, 320
