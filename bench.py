@@ -250,6 +250,24 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom_key),
                 "kernel": dom_key,
                 "bytes_per_launch": int(alg), "mean_launch_us": round(mean_ms[Mdom] * 1e3, 2)}
+    # the practical read ceiling beside the published peak: a plain streaming read of the
+    # same rotated planes (uw_stream_read, no other work), back to back like the GEMMs
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    pbytes = uw.direct_plane_bytes(h) // 16 * 16
+    for r in range(R):
+        uw.stream_read(idxs[r], sink, pbytes, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(4 * R):
+        uw.stream_read(idxs[r % R], sink, pbytes, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    read_us = a.elapsed_time(b) / (4 * R) * 1e3
+    read_gbs = pbytes / (read_us * 1e-6) / 1e9
+    roofline["read_ceiling_GBs"] = round(read_gbs, 1)
+    roofline["frac_of_read_ceiling"] = round(achieved / read_gbs, 4)
+    log(f"[bench] plain streaming read of one plane: {read_us:.1f} us = {read_gbs:.0f} GB/s "
+        f"({read_gbs / HBM_PEAK_GBS:.3f} of the peak); dominant kernel at {achieved / read_gbs:.3f} of it")
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s uncompressed-equivalent; per-M us: "
         + ", ".join(f"{M}: {mean_ms[M] * 1e3:.1f}" for M in Ms))
 

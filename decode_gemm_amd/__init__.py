@@ -163,6 +163,7 @@ def _load():
         "uw_stream_pair_create": ([ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)], ctypes.c_int),
         "uw_stream_destroy": ([P], ctypes.c_int),
         "uw_stream_cu_count": ([P, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+        "uw_stream_read": ([P, ctypes.c_size_t, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -383,6 +384,13 @@ def stream_pair_create(decode_cus: int):
 
 def stream_destroy(handle: int) -> None:
     _check(lib.uw_stream_destroy(handle))
+
+
+def stream_read(src, sink, nbytes: int | None = None, stream=None) -> None:
+    """uw_stream_read: read the device tensor src (its first nbytes, default all) once with
+    a plain streaming kernel; sink is a device tensor of at least 4 bytes it may modify."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib.uw_stream_read(_ptr(src), n, _ptr(sink), _stream(stream)))
 
 
 def stream_cu_count(stream=None) -> int:

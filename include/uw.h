@@ -441,6 +441,20 @@ uw_status uw_stream_pair_create(int decode_cus, void** gemm_stream, void** decod
 uw_status uw_stream_destroy(void* stream);
 uw_status uw_stream_cu_count(void* stream, int* out);
 
+/*
+ * uw_stream_read (device). Measurement helper for the HBM roofline ("GPU memory
+ * bottleneck": generating a token is bound by the weight bytes read from HBM, not by the
+ * arithmetic, so the small-batch GEMM is priced by its bytes): reads d_src[0, bytes)
+ * once with a plain streaming kernel on `stream` (eight workgroups per compute unit the
+ * stream may use, a grid-stride sweep of 16-byte coalesced loads, sixteen in flight per
+ * thread) and computes nothing from it. Timing it with events gives the read rate a kernel that does
+ * no other work reaches on this part, the practical ceiling beside the published peak.
+ * d_src: device, 16-byte aligned, bytes a multiple of 16 (0 is a no-op); d_sink: one
+ * device word the kernel may modify (its value is meaningless). Errors: UW_EINVAL
+ * (NULL pointers, misalignment), UW_EHIP.
+ */
+uw_status uw_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

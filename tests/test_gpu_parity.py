@@ -317,6 +317,25 @@ def test_run_pipeline_error_paths():
     uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 0)  # M = 0: no-op
 
 
+def test_stream_read_sizes_and_argument_errors():
+    """The bench's read-ceiling helper: ragged and empty sizes run to completion, and
+    misaligned or NULL arguments are rejected on the host before any launch."""
+    buf = empty_u8(3 << 20)
+    sink = zeros_u32(1)
+    for n in (0, 16, 4096 + 16, (1 << 20) + 48, 3 << 20):
+        uw.stream_read(buf, sink, n)
+    _sync()
+    with pytest.raises(uw.UwError) as e:
+        uw.stream_read(buf.data_ptr() + 4, sink, 64)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.stream_read(buf, sink, 40)
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:
+        uw.stream_read(buf, None, 64)
+    assert e.value.status == uw.EINVAL
+
+
 # ---------------------------------------------------------------- full sizes
 def _full_size_case(cfg, proj, Ms, n_samples=4096):
     w = synth.gen_weight(cfg, proj)
