@@ -609,8 +609,9 @@ def configs_sweep(uw, synth, torch, dev, stream, log):
 
 
 def large_m_line(uw, synth, torch, dev, stream, log):
-    """TFLOP/s of the reconstructive GEMM on the down_proj shape at M = 4096 (MFMA-bound),
-    best of the direct-palette and plain-bf16 variants, vs the 2.5 PFLOP/s bf16 peak."""
+    """TFLOP/s on the down_proj shape at M = 4096 (MFMA-bound) of the direct-palette pipeline
+    and of the full-decode pipeline (decode, then the best plain bf16 GEMM: ours or the vendor
+    library's), each with its autotuned variant, vs the 2.5 PFLOP/s bf16 peak."""
     cfg = synth.CONFIGS["down"]
     w = synth.gen_weight(cfg, "down")
     blob = uw.encode(w)

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libuw.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-HIP_SOURCES = ["uw_decode.hip", "uw_gemm.hip", "uw_runtime.hip"]
+HIP_SOURCES = ["uw_decode.hip", "uw_gemm.hip", "uw_runtime.hip", "uw_vendor.hip"]
 HOST_SOURCES = ["uw_host.cpp"]
 # Packed fp32 VALU forms are kept out of the generated code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -52,7 +52,8 @@ def build(verbose: bool = False) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    # hipBLASLt: the vendor GEMM variant of the full-decode pipeline's plain GEMM
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L/opt/rocm/lib", "-lhipblaslt", "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

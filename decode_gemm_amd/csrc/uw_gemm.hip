@@ -33,6 +33,11 @@
 
 namespace uw {
 
+// Y = X * W^T on bf16 weights with the vendor GEMM (uw_vendor.hip); hipErrorNotSupported
+// when the library offers no algorithm for the problem.
+hipError_t vendor_gemm_bf16(const uint16_t* w, const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+                            int64_t ldx, int64_t ldy, hipStream_t s);
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1130,7 +1135,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
 
 struct Variant {
     const char* name;
-    int kind;  // 0 skinny, 1 tiled, 2 wide
+    int kind;  // 0 skinny, 1 tiled, 2 wide, 3 the vendor GEMM (plain bf16 weights only)
     int rt, nw, u;
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
@@ -1146,7 +1151,7 @@ const Variant kVariants[] = {
     {"skinny rt4 u4 w4", 0, 4, 4, 4, 0, 0},  {"skinny rt4 u2 w8 x1", 0, 4, 8, 2, 0, 0, 1},
     {"skinny rt4 u2 w4 x1", 0, 4, 4, 2, 0, 0, 1}, {"skinny rt2 u4 w8 x1", 0, 2, 8, 4, 0, 0, 1},
     {"skinny rt4 u2 w4 xt", 0, 4, 4, 2, 0, 0, 0, 1}, {"skinny rt4 u4 w4 xt", 0, 4, 4, 4, 0, 0, 0, 1},
-    {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1},
+    {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1}, {"vendor hipblaslt", 3, 0, 0, 0, 0, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1265,6 +1270,10 @@ hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
 template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
+    if (v.kind == 3) {
+        if (SRC != UW_W_BF16) return hipErrorNotSupported;
+        return vendor_gemm_bf16(static_cast<const uint16_t*>(g.wplane), g.x, g.y, g.M, g.N, g.K, g.ldx, g.ldy, s);
+    }
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
     if (v.kind == 0) {
         if (v.rt == 1 && v.u == 8) return launch_skinny_rt<SRC, CONTIG, 1, 8, 4>(g, s);
@@ -1451,6 +1460,7 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     case UW_W_IDX: e = launch_src<UW_W_IDX, false>(g, var, s); break;
     default: e = contig ? launch_src<UW_W_DIRECT, true>(g, var, s) : launch_src<UW_W_DIRECT, false>(g, var, s); break;
     }
+    if (e == hipErrorNotSupported && var.kind == 3) return fail(UW_EUNSUPPORTED, "the vendor GEMM offers no algorithm for this problem");
     if (e != hipSuccess) return fail(UW_EHIP, "GEMM launch failed: %s", hipGetErrorString(e));
     return UW_OK;
 }
@@ -1478,9 +1488,9 @@ const char* uw_variant_name(int variant)
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src)
 {
     (void)N;
-    (void)src;
     if (variant < 0 || variant >= uw::kNumVariants || K % 64 || K < 64) return 0;
     const uw::Variant& v = uw::kVariants[variant];
+    if (v.kind == 3) return M >= 1 && src == UW_W_BF16;
     if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }

@@ -179,6 +179,11 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
                         if (r >= warmup && hipEventRecord(e0, s) != hipSuccess) { result = fail(UW_EHIP, "event record failed"); break; }
                         uw_status st = uw_run_pipeline(p, v, h, a->d_blob, a->d_direct, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
                                                        a->ws_bytes, nullptr, stream);
+                        if (st == UW_EUNSUPPORTED) {  // e.g. no vendor algorithm for this shape: not a candidate
+                            clear_error();
+                            t.clear();
+                            break;
+                        }
                         if (st != UW_OK) { result = st; break; }
                         if (r >= warmup) {
                             if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
@@ -190,7 +195,8 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
                             t.push_back(ms);
                         }
                     }
-                    if (result != UW_OK || t.empty()) break;
+                    if (result != UW_OK) break;
+                    if (t.empty()) continue;
                     std::sort(t.begin(), t.end());
                     const float med = t[t.size() / 2];
                     if (med < best.t_ms) {

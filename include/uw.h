@@ -24,7 +24,9 @@
  *     with leading dimension ldx; Y = X * W^T is [M][N] fp32 with leading dimension ldy.
  *   - "d_" pointers are device (HBM) pointers; all others are host pointers.
  *   - The caller owns every buffer. The library never allocates or frees device memory
- *     and keeps no pointer after a call returns.
+ *     and keeps no pointer after a call returns. (One exception: the first call of the
+ *     "vendor hipblaslt" GEMM variant on a device creates a hipBLASLt handle, which the
+ *     vendor library backs with resources of its own until the process ends.)
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Device
  *     calls are asynchronous on that stream; their return value reports argument
  *     validation and launch errors only.
@@ -235,7 +237,12 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
 /* Kernel variants of uw_recon_gemm (tile shape per CU and pipelining depth, "How the
  * reconstructive matmul works": wider tiles for large batches, deeper buffers for small
  * ones). uw_variant_count() variants exist; uw_variant_name() describes one;
- * uw_variant_supports() says whether a variant accepts (N, K, M, src). */
+ * uw_variant_supports() says whether a variant accepts (N, K, M, src). The variant named
+ * "vendor hipblaslt" takes plain bf16 weights only (UW_W_BF16, the GEMM of the
+ * full-decode pipeline, which hands the rebuilt weights to the vendor's standard matrix
+ * multiply: "Four ways to use compressed weights"); it calls hipBLASLt with fp32
+ * accumulation and fp32 output and returns UW_EUNSUPPORTED if that library offers no
+ * algorithm for the problem (uw_autotune then skips it). */
 int uw_variant_count(void);
 const char* uw_variant_name(int variant);
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
