@@ -99,7 +99,8 @@ def decode_bytes(h, mode):
     return {"full": s["sm"] + codes + s["row_base"] + s["raw"] + 2 * NK,
             "exp": codes + s["row_base"] + s["raw"] + NK,
             "idx": codes + NK // 2,
-            "direct": s["sm"] + codes + s["row_base"] + s["raw"] + direct_bytes(h)}[mode]
+            "direct": s["sm"] + codes + s["row_base"] + s["raw"] + direct_bytes(h),
+            "expand": direct_bytes(h) + 2 * NK}[mode]
 
 
 def gemm_bytes(h, M, src):
@@ -115,7 +116,7 @@ def algorithmic_bytes(h, M, pipeline):
     direct palette, whose plane is made at load) plus the GEMM's."""
     if pipeline == 3:
         return gemm_bytes(h, M, 3)
-    mode, src = {0: ("full", 0), 1: ("exp", 1), 2: ("idx", 2)}[pipeline]
+    mode, src = {0: ("full", 0), 1: ("exp", 1), 2: ("idx", 2), 4: ("expand", 0)}[pipeline]
     return decode_bytes(h, mode) + gemm_bytes(h, M, src)
 
 
@@ -282,7 +283,7 @@ def main():
         # every pipeline at every M (best variant each), cold weights via rotation
         pip = {}
         for M in Ms:
-            for p in range(4):
+            for p in range(5):
                 pl = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=5,
                                  warmup=1, pipeline_mask=1 << p, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
                 ts = []
@@ -404,7 +405,7 @@ def shape_sweep(uw, synth, torch, dev, stream, log, cfg, proj, Ms, copies=2):
         x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
         y = torch.empty(M, N, dtype=torch.float32, device=dev)
         per = {}
-        for p in range(4):
+        for p in range(5):
             pl = uw.autotune(h, blobs[0], x, y, [M], d_direct=planes[0], d_ws=ws, ws_bytes=ws_bytes, reps=5, warmup=2,
                              pipeline_mask=1 << p)[0]
             ms = timed(torch, stream, lambda r: uw.run_pipeline(p, h, blobs[r % copies], x, y, M, d_direct=planes[r % copies],
@@ -609,8 +610,9 @@ def configs_sweep(uw, synth, torch, dev, stream, log):
 
 
 def large_m_line(uw, synth, torch, dev, stream, log):
-    """TFLOP/s on the down_proj shape at M = 4096 (MFMA-bound) of the direct-palette pipeline
-    and of the full-decode pipeline (decode, then the best plain bf16 GEMM: ours or the vendor
+    """TFLOP/s on the down_proj shape at M = 4096 (MFMA-bound) of the direct-palette pipeline,
+    the full-decode pipeline and the expand pipeline (bf16 weights rebuilt in HBM from the
+    Huffman stream or from the direct plane, then the best plain bf16 GEMM: ours or the vendor
     library's), each with its autotuned variant, vs the 2.5 PFLOP/s bf16 peak."""
     cfg = synth.CONFIGS["down"]
     w = synth.gen_weight(cfg, "down")
@@ -624,7 +626,7 @@ def large_m_line(uw, synth, torch, dev, stream, log):
     y = torch.empty(M, N, dtype=torch.float32, device=dev)
     ws = torch.empty(uw.workspace_bytes(h, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
     res = {}
-    for p in (uw.PIPE_DIRECT, uw.PIPE_FULL):
+    for p in (uw.PIPE_DIRECT, uw.PIPE_FULL, uw.PIPE_EXPAND):
         pl = uw.autotune(h, b, x, y, [M], d_direct=idx, d_ws=ws, ws_bytes=ws.numel(), reps=5, warmup=2,
                          pipeline_mask=1 << p)[0]
         ts = []

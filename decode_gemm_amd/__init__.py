@@ -19,7 +19,8 @@ __all__ = [
     "UwError", "Header", "Plan", "lib", "encode", "inspect", "validate_header", "decode_full",
     "decode_exponent", "transcode_palette", "prepare_direct", "recon_gemm", "run_pipeline", "autotune", "swiglu",
     "workspace_bytes", "direct_plane_bytes", "variant_count", "variant_name", "variant_supports", "version",
-    "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT",
+    "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT", "PIPE_EXPAND",
+    "expand_direct",
     "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS", "Proj", "MlpLayer", "proj", "mlp_layers", "mlp_stack_workspace",
     "mlp_stack_forward",
 ]
@@ -30,8 +31,8 @@ STATUS = {0: "UW_OK", 1: "UW_EINVAL", 2: "UW_ESHAPE", 3: "UW_EFORMAT", 4: "UW_ER
           6: "UW_EHIP", 7: "UW_EUNSUPPORTED", 8: "UW_EINTERNAL"}
 OK, EINVAL, ESHAPE, EFORMAT, ERANGE, ENOSPACE, EHIP, EUNSUPPORTED, EINTERNAL = range(9)
 W_BF16, W_EXP, W_IDX, W_DIRECT = 0, 1, 2, 3
-PIPE_FULL, PIPE_EXP, PIPE_TRANSCODE, PIPE_DIRECT = 0, 1, 2, 3
-PIPELINE_NAMES = {0: "full", 1: "exp", 2: "transcode", 3: "direct"}
+PIPE_FULL, PIPE_EXP, PIPE_TRANSCODE, PIPE_DIRECT, PIPE_EXPAND = 0, 1, 2, 3, 4
+PIPELINE_NAMES = {0: "full", 1: "exp", 2: "transcode", 3: "direct", 4: "expand"}
 DERR_BADCODE, DERR_CHUNKLEN = 1, 2
 
 
@@ -164,6 +165,7 @@ def _load():
         "uw_stream_destroy": ([P], ctypes.c_int),
         "uw_stream_cu_count": ([P, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
         "uw_stream_read": ([P, ctypes.c_size_t, P, P], ctypes.c_int),
+        "uw_expand_direct": ([H, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)
@@ -266,6 +268,11 @@ def transcode_palette(h: Header, d_blob, d_idx, d_err=None, stream=None) -> None
 def prepare_direct(h: Header, d_blob, d_direct, d_err=None, stream=None) -> None:
     """uw_prepare_direct: the direct-palette plane (direct_plane_bytes(h) bytes), made once at load."""
     _check(lib.uw_prepare_direct(ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), _ptr(d_err), _stream(stream)))
+
+
+def expand_direct(h: Header, d_direct, d_w, stream=None) -> None:
+    """uw_expand_direct: bf16 W[N][K] (2*N*K bytes at d_w) rebuilt from a direct plane."""
+    _check(lib.uw_expand_direct(ctypes.byref(h), _ptr(d_direct), _ptr(d_w), _stream(stream)))
 
 
 def direct_plane_bytes(h: Header) -> int:

@@ -644,6 +644,41 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
     });
 }
 
+// ------------------------------------------------------------------------- expand
+// Direct plane -> bf16 W[N][K] in HBM, for a plain GEMM afterwards (the full-decode
+// pipeline's second half, fed from the load-time plane instead of the Huffman stream).
+// One wave per (row tile, group) block, lane l = 16 g + r: the 16 weights [16g, 16g+16) of
+// row 16 t + r, rebuilt exactly as the GEMMs rebuild them (palette, or the side table's
+// verbatim exponents on a raw row), then stored as two 16-byte pieces.
+template <bool CONTIG>
+__global__ void __launch_bounds__(256) expand_direct_kernel(GemmArgs a, uint16_t* w)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t G = static_cast<uint64_t>(a.K >> 6);
+    const uint64_t blk = static_cast<uint64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t * G + j
+    if (blk >= static_cast<uint64_t>(a.tiles) * G) return;
+    const uint64_t t = blk / G, j = blk - t * G;
+    const uint8_t* b = static_cast<const uint8_t*>(a.wplane) + 1536 * blk;
+    W16 wv;
+    wv.a = *reinterpret_cast<const u32x4*>(b + 16 * lane);
+    const u32x2 v = *reinterpret_cast<const u32x2*>(b + 1024 + 8 * lane);
+    wv.b.x = v.x;
+    wv.b.y = v.y;
+    wv.b.z = 0;
+    wv.b.w = 0;
+    const u32x2 meta = *reinterpret_cast<const u32x2*>(a.dmeta + 8 * blk);
+    const int r = static_cast<int>(lane & 15), g = static_cast<int>(lane >> 4);
+    u32x4 p0, p1;
+    rebuild16<UW_W_DIRECT, CONTIG>(a, wv, p0, p1);
+    if ((meta.x >> r) & 1u) rebuild16_raw(wv, *raw_exp_addr(a, meta, r, g, a.dmeta), p0, p1);
+    const int64_t row = static_cast<int64_t>(16 * t) + r;
+    if (row < a.N) {
+        u32x4* o = reinterpret_cast<u32x4*>(w + row * a.K + static_cast<int64_t>(64 * j) + 16 * g);
+        o[0] = p0;
+        o[1] = p1;
+    }
+}
+
 // ------------------------------------------------------------------------- tiled
 // 256 threads = 4 waves as 2 x 2; block tile BN (weight rows) x BM (activation rows);
 // wave tile (BN/2) x (BM/2) of 16 x 16 MFMA tiles. LDS per stage: W and X slices of 64 k
@@ -1440,6 +1475,38 @@ uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
     return UW_OK;
 }
 
+uw_status launch_expand_direct(const uw_header* h, const uint8_t* d_direct, uint16_t* d_w, void* stream)
+{
+    clear_error();
+    if (!h || !d_direct || !d_w) return fail(UW_EINVAL, "NULL argument");
+    uw_status st = check_header(h, h->total_bytes);
+    if (st != UW_OK) return st;
+    if (!aligned(d_direct, 16) || !aligned(d_w, 16)) return fail(UW_EINVAL, "device pointers must be 16-byte aligned");
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.wplane = d_direct;
+    g.N = h->N;
+    g.K = h->K;
+    ValueOrder vo;
+    value_order(h, &vo);
+    std::memcpy(g.vpal, vo.sorted, 16);
+    g.base4 = vo.sorted[0] * 0x01010101u;
+    const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
+    g.tiles = static_cast<uint32_t>(T);
+    g.dmeta = d_direct + 1536 * T * G;
+    g.dside = g.dmeta + (8 * T * G + 63) / 64 * 64;
+    if (T * G == 0) return UW_OK;
+    const dim3 grid(static_cast<uint32_t>((T * G + 3) / 4));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (vo.contiguous)
+        hipLaunchKernelGGL(expand_direct_kernel<true>, grid, dim3(256), 0, s, g, d_w);
+    else
+        hipLaunchKernelGGL(expand_direct_kernel<false>, grid, dim3(256), 0, s, g, d_w);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(UW_EHIP, "expand launch failed: %s", hipGetErrorString(e));
+    return UW_OK;
+}
+
 uw_status launch_gemm(const uw_gemm_args* p, void* stream)
 {
     clear_error();
@@ -1470,6 +1537,11 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
 extern "C" {
 
 uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream) { return uw::launch_gemm(args, stream); }
+
+uw_status uw_expand_direct(const uw_header* h, const uint8_t* d_direct, uint16_t* d_w, void* stream)
+{
+    return uw::launch_expand_direct(h, d_direct, d_w, stream);
+}
 
 uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
                                 void* stream)

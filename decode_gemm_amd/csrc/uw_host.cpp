@@ -445,6 +445,7 @@ uw_status uw_workspace_bytes(const uw_header* h, int32_t pipeline, size_t* out)
     case UW_PIPE_EXP: *out = n; return UW_OK;
     case UW_PIPE_TRANSCODE: *out = n / 2; return UW_OK;
     case UW_PIPE_DIRECT: *out = 0; return UW_OK;
+    case UW_PIPE_EXPAND: *out = 2 * n; return UW_OK;
     default: return fail(UW_EINVAL, "unknown pipeline %d", pipeline);
     }
 }

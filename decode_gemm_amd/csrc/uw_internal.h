@@ -50,6 +50,7 @@ constexpr uint64_t kStreamSlack = 64;
 
 // Device-side launchers (uw_decode.hip, uw_gemm.hip).
 enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2, DEC_DIRECT = 3 };
+constexpr int kPipelines = 5;  // uw_pipeline values 0 .. kPipelines - 1
 uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err,
                         void* stream);
 uw_status launch_gemm(const uw_gemm_args* a, void* stream);

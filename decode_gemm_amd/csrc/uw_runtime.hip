@@ -132,6 +132,12 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
         g.src = UW_W_DIRECT;
         g.d_wplane = d_direct;
         break;
+    case UW_PIPE_EXPAND:
+        if (!d_direct) return fail(UW_EINVAL, "the expand pipeline needs the direct plane (uw_prepare_direct)");
+        if ((st = uw_expand_direct(h, d_direct, static_cast<uint16_t*>(d_ws), stream)) != UW_OK) return st;
+        g.src = UW_W_BF16;
+        g.d_wplane = d_ws;
+        break;
     default: return fail(UW_EINVAL, "unknown pipeline %d", pipeline);
     }
     return uw_recon_gemm(&g, stream);
@@ -145,7 +151,7 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
         const uw_header* h = a->h;
         const int reps = a->reps > 0 ? a->reps : 20;
         const int warmup = a->warmup > 0 ? a->warmup : 3;
-        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0xFu;
+        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0x1Fu;
         const uint32_t vmask = a->variant_mask ? static_cast<uint32_t>(a->variant_mask) : 0xFFFFFFFFu;
         hipStream_t s = static_cast<hipStream_t>(stream);
         hipEvent_t e0, e1;
@@ -162,13 +168,14 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
             best.variant = -1;
             best.t_ms = 3.0e38f;
             best.reserved = 0;
-            for (int p = 0; p < 4 && result == UW_OK; p++) {
+            for (int p = 0; p < kPipelines && result == UW_OK; p++) {
                 if (!(pmask >> p & 1u)) continue;
-                if (p == UW_PIPE_DIRECT && !a->d_direct) continue;
+                if ((p == UW_PIPE_DIRECT || p == UW_PIPE_EXPAND) && !a->d_direct) continue;
                 size_t need = 0;
                 uw_workspace_bytes(h, p, &need);
                 if (need > a->ws_bytes) continue;
-                const int32_t src = p == UW_PIPE_FULL ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP : p == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
+                const int32_t src = p == UW_PIPE_FULL || p == UW_PIPE_EXPAND ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP
+                                    : p == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
                 for (int v = 0; v < uw_variant_count() && result == UW_OK; v++) {
                     if (!(vmask >> v & 1u) || !uw_variant_supports(v, h->N, h->K, M, src)) continue;
                     std::vector<float> t;
@@ -261,8 +268,8 @@ uw_status stack_layout(const uw_mlp_layer* L, int n, int64_t M, int slots, Stack
         for (int q = 0; q < 3; q++) {
             const uw_proj& pr = role_of(L[l], q);
             if (!pr.h || !pr.d_blob) return fail(UW_EINVAL, "layer %d projection %d: NULL header or blob", l, q);
-            if (pr.pipeline == UW_PIPE_DIRECT && !pr.d_direct)
-                return fail(UW_EINVAL, "layer %d projection %d: direct palette needs the direct plane", l, q);
+            if ((pr.pipeline == UW_PIPE_DIRECT || pr.pipeline == UW_PIPE_EXPAND) && !pr.d_direct)
+                return fail(UW_EINVAL, "layer %d projection %d: pipeline %d needs the direct plane", l, q, pr.pipeline);
             size_t need = 0;
             uw_status st = uw_workspace_bytes(pr.h, pr.pipeline, &need);
             if (st != UW_OK) return st;
@@ -293,6 +300,7 @@ uw_status decode_proj(const uw_proj& p, void* slot, void* stream)
     case UW_PIPE_EXP: return uw_decode_exponent(p.h, p.d_blob, static_cast<uint8_t*>(slot), nullptr, stream);
     case UW_PIPE_TRANSCODE: return uw_transcode_palette(p.h, p.d_blob, static_cast<uint8_t*>(slot), nullptr, stream);
     case UW_PIPE_DIRECT: return UW_OK;
+    case UW_PIPE_EXPAND: return uw_expand_direct(p.h, p.d_direct, static_cast<uint16_t*>(slot), stream);
     default: return fail(UW_EINVAL, "unknown pipeline %d", p.pipeline);
     }
 }
@@ -311,7 +319,7 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     g.d_y = y;
     g.ldy = ldy;
     g.variant = p.variant;
-    g.src = p.pipeline == UW_PIPE_FULL ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
+    g.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
           : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
     g.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
     return uw_recon_gemm(&g, stream);
@@ -590,7 +598,7 @@ uw_status uw_mlp_stack_autotune(uw_stack_tune_args* a, void* stream)
         uw_mlp_layer* L = a->layers;
         const int reps = a->reps > 0 ? a->reps : 5, warmup = a->warmup > 0 ? a->warmup : 1;
         const int max_passes = a->max_passes > 0 ? a->max_passes : 4;
-        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0xFu;
+        const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0x1Fu;
         const int slots = opt_slots(&a->opts);
         // layer class: 0 when all three projections have direct planes ("easy" once they
         // use them), 1 otherwise (a "hard" layer, which always needs preprocessing)
@@ -669,10 +677,10 @@ uw_status uw_mlp_stack_autotune(uw_stack_tune_args* a, void* stream)
             for (int c = 0; c < 2 && st == UW_OK; c++) {
                 if (!present[c]) continue;
                 for (int r = 0; r < 3 && st == UW_OK; r++) {
-                    for (int p = 0; p < 4 && st == UW_OK; p++) {
+                    for (int p = 0; p < kPipelines && st == UW_OK; p++) {
                         const int cur = get(c, r);
                         if (p == cur || !(pmask >> p & 1u)) continue;
-                        if (p == UW_PIPE_DIRECT && c == 1) {
+                        if ((p == UW_PIPE_DIRECT || p == UW_PIPE_EXPAND) && c == 1) {
                             // a hard layer may still hold a direct plane for this projection
                             bool all = true;
                             for (int l = 0; l < n; l++)

@@ -183,6 +183,17 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
  * swaps in its verbatim exponents. d_err as for the decoders.
  */
 uw_status uw_prepare_direct(const uw_header* h, const void* d_blob, uint8_t* d_direct, uint32_t* d_err, void* stream);
+/*
+ * uw_expand_direct (device). The bf16 weights W[N][K] (row-major, bit patterns) written to
+ * d_w from a direct plane made by uw_prepare_direct: the full decode of "Four ways to use
+ * compressed weights" (original weights rebuilt in HBM for a plain GEMM), fed from the
+ * load-time palette plane instead of the Huffman stream, so it is a pure streaming kernel
+ * (reads ~1.52 bytes per weight, writes 2). The result is bit-identical to uw_decode_full
+ * of the blob the plane was made from. d_direct, d_w: device, 16-byte aligned; d_w holds
+ * 2*N*K bytes. Errors: UW_EINVAL (NULL or misaligned pointers), UW_EFORMAT (bad header),
+ * UW_EHIP.
+ */
+uw_status uw_expand_direct(const uw_header* h, const uint8_t* d_direct, uint16_t* d_w, void* stream);
 /* Bytes of the direct plane of a blob: 1536*T*G + round_up(8*T*G, 64) + 64*n_raw. */
 uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out);
 
@@ -254,8 +265,18 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
  *   UW_PIPE_TRANSCODE uw_transcode_palette into workspace, then reconstructive GEMM
  *   UW_PIPE_DIRECT    reconstructive GEMM on the direct plane prepared once at load
  *                     (uw_prepare_direct)
+ *   UW_PIPE_EXPAND    uw_expand_direct of that direct plane into workspace, then plain
+ *                     bf16 GEMM: the full-decode pipeline fed from the load-time plane
+ *                     (a streaming kernel) instead of the Huffman stream, for batches
+ *                     large enough that the vendor GEMM on bf16 weights wins
  */
-typedef enum { UW_PIPE_FULL = 0, UW_PIPE_EXP = 1, UW_PIPE_TRANSCODE = 2, UW_PIPE_DIRECT = 3 } uw_pipeline;
+typedef enum {
+    UW_PIPE_FULL = 0,
+    UW_PIPE_EXP = 1,
+    UW_PIPE_TRANSCODE = 2,
+    UW_PIPE_DIRECT = 3,
+    UW_PIPE_EXPAND = 4
+} uw_pipeline;
 
 /* A per-(matrix, M) execution plan: which pipeline and which GEMM variant ("Why no
  * single pipeline wins": the per-model profile). t_ms = measured median time. */
@@ -266,13 +287,13 @@ typedef struct {
     int32_t reserved;
 } uw_plan;
 
-/* Workspace bytes a pipeline needs for a matrix (the preprocessing slot: 2, 1, 0.5 or 0
- * bytes per weight for full / exp / transcode / direct). */
+/* Workspace bytes a pipeline needs for a matrix (the preprocessing slot: 2, 1, 0.5, 0 or
+ * 2 bytes per weight for full / exp / transcode / direct / expand). */
 uw_status uw_workspace_bytes(const uw_header* h, int32_t pipeline, size_t* out);
 
 /* Run one pipeline end to end on `stream`: decode into d_ws if the pipeline needs it,
- * then the GEMM. d_direct = the direct plane from uw_prepare_direct (UW_PIPE_DIRECT
- * only). */
+ * then the GEMM. d_direct = the direct plane from uw_prepare_direct (UW_PIPE_DIRECT and
+ * UW_PIPE_EXPAND only). */
 uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob,
                           const uint8_t* d_direct, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
                           int64_t ldy, void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream);
@@ -282,7 +303,8 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
  * variant) pair on the caller's buffers with HIP events (warmup untimed launches, then
  * the median of reps timed ones) and return the fastest in out[i] ("Why no single
  * pipeline wins", "Sharing the GPU between decode and compute": measured, not
- * heuristic). d_direct may be NULL, in which case UW_PIPE_DIRECT is not a candidate.
+ * heuristic). d_direct may be NULL, in which case UW_PIPE_DIRECT and UW_PIPE_EXPAND are
+ * not candidates; pipeline_mask 0 means every pipeline (bits 0..4).
  * d_x must hold max(Ms) rows of K bf16, d_y max(Ms) rows of N fp32, and d_ws at least
  * the largest uw_workspace_bytes of the candidate pipelines (smaller workspaces drop
  * the pipelines that do not fit). Blocks until the measurements finish.
@@ -339,7 +361,7 @@ uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h
 typedef struct {
     const uw_header* h;       /* the projection's header (host) */
     const void* d_blob;       /* its blob on the device */
-    const uint8_t* d_direct;  /* its direct plane; required when pipeline == UW_PIPE_DIRECT */
+    const uint8_t* d_direct;  /* its direct plane; required for UW_PIPE_DIRECT and UW_PIPE_EXPAND */
     int32_t pipeline;         /* uw_pipeline */
     int32_t variant;          /* GEMM variant, -1 = default */
 } uw_proj;
@@ -392,7 +414,8 @@ uw_status uw_mlp_stack_forward_ex(const uw_mlp_layer* layers, int n_layers, int6
  * for some projection and always need preprocessing). The coordinates are (class, role)
  * for role gate, up, down of each class present, and, with a decode stream and at least 3
  * slots, the decode order. Each pass tries every other pipeline (in pipeline_mask; direct
- * palette only where every layer of the class has that projection's direct plane) for one
+ * palette and expand only where every layer of the class has that projection's direct
+ * plane) for one
  * coordinate at a time, applied to all layers of the class with the default GEMM variant,
  * times the whole forward (warmup untimed runs, then the median of reps, HIP events on
  * `stream`) and keeps a change only if it is at least 1% faster; passes repeat, gate, up,
@@ -417,7 +440,7 @@ typedef struct {
     size_t ws_bytes;
     void* decode_stream;
     uw_stack_opts opts;
-    uint32_t pipeline_mask; /* 0 = all four */
+    uint32_t pipeline_mask; /* 0 = all five */
     int32_t reps;           /* 0 = 5 */
     int32_t warmup;         /* 0 = 1 */
     int32_t max_passes;     /* 0 = 4 */

@@ -81,6 +81,12 @@ def _check_decoders(m: Mat, what: str):
     dref = oracle.direct_plane(m.w)
     assert out.numel() == dref.size, f"{what}: direct plane size"
     assert err == 0 and (host(out) == dref).all(), f"{what}: direct plane differs"
+    # the direct plane expanded back to bf16 is the original matrix, bit for bit
+    wx = empty_u16(m.N * m.K)
+    wx.fill_(0x5A5A)  # every weight must be written
+    uw.expand_direct(m.h, out, wx)
+    _sync()
+    assert (host(wx, np.uint16).reshape(m.N, m.K) == m.w).all(), f"{what}: expanded direct plane differs"
 
 
 def test_decoders_tiny_library_and_oracle_blobs():
@@ -284,7 +290,7 @@ def test_pipelines_tiny():
     for M in (4, 1, 64, 200):
         x = synth.gen_x(cfg, M, m.K)
         y_ref, a_ref = oracle.gemm(x, w)
-        for p in range(4):
+        for p in range(5):
             log(f"  pipeline {p} M={M}")
             y = empty_f32(M, m.N)
             err = zeros_u32()
@@ -305,6 +311,14 @@ def test_run_pipeline_error_paths():
     with pytest.raises(uw.UwError) as e:
         uw.run_pipeline(uw.PIPE_DIRECT, m.h, m.d_blob, x, y, 4)
     assert e.value.status == uw.EINVAL
+    ws = empty_u8(uw.workspace_bytes(m.h, uw.PIPE_EXPAND))
+    with pytest.raises(uw.UwError) as e:  # expand without the direct plane
+        uw.run_pipeline(uw.PIPE_EXPAND, m.h, m.d_blob, x, y, 4, d_ws=ws, ws_bytes=ws.numel())
+    assert e.value.status == uw.EINVAL
+    with pytest.raises(uw.UwError) as e:  # expand into a workspace too small
+        uw.run_pipeline(uw.PIPE_EXPAND, m.h, m.d_blob, x, y, 4, d_direct=m.decode("direct")[0], d_ws=ws,
+                        ws_bytes=ws.numel() - 16)
+    assert e.value.status == uw.ENOSPACE
     with pytest.raises(uw.UwError) as e:
         uw.recon_gemm(m.h, m.d_blob, uw.W_IDX, empty_u8(m.N * m.K // 2), x, y, 4, ldx=m.K - 8)
     assert e.value.status == uw.EINVAL
@@ -402,9 +416,9 @@ def test_autotune_picks_the_fastest_and_the_choice_is_correct():
     plans = uw.autotune(m.h, m.d_blob, d_x, y, Ms, d_direct=direct, d_ws=ws, ws_bytes=ws.numel(), reps=15, warmup=3)
     log(f"  plans {plans}")
     for M, plan in zip(Ms, plans):
-        assert 0 <= plan.pipeline <= 3 and plan.t_ms > 0
+        assert 0 <= plan.pipeline <= 4 and plan.t_ms > 0
         per = []
-        for p in range(4):
+        for p in range(5):
             per.append(uw.autotune(m.h, m.d_blob, d_x, y, [M], d_direct=direct, d_ws=ws, ws_bytes=ws.numel(), reps=15,
                                    warmup=3, pipeline_mask=1 << p)[0].t_ms)
         # kernels here run ~10 us, so separate measurements differ by a few us of launch noise
@@ -464,14 +478,14 @@ def test_mlp_stack_forward_one_and_two_streams():
     K, F, M = 256, 512, 5
     x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
     pipes = [(uw.PIPE_FULL, uw.PIPE_FULL, uw.PIPE_EXP), (uw.PIPE_DIRECT, uw.PIPE_TRANSCODE, uw.PIPE_DIRECT),
-             (uw.PIPE_EXP, uw.PIPE_DIRECT, uw.PIPE_FULL)]
+             (uw.PIPE_EXP, uw.PIPE_DIRECT, uw.PIPE_FULL), (uw.PIPE_EXPAND, uw.PIPE_DIRECT, uw.PIPE_EXPAND)]
     mats, keep, layers = [], [], []
     for l, pp in enumerate(pipes):
         trip = []
         for q, (n, k) in enumerate(((F, K), (F, K), (K, F))):
             w = synth.f32_to_bf16_bits(rng.standard_normal((n, k), dtype=np.float32) * 0.05)
             m = Mat(w, 256)
-            d = m.decode("direct")[0] if pp[q] == uw.PIPE_DIRECT else None
+            d = m.decode("direct")[0] if pp[q] in (uw.PIPE_DIRECT, uw.PIPE_EXPAND) else None
             keep.append((m, d))
             trip.append(uw.proj(m.h, m.d_blob, pp[q], d_direct=d))
         mats.append([t[0] for t in keep[-3:]])

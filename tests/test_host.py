@@ -179,7 +179,7 @@ def test_workspace_bytes_follow_the_pipelines():
     h = uw.inspect(uw.encode(w))
     n = w.size
     # preprocessing output per weight: 2 (full), 1 (exponent-only), 0.5 (transcode), 0 (direct)
-    assert [uw.workspace_bytes(h, p) for p in range(4)] == [2 * n, n, n // 2, 0]
+    assert [uw.workspace_bytes(h, p) for p in range(5)] == [2 * n, n, n // 2, 0, 2 * n]
     with pytest.raises(uw.UwError):
         uw.workspace_bytes(h, 7)
 
