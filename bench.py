@@ -302,7 +302,7 @@ def main():
                     "uncompressed_GBs": round(2 * N * K / (us * 1e-6) / 1e9, 1),
                     "hbm_frac_compressed": round(algorithmic_bytes(h, M, p) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         detail["pipelines"] = pip
-        detail["decoders"] = decoder_detail(uw, torch, h, blobs, stream, log)
+        detail["decoders"] = decoder_detail(uw, torch, h, blobs, stream, log, planes=idxs)
         large_m = large_m_line(uw, synth, torch, dev, stream, log)
 
     cpu = None
@@ -338,9 +338,10 @@ def main():
     print(json.dumps(out))
 
 
-def decoder_detail(uw, torch, h, blobs, stream, log):
-    """Each decoder alone on rotated copies of the gate blob: median time, the bytes it must
-    move, and the fraction of the HBM roof that rate is."""
+def decoder_detail(uw, torch, h, blobs, stream, log, planes=None):
+    """Each decoder alone on rotated copies of the gate blob (and the expand kernel on rotated
+    copies of its direct plane): median time, the bytes it must move, and the fraction of the
+    HBM roof that rate is."""
     N, K = h.N, h.K
     outs = {"full": torch.empty(2 * N * K, dtype=torch.uint8, device=blobs[0].device),
             "exp": torch.empty(N * K, dtype=torch.uint8, device=blobs[0].device),
@@ -350,15 +351,21 @@ def decoder_detail(uw, torch, h, blobs, stream, log):
            "exp": lambda b, o: uw.decode_exponent(h, b, o, stream=stream),
            "idx": lambda b, o: uw.transcode_palette(h, b, o, stream=stream),
            "direct": lambda b, o: uw.prepare_direct(h, b, o, stream=stream)}
+    srcs = {mode: blobs for mode in fns}
+    if planes:
+        outs["expand"] = outs["full"]
+        fns["expand"] = lambda p, o: uw.expand_direct(h, p, o, stream=stream)
+        srcs["expand"] = planes
     res = {}
-    R = len(blobs)
     for mode, fn in fns.items():
-        fn(blobs[0], outs[mode])
+        src = srcs[mode]
+        R = len(src)
+        fn(src[0], outs[mode])
         ts = []
         for r in range(3 * R):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            fn(blobs[r % R], outs[mode])
+            fn(src[r % R], outs[mode])
             b.record(stream)
             ts.append((a, b))
         torch.cuda.synchronize()
