@@ -281,6 +281,34 @@ def test_gemm_parity_ragged(N, K):
                 check_gemm(_run_gemm(m, planes, src, x, v), y_ref, a_ref, f"N={N} K={K} M={M} src={src} v={v}")
 
 
+def test_gemm_padded_leading_dimensions():
+    """X and Y as rows of wider buffers (ldx > K, ldy > N): every loader and variant reads
+    only the first K of each X row (the rest holds NaN, which would poison any output it
+    reached), writes only the first N of each Y row (the rest keeps its sentinel) and
+    matches the oracle there."""
+    cfg = synth.Config("pad", 9, (("w", 200, 320),), 0.02, "normal", 0.001, 0.0, 12, (1,))
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w, 256)
+    planes = _planes(m)
+    ldx, ldy = m.K + 72, m.N + 12
+    for M in (1, 17, 64, 130):
+        x = synth.gen_x(cfg, M, m.K)
+        xp = np.full((M, ldx), 0x7FC0, np.uint16)
+        xp[:, : m.K] = x
+        d_x = dev(xp)
+        y_ref, a_ref = oracle.gemm(x, w)
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX, uw.W_DIRECT):
+            for v in _variants_for(m, M, src):
+                log(f"  padded M={M} src={src} variant={v}")
+                y = empty_f32(M, ldy)
+                y.fill_(12345.0)
+                uw.recon_gemm(m.h, m.d_blob, src, planes[src], d_x, y, M, ldx=ldx, ldy=ldy, variant=v)
+                _sync()
+                yh = host(y).reshape(M, ldy)
+                check_gemm(yh[:, : m.N], y_ref, a_ref, f"padded M={M} src={src} v={v}")
+                assert (yh[:, m.N:] == 12345.0).all(), f"padded M={M} src={src} v={v}: wrote past N"
+
+
 def test_pipelines_tiny():
     cfg = synth.CONFIGS["tiny"]
     w = synth.gen_weight(cfg, "w")
