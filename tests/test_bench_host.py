@@ -38,6 +38,10 @@ def test_byte_accounting_matches_the_library_sizes():
     full = bench.algorithmic_bytes(h, M, 0)
     assert full == bench.decode_bytes(h, "full") + 2 * N * K + 2 * M * K + 4 * M * N
     assert bench.decode_bytes(h, "full") - bench.decode_bytes(h, "exp") == N * K + N * K  # sm in, 2 vs 1 B out
+    # expand: reads the direct plane, writes bf16 W, then the plain GEMM reads it
+    assert bench.decode_bytes(h, "expand") == uw.direct_plane_bytes(h) + 2 * N * K
+    assert bench.algorithmic_bytes(h, M, 4) == bench.decode_bytes(h, "expand") + 2 * N * K + 2 * M * K + 4 * M * N
+    assert uw.workspace_bytes(h, uw.PIPE_EXPAND) == 2 * N * K
 
 
 def test_measured_traffic_needs_the_profiled_sources(tmp_path, monkeypatch):
