@@ -253,7 +253,10 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
  * full-decode pipeline, which hands the rebuilt weights to the vendor's standard matrix
  * multiply: "Four ways to use compressed weights"); it calls hipBLASLt with fp32
  * accumulation and fp32 output and returns UW_EUNSUPPORTED if that library offers no
- * algorithm for the problem (uw_autotune then skips it). */
+ * algorithm for the problem (uw_autotune then skips it). Its first call on a device, and
+ * its first call for each (M, N, K, ldx, ldy), set up hipBLASLt state on the host (a
+ * handle, descriptors, a heuristic query); make those calls outside stream capture, e.g.
+ * during uw_autotune or a warmup forward. */
 int uw_variant_count(void);
 const char* uw_variant_name(int variant);
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
