@@ -10,8 +10,9 @@
 //
 // Per device, one hipBLASLt handle is created on first use (hipBLASLt allocates its own
 // internal resources then). Per (device, M, N, K, ldx, ldy) the descriptors and the
-// heuristic's first algorithm that needs no workspace are built once and kept; the
-// library call itself takes no lock.
+// heuristic's first algorithm that needs no workspace are built once and kept for the life
+// of the process (one small entry per distinct problem). One mutex covers the cache and the
+// enqueue, so threads may share a device's handle; the enqueue is a short host call.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -35,7 +36,7 @@ using PlanKey = std::tuple<int, int64_t, int64_t, int64_t, int64_t, int64_t>;
 
 std::mutex g_mu;
 hipblasLtHandle_t g_handle[64] = {};
-std::map<PlanKey, VendorPlan> g_plans;  // nodes never move: a found plan stays valid
+std::map<PlanKey, VendorPlan> g_plans;
 
 // Build the plan of one problem; false (with the plan's resources released) when hipBLASLt
 // offers no algorithm for it.
@@ -82,28 +83,24 @@ hipError_t vendor_gemm_bf16(const uint16_t* w, const uint16_t* x, float* y, int6
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    const VendorPlan* plan = nullptr;
-    hipblasLtHandle_t hd = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
-            g_handle[dev] = nullptr;
-            return hipErrorNotSupported;
-        }
-        hd = g_handle[dev];
-        const PlanKey key{dev, M, N, K, ldx, ldy};
-        auto it = g_plans.find(key);
-        if (it == g_plans.end()) {
-            VendorPlan p;
-            build_plan(hd, M, N, K, ldx, ldy, p);
-            it = g_plans.emplace(key, p).first;  // a failed plan is kept too: asked again, it fails at once
-        }
-        plan = &it->second;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
+        g_handle[dev] = nullptr;
+        return hipErrorNotSupported;
     }
-    if (!plan->ok) return hipErrorNotSupported;
+    const hipblasLtHandle_t hd = g_handle[dev];
+    const PlanKey key{dev, M, N, K, ldx, ldy};
+    auto it = g_plans.find(key);
+    if (it == g_plans.end()) {
+        VendorPlan p;
+        build_plan(hd, M, N, K, ldx, ldy, p);
+        it = g_plans.emplace(key, p).first;  // a failed plan is kept too: asked again, it fails at once
+    }
+    const VendorPlan& plan = it->second;
+    if (!plan.ok) return hipErrorNotSupported;
     const float alpha = 1.0f, beta = 0.0f;
-    const hipblasStatus_t st = hipblasLtMatmul(hd, plan->op, &alpha, w, plan->a, x, plan->b, &beta, y, plan->d, y, plan->d,
-                                               &plan->algo, nullptr, 0, s);
+    const hipblasStatus_t st = hipblasLtMatmul(hd, plan.op, &alpha, w, plan.a, x, plan.b, &beta, y, plan.d, y, plan.d,
+                                               &plan.algo, nullptr, 0, s);
     return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
 }
 
