@@ -59,7 +59,7 @@ struct GemmArgs {
     const uint8_t* dmeta;  // direct plane: per (tile, group) raw mask and side-table base
     const uint8_t* dside;  // direct plane: raw exponents, 64 bytes per raw (row, group)
     uint32_t tiles;        // direct plane: ceil(N / 16)
-    uint32_t kgroups;      // tiled / wide kernels: 64-groups per K slice (blockIdx.y); 0 = all
+    uint32_t kgroups;      // K split: 64-groups per K slice (blockIdx.y), partial sums added into a zeroed Y; 0 = all
 };
 
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c)
@@ -303,7 +303,11 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     const int r = lane & 15, g = lane >> 4;
     const int64_t nb = static_cast<int64_t>(blockIdx.x) * (16 * RT);
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
-    const uint32_t T = G > static_cast<uint32_t>(wave) ? (G - wave + NW - 1) / NW : 0;  // groups of this wave
+    // K slice of this block (blockIdx.y; all of K unless the launch splits K): groups [j0, j0 + Gs)
+    const uint32_t kgs = a.kgroups ? a.kgroups : G;
+    const uint32_t j0 = blockIdx.y * kgs;
+    const uint32_t Gs = (j0 + kgs < G ? j0 + kgs : G) - j0;
+    const uint32_t T = Gs > static_cast<uint32_t>(wave) ? (Gs - wave + NW - 1) / NW : 0;  // groups of this wave
 
     floatx4 acc[RT][CT];
 #pragma unroll
@@ -425,7 +429,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     // raw exponents of group t + U/2, multiply, then refill the X pieces
     auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        const uint32_t j = wave + NW * t;
+        const uint32_t j = j0 + wave + NW * t;
         u32x4 XF[XT ? CT : 1][2];  // XT: this step's X fragments, back from the LDS tile
         if (XT) {
 #pragma unroll
@@ -489,7 +493,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     // flight, once per ring turn.
     if (T > 0) {
         const auto jc = [&](int k) __attribute__((always_inline)) {
-            return wave + NW * (static_cast<uint32_t>(k) < T ? static_cast<uint32_t>(k) : T - 1);
+            return j0 + wave + NW * (static_cast<uint32_t>(k) < T ? static_cast<uint32_t>(k) : T - 1);
         };
         [&]<int... us>(std::integer_sequence<int, us...>) {
             if constexpr (XNEAR) {
@@ -553,6 +557,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                 while (bits) {
                     const uint32_t j = 32 * wd + __builtin_ctz(bits);
                     bits &= bits - 1;
+                    if (j < j0 || j >= j0 + Gs) {  // another K slice's group
+                        ri++;
+                        continue;
+                    }
                     u32x4 t0v = {0, 0, 0, 0}, t1v = t0v, u0v = t0v, u1v = t0v;
                     if (r == (li & 15)) raw_pieces<SRC>(a, row, j, ri, g, t0v, t1v, u0v, u1v);
                     ri++;
@@ -605,7 +613,10 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 {
     extern __shared__ float red[];
     skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>(a, red, [&](int, int64_t n, int64_t m, float v) {
-        a.y[m * a.ldy + n] = v;
+        if (a.kgroups)
+            atomicAdd(a.y + m * a.ldy + n, v);  // K split: Y was zeroed, every slice adds its part
+        else
+            a.y[m * a.ldy + n] = v;
     });
 }
 
@@ -1175,6 +1186,7 @@ struct Variant {
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
     int xt;     // skinny: X read as whole row segments and put in operand order through LDS
+    int ks;     // skinny: K cut into slices so that row blocks x slices fill the CUs (fp32 atomics into Y)
 };
 
 const Variant kVariants[] = {
@@ -1187,6 +1199,7 @@ const Variant kVariants[] = {
     {"skinny rt4 u2 w4 x1", 0, 4, 4, 2, 0, 0, 1}, {"skinny rt2 u4 w8 x1", 0, 2, 8, 4, 0, 0, 1},
     {"skinny rt4 u2 w4 xt", 0, 4, 4, 2, 0, 0, 0, 1}, {"skinny rt4 u4 w4 xt", 0, 4, 4, 4, 0, 0, 0, 1},
     {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1}, {"vendor hipblaslt", 3, 0, 0, 0, 0, 0},
+    {"skinny rt4 u2 w4 ks", 0, 4, 4, 2, 0, 0, 0, 0, 1}, {"skinny rt4 u2 w4 xt ks", 0, 4, 4, 2, 0, 0, 0, 1, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1207,7 +1220,9 @@ hipError_t allow_lds(const void* fn, size_t bytes, uint64_t& done)
 template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
 hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
-    const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)));
+    const uint32_t G = static_cast<uint32_t>(g.K / 64);
+    const uint32_t ks = g.kgroups ? (G + g.kgroups - 1) / g.kgroups : 1;
+    const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)), ks);
     constexpr size_t lds = skinny_lds<CT, RT, NW, XT>();
     static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), lds, attr_done);
@@ -1302,6 +1317,19 @@ hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
+// K slices of a skinny "ks" launch: as many as it takes for row blocks x slices to fill the
+// CUs, each slice at least 8 groups (1 = no split).
+uint32_t skinny_slices(int64_t N, int64_t K, int rt)
+{
+    const uint32_t G = static_cast<uint32_t>(K / 64);
+    const uint32_t blocks = static_cast<uint32_t>((N + 16 * rt - 1) / (16 * rt));
+    uint32_t ks = cu_count() / (blocks ? blocks : 1);
+    const uint32_t most = G / 8 ? G / 8 : 1;
+    ks = ks < 1 ? 1 : ks > most ? most : ks;
+    const uint32_t kg = (G + ks - 1) / ks;
+    return (G + kg - 1) / kg;
+}
+
 template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
@@ -1310,6 +1338,16 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
         return vendor_gemm_bf16(static_cast<const uint16_t*>(g.wplane), g.x, g.y, g.M, g.N, g.K, g.ldx, g.ldy, s);
     }
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
+    if (v.kind == 0 && v.ks) {
+        // Y is zeroed first and every slice adds its part with fp32 atomics
+        const uint32_t G = static_cast<uint32_t>(g.K / 64);
+        const uint32_t ks = skinny_slices(g.N, g.K, v.rt);
+        GemmArgs g2 = g;
+        g2.kgroups = ks > 1 ? (G + ks - 1) / ks : 0;
+        if (g2.kgroups) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
+        if (v.xt) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, true>(g2, s);
+        return launch_skinny_rt<SRC, CONTIG, 4, 2, 4>(g2, s);
+    }
     if (v.kind == 0) {
         if (v.rt == 1 && v.u == 8) return launch_skinny_rt<SRC, CONTIG, 1, 8, 4>(g, s);
         if (v.rt == 1 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 1, 4, 8>(g, s);
@@ -1359,6 +1397,8 @@ hipError_t launch_gate_up_rt(const GateUpArgs& ga, hipStream_t s)
 hipError_t launch_gate_up(const GateUpArgs& ga, const Variant& v, hipStream_t s)
 {
     if (v.kind != 0) return hipErrorNotSupported;
+    // a "ks" variant that cuts nothing on this shape is its unsplit neighbour, which has a fused form
+    if (v.ks && skinny_slices(ga.gate.N, ga.gate.K, v.rt) > 1) return hipErrorNotSupported;
     if (v.xt && v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4, false, true>(ga, s);
     if (v.xt || v.xnear) return hipErrorNotSupported;
     if (v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4>(ga, s);

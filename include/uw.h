@@ -205,10 +205,11 @@ uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out);
  * groups. Weights are rebuilt in registers / LDS and fed to bf16 MFMA; they are never
  * written to memory. Accumulation is fp32; Y is overwritten (not accumulated into).
  * When a problem has too few output tiles to fill the GPU (long K, small N*M), the
- * 128x128 and 256x256 variants cut K into slices: Y is zeroed on the stream, then each
- * slice adds its partial sums into Y with fp32 atomics. With three or more slices the
- * order of those additions is not fixed, so Y may differ in the last bits from run to
- * run (always within the same error bound); one or two slices give identical results.
+ * 128x128 and 256x256 variants and the skinny variants named "... ks" cut K into slices:
+ * Y is zeroed on the stream, then each slice adds its partial sums into Y with fp32
+ * atomics. With three or more slices the order of those additions is not fixed, so Y may
+ * differ in the last bits from run to run (always within the same error bound); one or
+ * two slices give identical results. The default variant (-1) never picks a "ks" variant.
  */
 typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2, UW_W_DIRECT = 3 } uw_wsrc;
 
