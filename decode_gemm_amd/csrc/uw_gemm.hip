@@ -1599,10 +1599,11 @@ const char* uw_variant_name(int variant)
 
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src)
 {
-    (void)N;
     if (variant < 0 || variant >= uw::kNumVariants || K % 64 || K < 64) return 0;
     const uw::Variant& v = uw::kVariants[variant];
     if (v.kind == 3) return M >= 1 && src == UW_W_BF16;
+    // a "ks" variant exists only where it cuts K (elsewhere it would be its unsplit neighbour)
+    if (v.kind == 0 && v.ks && uw::skinny_slices(N, K, v.rt) < 2) return 0;
     if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }

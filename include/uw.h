@@ -209,7 +209,8 @@ uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out);
  * Y is zeroed on the stream, then each slice adds its partial sums into Y with fp32
  * atomics. With three or more slices the order of those additions is not fixed, so Y may
  * differ in the last bits from run to run (always within the same error bound); one or
- * two slices give identical results. The default variant (-1) never picks a "ks" variant.
+ * two slices give identical results. The default variant (-1) never picks a "ks" variant,
+ * and uw_variant_supports reports one only for shapes it actually splits.
  */
 typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2, UW_W_DIRECT = 3 } uw_wsrc;
 
