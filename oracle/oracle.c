@@ -543,93 +543,3 @@ void or_swiglu(const float* g, const float* u, int64_t n, uint16_t* h)
 }
 
 uint16_t or_f64_to_bf16(double x) { return f64_to_bf16(x); }
-
-/* ---- direct-palette plane: the load-time form the direct pipeline's matmul reads
- * ("Four ways to use compressed weights": transcoded once at model load into a compact
- * 4-bit palette form). With T = ceil(N/16) row tiles and G = K/64 groups:
- *   blocks  T*G blocks of 1536 bytes, block (t, j) at 1536*(t*G + j). For lane
- *           l = 16*g + r (g = 0..3, r = 0..15), i.e. row 16t+r, weights 64j+16g .. +15:
- *             bytes 16l .. 16l+15       weight x: (mantissa_x << 1) | sign of weight x^1
- *             bytes 1024+8l .. +7       two index dwords, one per 8-weight unit (weights
- *                                       16g..16g+7, then 16g+8..16g+15); in each, byte b
- *                                       holds unit weight b (low nibble) and b+4 (high)
- *           The index is the position of the weight's exponent in the palette sorted by
- *           value (ascending); in a raw group it is 0 (the sign/mantissa bytes are kept).
- *           Rows >= N are zero.
- *   meta    at 1536*T*G: T*G entries of two u32: bit r of the first = group j of row
- *           16t+r is raw; the second = index in the side table of the first raw row of
- *           (t, j).
- *   side    at the meta end rounded up to 64: one 64-byte entry per raw (row, group): its
- *           exponents, ordered by tile, then group, then row.
- * Total bytes: 1536*T*G + round_up(8*T*G, 64) + 64*n_raw. The palette is the blob's
- * (top-16 by count). */
-uint64_t or_direct_plane_bytes(int64_t N, int64_t K, int64_t n_raw)
-{
-    int64_t T = (N + 15) / 16, G = K / 64;
-    return (uint64_t)(1536 * T * G) + round_up((uint64_t)(8 * T * G), 64) + 64 * (uint64_t)n_raw;
-}
-
-void or_direct_plane(const uint16_t* w, int64_t N, int64_t K, uint8_t* out)
-{
-    int64_t n = N * K;
-    uint8_t* e = (uint8_t*)malloc((size_t)n);
-    or_split(w, n, NULL, e);
-    uint8_t palette[16];
-    int n_pal = or_palette(e, n, palette, NULL);
-    /* value order: rank of each palette exponent among the palette's values */
-    int vo[256];
-    for (int v = 0; v < 256; v++) vo[v] = -1;
-    for (int i = 0; i < n_pal; i++) {
-        int below = 0;
-        for (int k = 0; k < n_pal; k++)
-            if (palette[k] < palette[i]) below++;
-        vo[palette[i]] = below;
-    }
-    int64_t T = (N + 15) / 16, G = K / 64;
-    uint64_t total_raw = 0;
-    for (int64_t i = 0; i < n; i += 64) {
-        int raw = 0;
-        for (int t = 0; t < 64; t++)
-            if (vo[e[i + t]] < 0) raw = 1;
-        total_raw += (uint64_t)raw;
-    }
-    uint64_t bytes = or_direct_plane_bytes(N, K, (int64_t)total_raw);
-    memset(out, 0, (size_t)bytes);
-    uint8_t* meta = out + 1536 * T * G;
-    uint8_t* side = out + 1536 * T * G + round_up((uint64_t)(8 * T * G), 64);
-    uint32_t next_side = 0;
-    for (int64_t t = 0; t < T; t++) {
-        for (int64_t j = 0; j < G; j++) {
-            uint8_t* blk = out + 1536 * (t * G + j);
-            uint32_t mask = 0, base = next_side;
-            for (int r = 0; r < 16; r++) {
-                int64_t row = 16 * t + r;
-                if (row >= N) continue;
-                const uint16_t* gw = w + row * K + j * 64;
-                const uint8_t* ge = e + row * K + j * 64;
-                int raw = 0;
-                for (int x = 0; x < 64; x++)
-                    if (vo[ge[x]] < 0) raw = 1;
-                if (raw) {
-                    mask |= 1u << r;
-                    memcpy(side + 64 * (uint64_t)next_side, ge, 64);
-                    next_side++;
-                }
-                for (int x = 0; x < 64; x++) {
-                    int g = x / 16, l = 16 * g + r, xl = x % 16;
-                    uint8_t mant = (uint8_t)(gw[x] & 0x7F);
-                    uint8_t partner_sign = (uint8_t)(gw[x ^ 1] >> 15);
-                    blk[16 * l + xl] = (uint8_t)((mant << 1) | partner_sign);
-                    if (!raw) {
-                        int unit = xl / 8, b = xl % 8;
-                        int byte = 1024 + 8 * l + 4 * unit + (b % 4);
-                        blk[byte] |= (uint8_t)(vo[ge[x]] << (b < 4 ? 0 : 4));
-                    }
-                }
-            }
-            memcpy(meta + 8 * (t * G + j), &mask, 4);
-            memcpy(meta + 8 * (t * G + j) + 4, &base, 4);
-        }
-    }
-    free(e);
-}
