@@ -1,21 +1,29 @@
-"""Benchmark: decode + GEMM throughput of the exponent-compressed gate projection on one
-MI355X, as uncompressed-equivalent weight GB/s (2 * N * K bytes per forward / time).
+"""Benchmark: the exponent-compressed, Llama-3.1-8B-shaped MLP stack on one MI355X.
 
-Workload (the small-batch, decode-bound case): a Llama-3.1-8B gate_proj-shaped matrix,
-W 14336 x 4096 bf16 ~ N(0, 0.02) with 0.01% of entries pushed by 2^+-10, synthetic and
-seeded; X M x 4096 bf16 ~ N(0, 1). One step = one forward of the matrix for each batch
-size M in {1, 16, 64}, each through the pipeline the autotuner picked for that M
-(full decode + GEMM, exponent-only, palette transcode or direct palette), with the
-weights' compressed planes rotated over enough copies that the 256 MB Infinity Cache
-cannot serve them. Inputs are resident in HBM when the timed region starts.
+Workload: 32 SwiGLU MLP layers of Llama-3.1-8B's shape -- gate and up 14336 x 4096, down
+4096 x 14336, bf16 weights ~ N(0, sigma_l) with sigma_l = 0.02 * U(0.8, 1.2) per layer,
+synthetic and seeded -- every projection held exponent-compressed on the GPU and run
+through the plan the autotuner measured for its shape and batch size (pipeline, GEMM
+variant, K split). Every layer reads the same X (M x 4096 bf16 ~ N(0, 1)).
+
+One step = one forward of the whole stack (per layer: gate, up, SwiGLU, down) for each
+batch size M in {1, 16, 64}: the small-batch regime, bound by the weight bytes read from
+HBM. value = the uncompressed-equivalent weight bytes of those three forwards (3 x 96
+matrices x 2 N K bytes) per second of the step. Inputs are resident in HBM when the
+timed region starts; the timed region is `steps` steps launched back to back between two
+HIP events on the launch stream.
 
 The JSON line also carries:
-  roofline      the dominant kernel's algorithmic HBM bytes per launch / its mean
-                duration (HIP events on its stream, inside the timed region) vs 8 TB/s
-  cpu_baseline  the CPU oracle (bit-serial decode + fp64 GEMM) timed on one host core
-                on one full step of the same workload
-  detail        per-M plans and the time of each of the four pipelines
-  large_m       TFLOP/s of the down_proj-shaped (4096 x 14336) GEMM at M = 4096
+  roofline      the step's dominant kernel (the largest share of the step): algorithmic
+                HBM bytes per launch / its mean launch duration (HIP events around back-
+                to-back launches over the 32 layers, on the launch stream) vs 8 TB/s, and
+                the read rate of a plain streaming kernel over the same planes
+  large_m       the same stack forward at M = 1024 and 4096 (MFMA-bound): TFLOP/s and
+                the fraction of the 2.5 PFLOP/s bf16 peak, and each projection's GEMM alone
+  cpu_baseline  the CPU oracle (bit-serial decode + fp64 GEMM) on a bounded sample of the
+                same workload, on one thread and on all host cores
+  detail        the plans, and the single-matrix gate-shaped workload (14336 x 4096 with
+                0.01% outliers) through every pipeline, and each decoder alone
 """
 from __future__ import annotations
 
@@ -32,6 +40,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+SMALL_MS = (1, 16, 64)
+LARGE_MS = (1024, 4096)
+ROLES = ("gate", "up", "down")
 # measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by the counters of a copy of known size); used only while the GEMM sources
 # still hash to what was profiled
@@ -64,20 +75,21 @@ def measured_traffic(key):
     return None if k is None else int(k["hbm_bytes_per_launch"])
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--copies", type=int, default=6, help="rotated copies of the compressed weights")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--no-detail", action="store_true", help="skip per-pipeline detail and the large-M line")
+    p.add_argument("--no-detail", action="store_true", help="skip the single-matrix pipelines and decoders")
+    p.add_argument("--no-large", action="store_true", help="skip the M = 1024 / 4096 stack forwards")
+    p.add_argument("--plans", help="read the plans from this JSON file (written by --save-plans) instead of tuning")
+    p.add_argument("--save-plans", help="write the measured plans to this JSON file")
     p.add_argument("--copy-probe", action="store_true", help="also launch a plain 256 MiB copy kernel (counter scale)")
-    p.add_argument("--configs", action="store_true",
-                   help="also sweep the down_proj, 70B-layer and 32-layer-stack workloads (a few minutes more)")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
+# ---------------------------------------------------------------- byte accounting
 def section_bytes(h):
     """Bytes of each section of the Huffman-format blob."""
     N, K = h.N, h.K
@@ -120,6 +132,162 @@ def algorithmic_bytes(h, M, pipeline):
     return decode_bytes(h, mode) + gemm_bytes(h, M, src)
 
 
+def resident_bytes(h, pipeline, blob_bytes):
+    """B_res: the resident bytes of the format a pipeline starts from (the Huffman blob for
+    full / exponent / transcode, the direct plane for direct palette and expand)."""
+    return direct_bytes(h) if pipeline in (3, 4) else blob_bytes
+
+
+def gate_up_bytes(hg, hu, M):
+    """The fused gate/up/SwiGLU launch: both direct planes, X, g and u (fp32), h (bf16)."""
+    return direct_bytes(hg) + direct_bytes(hu) + 2 * M * hg.K + 4 * M * hg.N + 4 * M * hu.N + 2 * M * hg.N
+
+
+# ---------------------------------------------------------------- the stack
+class Stack:
+    """The 32-layer stack on the device: per (layer, role) the header, the blob and the
+    direct plane made from it at load."""
+
+    def __init__(self, uw, synth, torch, dev, log):
+        import concurrent.futures as cf
+
+        self.cfg = cfg = synth.CONFIGS["stack"]
+        self.L = cfg.layers
+        sig = synth.gen_stack_sigmas(cfg)
+        t0 = time.time()
+
+        def make(i):
+            layer, q = divmod(i, 3)
+            return uw.encode(synth.gen_weight(cfg, ROLES[q], layer, sigma=float(sig[layer])))
+
+        self.h = [[None] * 3 for _ in range(self.L)]
+        self.blob = [[None] * 3 for _ in range(self.L)]
+        self.plane = [[None] * 3 for _ in range(self.L)]
+        self.blob_bytes = [[0] * 3 for _ in range(self.L)]
+        workers = max(1, min(16, os.cpu_count() or 8))
+        with cf.ThreadPoolExecutor(workers) as ex:
+            for i, b in enumerate(ex.map(make, range(3 * self.L))):
+                layer, q = divmod(i, 3)
+                h = uw.inspect(b)
+                db = torch.from_numpy(b).to(dev)
+                dp = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+                uw.prepare_direct(h, db, dp)
+                self.h[layer][q], self.blob[layer][q], self.plane[layer][q] = h, db, dp
+                self.blob_bytes[layer][q] = b.size
+        torch.cuda.synchronize()
+        self.Nff, self.K = self.h[0][0].N, self.h[0][0].K
+        self.weight_bytes = sum(2 * h.N * h.K for row in self.h for h in row)
+        self.macs = sum(h.N * h.K for row in self.h for h in row)
+        blob_total = sum(sum(r) for r in self.blob_bytes)
+        plane_total = sum(uw.direct_plane_bytes(h) for row in self.h for h in row)
+        log(f"[bench] stack: {3 * self.L} matrices encoded and prepared in {time.time() - t0:.1f}s; "
+            f"Huffman {blob_total / 1e9:.2f} GB ({blob_total / self.weight_bytes * 2:.3f} B/w), direct planes "
+            f"{plane_total / 1e9:.2f} GB ({plane_total / self.weight_bytes * 2:.3f} B/w), bf16 {self.weight_bytes / 1e9:.2f} GB")
+        self.blob_total, self.plane_total = blob_total, plane_total
+
+    def rot(self, uw, q):
+        return [uw.proj(self.h[l][q], self.blob[l][q], d_direct=self.plane[l][q]) for l in range(self.L)]
+
+    def layers(self, uw, plans_m):
+        """uw_mlp_layer array with gate and up on plans_m['gate'], down on plans_m['down']."""
+        rows = []
+        for l in range(self.L):
+            trip = []
+            for q in range(3):
+                p = plans_m["down" if q == 2 else "gate"]
+                trip.append(uw.proj(self.h[l][q], self.blob[l][q], p["pipeline"], d_direct=self.plane[l][q],
+                                    variant=p["variant"], split_k=p["split_k"]))
+            rows.append(trip)
+        return uw.mlp_layers(rows)
+
+
+def tune_plans(uw, synth, torch, dev, stack, Ms, log):
+    """uw_autotune per (M, role) with the 32 layers of that role as its rotation set, every
+    pipeline, variant and K split; up runs on gate's plan (same shape and statistics)."""
+    plans = {}
+    for M in Ms:
+        plans[M] = {}
+        for role, q in (("gate", 0), ("down", 2)):
+            h0 = stack.h[0][q]
+            x = torch.from_numpy(synth.gen_x(stack.cfg, M, h0.K).view(np.int16)).to(dev)
+            y = torch.empty(M, h0.N, dtype=torch.float32, device=dev)
+            ws = torch.empty(uw.workspace_bytes(h0, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+            reps, trials = (10, 3) if M <= 64 else (3, 2) if M <= 1024 else (2, 2)
+            t0 = time.time()
+            pl = uw.autotune(h0, stack.blob[0][q], x, y, [M], d_ws=ws, ws_bytes=ws.numel(), reps=reps, warmup=1,
+                             trials=trials, rot=stack.rot(uw, q), tune_split=True)[0]
+            plans[M][role] = {"pipeline": pl.pipeline, "variant": pl.variant, "split_k": pl.split_k, "t_ms": pl.t_ms}
+            log(f"[bench] plan M={M} {role}: {uw.PIPELINE_NAMES[pl.pipeline]} / {uw.variant_name(pl.variant)} / "
+                f"split {pl.split_k}: {pl.t_ms * 1e3:.1f} us ({time.time() - t0:.1f}s)")
+            del x, y, ws
+    return plans
+
+
+def plans_to_json(uw, plans):
+    return {str(M): {r: {"pipeline": uw.PIPELINE_NAMES[p["pipeline"]], "variant": uw.variant_name(p["variant"]),
+                         "split_k": p["split_k"], "t_ms": round(float(p["t_ms"]), 5)} for r, p in pm.items()}
+            for M, pm in plans.items()}
+
+
+def plans_from_json(uw, d):
+    names = {uw.variant_name(v): v for v in range(uw.variant_count())}
+    pipes = {v: k for k, v in uw.PIPELINE_NAMES.items()}
+    return {int(M): {r: {"pipeline": pipes[p["pipeline"]], "variant": names[p["variant"]], "split_k": p["split_k"],
+                         "t_ms": p.get("t_ms", 0.0)} for r, p in pm.items()} for M, pm in d.items()}
+
+
+def step_ops(uw, torch, dev, stack, plans_m, M, x, bufs):
+    """The launches one stack forward at M is made of, as callables over a layer index, with
+    their algorithmic bytes: the fused gate/up/SwiGLU launch where the stack uses it (both
+    direct planes, M <= 64, a variant with a fused form, no K split), otherwise gate and up
+    through their pipeline and the SwiGLU; then down."""
+    pg, pd = plans_m["gate"], plans_m["down"]
+    g, u, hbuf, yd, ws = bufs
+    ops = []
+    fused = pg["pipeline"] == uw.PIPE_DIRECT and M <= 64
+    if fused:
+        try:
+            l = 0
+            uw.recon_gemm_gate_up(stack.h[l][0], stack.blob[l][0], stack.plane[l][0], stack.h[l][1], stack.blob[l][1],
+                                  stack.plane[l][1], x, g, u, hbuf, M, variant=pg["variant"], split_k=pg["split_k"])
+        except uw.UwError as e:
+            if e.status != uw.EUNSUPPORTED:
+                raise
+            fused = False
+    if fused:
+        ops.append(("gate_up fused", pg, lambda l: uw.recon_gemm_gate_up(
+            stack.h[l][0], stack.blob[l][0], stack.plane[l][0], stack.h[l][1], stack.blob[l][1], stack.plane[l][1], x,
+            g, u, hbuf, M, variant=pg["variant"], split_k=pg["split_k"]),
+            gate_up_bytes(stack.h[0][0], stack.h[0][1], M)))
+    else:
+        for q, out in ((0, g), (1, u)):
+            ops.append((ROLES[q], pg, (lambda q, out: lambda l: uw.run_pipeline(
+                pg["pipeline"], stack.h[l][q], stack.blob[l][q], x, out, M, d_direct=stack.plane[l][q], d_ws=ws,
+                ws_bytes=ws.numel(), variant=pg["variant"], split_k=pg["split_k"]))(q, out),
+                algorithmic_bytes(stack.h[0][q], M, pg["pipeline"])))
+        ops.append(("swiglu", None, lambda l: uw.swiglu(g, u, hbuf, M * stack.Nff), 10 * M * stack.Nff))
+    ops.append(("down", pd, lambda l: uw.run_pipeline(
+        pd["pipeline"], stack.h[l][2], stack.blob[l][2], hbuf, yd, M, d_direct=stack.plane[l][2], d_ws=ws,
+        ws_bytes=ws.numel(), variant=pd["variant"], split_k=pd["split_k"]),
+        algorithmic_bytes(stack.h[0][2], M, pd["pipeline"])))
+    return ops
+
+
+def time_op(torch, stream, stack, fn, reps):
+    """Mean duration (ms) of fn(layer) launched back to back over the layers, `reps` times
+    round, between two HIP events on the launch stream."""
+    for l in range(stack.L):
+        fn(l)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(reps):
+        for l in range(stack.L):
+            fn(l)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * stack.L)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -134,90 +302,38 @@ def main():
     import decode_gemm_amd as uw
     import synth
 
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    cfg = synth.CONFIGS["gate"]
-    Ms = list(cfg.Ms)
-    t0 = time.time()
-    w = synth.gen_weight(cfg, "gate")
-    blob = uw.encode(w)
-    h = uw.inspect(blob)
-    N, K = h.N, h.K
-    log = lambda *a: print(*a, file=sys.stderr, flush=True)
-    log(f"[bench] gate {N}x{K}: blob {blob.size / 1e6:.1f} MB ({blob.size / (N * K):.3f} B/w), raw groups {h.n_raw}, "
-        f"prep {time.time() - t0:.1f}s")
+    stack = Stack(uw, synth, torch, dev, log)
+    Ms_all = SMALL_MS + (() if args.no_large else LARGE_MS)
+    if args.plans:
+        with open(args.plans) as fh:
+            plans = plans_from_json(uw, json.load(fh)["plans"])
+        log(f"[bench] plans read from {args.plans}")
+    else:
+        plans = tune_plans(uw, synth, torch, dev, stack, Ms_all, log)
+    if args.save_plans:
+        with open(args.save_plans, "w") as fh:
+            json.dump({"format": "uw-stack-plans-1", "workload": "8B-shaped 32-layer SwiGLU MLP stack",
+                       "plans": plans_to_json(uw, plans)}, fh, indent=1)
 
-    # R copies of the blob and of its load-time direct-palette plane
-    R = args.copies
-    d_blob = torch.from_numpy(blob).to(dev)
-    blobs, idxs = [], []
-    for r in range(R):
-        b = d_blob.clone()
-        i = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
-        uw.prepare_direct(h, b, i)
-        blobs.append(b)
-        idxs.append(i)
-    del d_blob
-    xs = {M: torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev) for M in Ms}
-    ys = {M: torch.empty(M, N, dtype=torch.float32, device=dev) for M in Ms}
-    ws_bytes = uw.workspace_bytes(h, uw.PIPE_FULL)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    # plans: uw_autotune per M (single launches, cold caches: the scrub buffer is
-    # overwritten before each rep), then the timed step's own conditions decide between
-    # its pick and every direct-palette variant: launches back to back over the rotated
-    # copies, X resident, as in the timed region
-    tuned = {}
-    for M in Ms:
-        tuned[M] = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=10,
-                               warmup=2, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
-    log("[bench] autotune: " + ", ".join(f"M={M}: {tuned[M]!r} ({uw.variant_name(tuned[M].variant)})" for M in Ms))
-
-    def back_to_back_us(pipeline, variant, M, n):
-        for r in range(R):
-            uw.run_pipeline(pipeline, h, blobs[r], xs[M], ys[M], M, d_direct=idxs[r], d_ws=ws, ws_bytes=ws_bytes,
-                            variant=variant, stream=stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for r in range(n):
-            uw.run_pipeline(pipeline, h, blobs[r % R], xs[M], ys[M], M, d_direct=idxs[r % R], d_ws=ws,
-                            ws_bytes=ws_bytes, variant=variant, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n * 1e3
-
-    plans, choice = {}, {}
-    for M in Ms:
-        cands = [(tuned[M].pipeline, tuned[M].variant)]
-        cands += [(uw.PIPE_DIRECT, v) for v in range(uw.variant_count())
-                  if uw.variant_supports(v, N, K, M, uw.W_DIRECT) and (uw.PIPE_DIRECT, v) != cands[0]]
-        times = {c: back_to_back_us(c[0], c[1], M, 4 * R) for c in cands}
-        best = min(times, key=times.get)
-        plans[M] = uw.Plan(best[0], best[1], times[best] / 1e3, 0)
-        choice[M] = {"autotune": f"{uw.PIPELINE_NAMES[cands[0][0]]} / {uw.variant_name(cands[0][1])}",
-                     "autotune_back_to_back_us": round(times[cands[0]], 2), "candidates": len(cands)}
-    log("[bench] plans: " + ", ".join(f"M={M}: {plans[M]!r} ({uw.variant_name(plans[M].variant)})" for M in Ms))
-
-    seq = [0]
-
-    def launch(M):
-        c = seq[0] % R
-        seq[0] += 1
-        p = plans[M]
-        uw.run_pipeline(p.pipeline, h, blobs[c], xs[M], ys[M], M, d_direct=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
-                        variant=p.variant, stream=stream)
+    # ---- the timed step: one stack forward at each small M
+    Nff, K, L = stack.Nff, stack.K, stack.L
+    arrs = {M: stack.layers(uw, plans[M]) for M in SMALL_MS}
+    xs = {M: torch.from_numpy(synth.gen_x(stack.cfg, M, K).view(np.int16)).to(dev) for M in SMALL_MS}
+    ys = {M: torch.empty(M, K, dtype=torch.float32, device=dev) for M in SMALL_MS}
+    nbs = {M: uw.mlp_stack_workspace(arrs[M], M) for M in SMALL_MS}
+    ws = torch.empty(max(nbs.values()), dtype=torch.uint8, device=dev)
 
     def step():
-        for M in Ms:
-            launch(M)
+        for M in SMALL_MS:
+            uw.mlp_stack_forward(arrs[M], M, xs[M], ys[M], ws, nbs[M], stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: K steps back to back, HIP events on the launch stream at both ends only
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -225,91 +341,81 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    uncompressed = 2.0 * N * K * len(Ms)
-    value = uncompressed / (ms_per_step * 1e-3) / 1e9
-
-    # per-M launch durations: each M's pipeline launched K times back to back (rotated
-    # copies), events at both ends, so no event sits between two launches
-    mean_ms = {}
-    for M in Ms:
+    value = len(SMALL_MS) * stack.weight_bytes / (ms_per_step * 1e-3) / 1e9
+    # each M's forward alone, back to back
+    fwd_ms = {}
+    for M in SMALL_MS:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(args.steps):
-            launch(M)
+        for _ in range(max(3, args.steps // 2)):
+            uw.mlp_stack_forward(arrs[M], M, xs[M], ys[M], ws, nbs[M], stream=stream)
         b.record(stream)
         torch.cuda.synchronize()
-        mean_ms[M] = a.elapsed_time(b) / args.steps
+        fwd_ms[M] = a.elapsed_time(b) / max(3, args.steps // 2)
+    log(f"[bench] step {ms_per_step:.3f} ms = {value:.0f} GB/s uncompressed-equivalent; forwards (ms): "
+        + ", ".join(f"M={M} {fwd_ms[M]:.3f}" for M in SMALL_MS))
 
-    # dominant kernel: the pipeline launch with the largest share of the step; when the
-    # pipeline is direct palette this is exactly one GEMM kernel launch
-    Mdom = max(Ms, key=lambda M: mean_ms[M])
-    pdom = plans[Mdom]
-    alg = algorithmic_bytes(h, Mdom, pdom.pipeline)
-    achieved = alg / (mean_ms[Mdom] * 1e-3) / 1e9
-    dom_key = f"{uw.PIPELINE_NAMES[pdom.pipeline]} pipeline, {uw.variant_name(pdom.variant)}, M={Mdom}"
+    # ---- the launches of the step, each timed back to back over the layers; the dominant
+    # kernel is the group of launches of one kernel build (same op, plan and 16-column tile
+    # count) with the largest share of the step
+    groups = {}
+    op_rows = {}
+    for M in SMALL_MS:
+        g = torch.empty(M, Nff, dtype=torch.float32, device=dev)
+        u = torch.empty_like(g)
+        hbuf = torch.empty(M * Nff, dtype=torch.int16, device=dev)
+        yd = torch.empty(M, K, dtype=torch.float32, device=dev)
+        wsp = torch.empty(uw.workspace_bytes(stack.h[0][0], uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+        for name, plan, fn, nbytes in step_ops(uw, torch, dev, stack, plans[M], M, xs[M], (g, u, hbuf, yd, wsp)):
+            ms = time_op(torch, stream, stack, fn, max(3, args.steps // 2))
+            pipe = uw.PIPELINE_NAMES[plan["pipeline"]] if plan else "-"
+            var = uw.variant_name(plan["variant"]) if plan else "-"
+            split = plan["split_k"] if plan else 1
+            key = (name, pipe, var, split > 1, (M + 15) // 16)
+            grp = groups.setdefault(key, {"ms": 0.0, "bytes": 0, "launches": 0, "Ms": []})
+            grp["ms"] += ms * L
+            grp["bytes"] += nbytes * L
+            grp["launches"] += L
+            grp["Ms"].append(M)
+            op_rows[f"M={M} {name}"] = {"pipeline": pipe, "variant": var, "split_k": split, "us": round(ms * 1e3, 2),
+                                        "bytes": int(nbytes),
+                                        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del g, u, hbuf, yd, wsp
+    dom = max(groups, key=lambda k: groups[k]["ms"])
+    dg = groups[dom]
+    mean_us = dg["ms"] / dg["launches"] * 1e3
+    achieved = dg["bytes"] / (dg["ms"] * 1e-3) / 1e9
+    dom_key = f"{dom[0]}, {dom[1]}, {dom[2]}{' (K split)' if dom[3] else ''}, M={'/'.join(map(str, dg['Ms']))}"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom_key),
-                "kernel": dom_key,
-                "bytes_per_launch": int(alg), "mean_launch_us": round(mean_ms[Mdom] * 1e3, 2)}
-    # the practical read ceiling beside the published peak: a plain streaming read of the
-    # same rotated planes (uw_stream_read, no other work), back to back like the GEMMs
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom_key), "kernel": dom_key,
+                "bytes_per_launch": int(dg["bytes"] / dg["launches"]), "mean_launch_us": round(mean_us, 2),
+                "launches_per_step": dg["launches"], "share_of_step": round(dg["ms"] / ms_per_step, 4)}
+    # the read rate of a plain streaming kernel over the same planes (no other work)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    pbytes = uw.direct_plane_bytes(h) // 16 * 16
-    for r in range(R):
-        uw.stream_read(idxs[r], sink, pbytes, stream=stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for r in range(4 * R):
-        uw.stream_read(idxs[r % R], sink, pbytes, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    read_us = a.elapsed_time(b) / (4 * R) * 1e3
-    read_gbs = pbytes / (read_us * 1e-6) / 1e9
+    pb = uw.direct_plane_bytes(stack.h[0][0]) // 16 * 16
+    read_ms = time_op(torch, stream, stack, lambda l: uw.stream_read(stack.plane[l][0], sink, pb, stream=stream), 3)
+    read_gbs = pb / (read_ms * 1e-3) / 1e9
     roofline["read_ceiling_GBs"] = round(read_gbs, 1)
     roofline["frac_of_read_ceiling"] = round(achieved / read_gbs, 4)
-    log(f"[bench] plain streaming read of one plane: {read_us:.1f} us = {read_gbs:.0f} GB/s "
-        f"({read_gbs / HBM_PEAK_GBS:.3f} of the peak); dominant kernel at {achieved / read_gbs:.3f} of it")
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s uncompressed-equivalent; per-M us: "
-        + ", ".join(f"{M}: {mean_ms[M] * 1e3:.1f}" for M in Ms))
+    log(f"[bench] dominant: {dom_key}: {mean_us:.2f} us/launch, {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} "
+        f"of 8 TB/s ({achieved / read_gbs:.3f} of the {read_gbs:.0f} GB/s read ceiling); launches: {op_rows}")
 
-    detail = {"plans": {str(M): {"pipeline": uw.PIPELINE_NAMES[plans[M].pipeline], "variant": uw.variant_name(plans[M].variant),
-                                 "us": round(mean_ms[M] * 1e3, 2), "selection": choice[M],
-                                 "hbm_frac_compressed": round(algorithmic_bytes(h, M, plans[M].pipeline) / (mean_ms[M] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-                        for M in Ms},
-              "blob_bytes_per_weight": round(blob.size / (N * K), 4),
-              "direct_plane_bytes_per_weight": round(uw.direct_plane_bytes(h) / (N * K), 4)}
-    large_m = None
+    large = None if args.no_large else large_m(uw, synth, torch, dev, stream, stack, plans, log)
+    detail = {"plans": plans_to_json(uw, plans), "launches": op_rows,
+              "forward_ms": {str(M): round(fwd_ms[M], 4) for M in SMALL_MS},
+              "blob_bytes_per_weight": round(2 * stack.blob_total / stack.weight_bytes, 4),
+              "direct_plane_bytes_per_weight": round(2 * stack.plane_total / stack.weight_bytes, 4)}
+    for M in SMALL_MS:
+        # the forward's HBM fraction on the resident bytes it starts from (every plane it
+        # reads once, X, the final Y) and on everything it moves
+        res = stack.plane_total + 2 * M * K + 4 * M * K
+        detail.setdefault("forward_hbm_frac", {})[str(M)] = round(res / (fwd_ms[M] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if not args.no_detail:
-        # every pipeline at every M (best variant each), cold weights via rotation
-        pip = {}
-        for M in Ms:
-            for p in range(5):
-                pl = uw.autotune(h, blobs[0], xs[M], ys[M], [M], d_direct=idxs[0], d_ws=ws, ws_bytes=ws_bytes, reps=5,
-                                 warmup=1, pipeline_mask=1 << p, d_scrub=scrub, scrub_bytes=scrub.numel())[0]
-                ts = []
-                for r in range(3 * R):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    c = r % R
-                    a.record(stream)
-                    uw.run_pipeline(p, h, blobs[c], xs[M], ys[M], M, d_direct=idxs[c], d_ws=ws, ws_bytes=ws_bytes,
-                                    variant=pl.variant, stream=stream)
-                    b.record(stream)
-                    ts.append((a, b))
-                torch.cuda.synchronize()
-                us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
-                pip[f"M={M} {uw.PIPELINE_NAMES[p]}"] = {
-                    "variant": uw.variant_name(pl.variant), "us": round(us, 2),
-                    "uncompressed_GBs": round(2 * N * K / (us * 1e-6) / 1e9, 1),
-                    "hbm_frac_compressed": round(algorithmic_bytes(h, M, p) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        detail["pipelines"] = pip
-        detail["decoders"] = decoder_detail(uw, torch, h, blobs, stream, log, planes=idxs)
-        large_m = large_m_line(uw, synth, torch, dev, stream, log)
+        del arrs, ws
+        torch.cuda.empty_cache()
+        detail["single_matrix"] = single_matrix_detail(uw, synth, torch, dev, stream, log)
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(synth, cfg, w, Ms, log)
-
-    sweep = configs_sweep(uw, synth, torch, dev, stream, log) if args.configs else None
+    cpu = None if args.no_cpu else cpu_baseline(synth, log)
 
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -325,23 +431,107 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B gate_proj shape, W 14336x4096 bf16 N(0,0.02) + 0.01% 2^+-10 outliers, "
-                               "exponent-compressed; X Mx4096 bf16, M in {1,16,64}; autotuned pipeline per M",
-                   "global_batch": int(sum(Ms)), "seq_len": 1, "parallelism": "single GPU"},
+        "config": {"workload": "Llama-3.1-8B-shaped MLP stack: 32 SwiGLU layers (gate, up 14336x4096; down 4096x14336) "
+                               "bf16 N(0, 0.02*U(0.8,1.2)) exponent-compressed; one step = a stack forward at each "
+                               "M in {1,16,64}; autotuned plan per (M, projection)",
+                   "global_batch": int(sum(SMALL_MS)), "seq_len": 1, "parallelism": "single GPU",
+                   "layers": L, "Ms": list(SMALL_MS)},
         "roofline": roofline,
+        "large_m": large,
         "cpu_baseline": cpu,
         "detail": detail,
-        "large_m": large_m,
     }
-    if sweep is not None:
-        out["configs"] = sweep
     print(json.dumps(out))
 
 
+def large_m(uw, synth, torch, dev, stream, stack, plans, log):
+    """The stack forward at M = 1024 and 4096 on its plans: TFLOP/s (2 M x every matrix's
+    N K per forward) vs the bf16 peak, and each projection's GEMM alone (back to back over
+    the layers)."""
+    res = {"unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS}
+    for M in LARGE_MS:
+        arr = stack.layers(uw, plans[M])
+        x = torch.from_numpy(synth.gen_x(stack.cfg, M, stack.K).view(np.int16)).to(dev)
+        y = torch.empty(M, stack.K, dtype=torch.float32, device=dev)
+        nb = uw.mlp_stack_workspace(arr, M)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        torch.cuda.synchronize()
+        reps = 3 if M <= 1024 else 2
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = 2.0 * M * stack.macs / (ms * 1e-3) / 1e12
+        row = {"forward_ms": round(ms, 3), "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+               "tokens_per_s": round(M / (ms * 1e-3), 1), "plans": plans_to_json(uw, {M: plans[M]})[str(M)]}
+        del ws
+        g = torch.empty(M, stack.Nff, dtype=torch.float32, device=dev)
+        hb = torch.empty(M * stack.Nff, dtype=torch.int16, device=dev)
+        hb.zero_()
+        wsp = torch.empty(uw.workspace_bytes(stack.h[0][0], uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+        for role, q, xin, out, N, Kin in (("gate", 0, x, g, stack.Nff, stack.K), ("down", 2, hb, y, stack.K, stack.Nff)):
+            p = plans[M][role]
+            fn = lambda l: uw.run_pipeline(p["pipeline"], stack.h[l][q], stack.blob[l][q], xin, out, M,
+                                           d_direct=stack.plane[l][q], d_ws=wsp, ws_bytes=wsp.numel(),
+                                           variant=p["variant"], split_k=p["split_k"])
+            oms = time_op(torch, stream, stack, fn, 1)
+            otf = 2.0 * M * N * Kin / (oms * 1e-3) / 1e12
+            row[role] = {"us": round(oms * 1e3, 1), "tflops": round(otf, 1), "mfma_frac": round(otf / BF16_PEAK_TFLOPS, 4)}
+        del g, hb, wsp, x, y
+        torch.cuda.empty_cache()
+        res[str(M)] = row
+        log(f"[bench] stack M={M}: {row}")
+    return res
+
+
+def single_matrix_detail(uw, synth, torch, dev, stream, log, copies=6):
+    """The single-matrix gate-shaped workload (14336 x 4096, 0.01% outliers x 2^+-10) at M in
+    {1, 16, 64}: each pipeline's best plan (rotated copies, back to back), its HBM fraction on
+    the resident bytes it starts from plus X and Y (and on all the bytes it moves), and each
+    decoder alone."""
+    cfg = synth.CONFIGS["gate"]
+    w = synth.gen_weight(cfg, "gate")
+    blob = uw.encode(w)
+    del w
+    h = uw.inspect(blob)
+    N, K = h.N, h.K
+    blobs, planes = [], []
+    for _ in range(copies):
+        b = torch.from_numpy(blob).to(dev)
+        d = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
+        uw.prepare_direct(h, b, d)
+        blobs.append(b)
+        planes.append(d)
+    rot = [uw.proj(h, blobs[r], d_direct=planes[r]) for r in range(copies)]
+    ws = torch.empty(uw.workspace_bytes(h, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
+    pip = {}
+    for M in SMALL_MS:
+        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        for p in range(5):
+            pl = uw.autotune(h, blobs[0], x, y, [M], d_ws=ws, ws_bytes=ws.numel(), reps=12, warmup=2, trials=3, rot=rot,
+                             pipeline_mask=1 << p, tune_split=True)[0]
+            us = pl.t_ms * 1e3
+            res = resident_bytes(h, p, blob.size) + 2 * M * K + 4 * M * N
+            pip[f"M={M} {uw.PIPELINE_NAMES[p]}"] = {
+                "variant": uw.variant_name(pl.variant), "split_k": pl.split_k, "us": round(us, 2),
+                "uncompressed_GBs": round(2 * N * K / (us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(res / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "moved_frac": round(algorithmic_bytes(h, M, p) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] single matrix: {pip}")
+    return {"workload": "gate_proj shape W 14336x4096 bf16 N(0,0.02) + 0.01% 2^+-10 outliers, M in {1,16,64}",
+            "blob_bytes_per_weight": round(blob.size / (N * K), 4),
+            "pipelines": pip, "decoders": decoder_detail(uw, torch, h, blobs, stream, log, planes=planes)}
+
+
 def decoder_detail(uw, torch, h, blobs, stream, log, planes=None):
-    """Each decoder alone on rotated copies of the gate blob (and the expand kernel on rotated
-    copies of its direct plane): median time, the bytes it must move, and the fraction of the
-    HBM roof that rate is."""
+    """Each decoder alone, launched back to back over rotated copies of the blob (the expand
+    kernel over rotated copies of its direct plane): mean time, the bytes it must move, and
+    the fraction of the HBM roof that rate is."""
     N, K = h.N, h.K
     outs = {"full": torch.empty(2 * N * K, dtype=torch.uint8, device=blobs[0].device),
             "exp": torch.empty(N * K, dtype=torch.uint8, device=blobs[0].device),
@@ -360,16 +550,15 @@ def decoder_detail(uw, torch, h, blobs, stream, log, planes=None):
     for mode, fn in fns.items():
         src = srcs[mode]
         R = len(src)
-        fn(src[0], outs[mode])
-        ts = []
-        for r in range(3 * R):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+        for r in range(R):
+            fn(src[r], outs[mode])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(4 * R):
             fn(src[r % R], outs[mode])
-            b.record(stream)
-            ts.append((a, b))
+        b.record(stream)
         torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+        us = a.elapsed_time(b) / (4 * R) * 1e3
         nbytes = decode_bytes(h, mode)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[mode] = {"us": round(us, 2), "bytes": int(nbytes), "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -377,300 +566,104 @@ def decoder_detail(uw, torch, h, blobs, stream, log, planes=None):
     return res
 
 
-def timed(torch, stream, fn, reps=10):
-    """Median of per-launch HIP-event times (ms) of fn(rep)."""
-    ev = []
-    for r in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        fn(r)
-        b.record(stream)
-        ev.append((a, b))
-    torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
-def shape_sweep(uw, synth, torch, dev, stream, log, cfg, proj, Ms, copies=2):
-    """One projection shape: the autotuned plan and each pipeline's best per M, timed over
-    rotated copies of the compressed weights."""
-    w = synth.gen_weight(cfg, proj)
-    blob = uw.encode(w)
-    del w
-    h = uw.inspect(blob)
-    N, K = h.N, h.K
-    blobs, planes = [], []
-    for _ in range(copies):
-        b = torch.from_numpy(blob).to(dev)
-        d = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
-        uw.prepare_direct(h, b, d)
-        blobs.append(b)
-        planes.append(d)
-    ws_bytes = uw.workspace_bytes(h, uw.PIPE_FULL)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    rows = {}
-    for M in Ms:
-        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
-        y = torch.empty(M, N, dtype=torch.float32, device=dev)
-        per = {}
-        for p in range(5):
-            pl = uw.autotune(h, blobs[0], x, y, [M], d_direct=planes[0], d_ws=ws, ws_bytes=ws_bytes, reps=5, warmup=2,
-                             pipeline_mask=1 << p)[0]
-            ms = timed(torch, stream, lambda r: uw.run_pipeline(p, h, blobs[r % copies], x, y, M, d_direct=planes[r % copies],
-                                                                d_ws=ws, ws_bytes=ws_bytes, variant=pl.variant,
-                                                                stream=stream))
-            alg = algorithmic_bytes(h, M, p)
-            per[uw.PIPELINE_NAMES[p]] = {
-                "variant": uw.variant_name(pl.variant), "us": round(ms * 1e3, 2),
-                "uncompressed_GBs": round(2 * N * K / (ms * 1e-3) / 1e9, 1),
-                "hbm_frac_compressed": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
-                "mfma_frac": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        best = min(per, key=lambda k: per[k]["us"])
-        rows[str(M)] = {"best": best, **per}
-        log(f"[bench] {cfg.name}/{proj} {N}x{K} M={M}: best {best} {per[best]}")
-    return {"shape": [N, K], "blob_bytes_per_weight": round(blob.size / (N * K), 4), "by_M": rows}
-
-
-def stack_sweep(uw, synth, torch, dev, stream, log, Ms):
-    """The 32-layer SwiGLU stack through uw_mlp_stack_forward: per M, plans autotuned on
-    layer 0's gate and down shapes, one forward timed with one stream and with a separate
-    decode stream."""
+def cpu_baseline(synth, log):
+    """The CPU oracle as it stands (plain scalar C, one call per matrix) on a bounded sample
+    of the step: projections of the stack at M = 1, 16 and 64, each forward a bit-serial
+    decode of its Huffman blob to bf16 W and an fp64 GEMM. One thread on layer 0's gate and
+    down; then two projections per thread on all host cores (up to 16), started together.
+    The encode is not timed. Also the M = 1024 forward, extrapolated from a 16-row (1/64)
+    sample of X."""
     import concurrent.futures as cf
+    import threading
+
+    import oracle
 
     cfg = synth.CONFIGS["stack"]
     sig = synth.gen_stack_sigmas(cfg)
-    L = cfg.layers
-    t0 = time.time()
 
-    def make(i):
+    def prep(i):
         layer, q = divmod(i, 3)
-        proj = ("gate", "up", "down")[q]
-        return uw.encode(synth.gen_weight(cfg, proj, layer, sigma=float(sig[layer])))
+        w = synth.gen_weight(cfg, ROLES[q], layer, sigma=float(sig[layer]))
+        blob = oracle.encode(w, chunk=256)
+        xs = {M: synth.gen_x(cfg, M, w.shape[1]) for M in SMALL_MS}
+        return blob, xs, w.shape
 
-    with cf.ThreadPoolExecutor(max(1, min(16, (os.cpu_count() or 8)))) as ex:
-        blobs_h = list(ex.map(make, range(3 * L)))
-    hs = [uw.inspect(b) for b in blobs_h]
-    d_blobs, d_planes = [], []
-    for b, h in zip(blobs_h, hs):
-        db = torch.from_numpy(b).to(dev)
-        dp = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
-        uw.prepare_direct(h, db, dp)
-        d_blobs.append(db)
-        d_planes.append(dp)
-    del blobs_h
-    torch.cuda.synchronize()
-    log(f"[bench] stack: {3 * L} matrices encoded and prepared in {time.time() - t0:.1f}s")
-    Nff, K = hs[0].N, hs[0].K
-    weight_bytes = sum(2 * h.N * h.K for h in hs)
-    ws_t = torch.empty(uw.workspace_bytes(hs[0], uw.PIPE_FULL), dtype=torch.uint8, device=dev)
-    side = torch.cuda.Stream()
-    rows = {}
-    for M in Ms:
-        plans = {}
-        for q, Kin, Nout in ((0, K, Nff), (2, Nff, K)):
-            x = torch.from_numpy(synth.gen_x(cfg, M, Kin).view(np.int16)).to(dev)
-            y = torch.empty(M, Nout, dtype=torch.float32, device=dev)
-            plans[q] = uw.autotune(hs[q], d_blobs[q], x, y, [M], d_direct=d_planes[q], d_ws=ws_t, ws_bytes=ws_t.numel(),
-                                   reps=5, warmup=2)[0]
-        layers = []
-        for layer in range(L):
-            trip = []
-            for q in range(3):
-                i = 3 * layer + q
-                pl = plans[0 if q < 2 else 2]
-                trip.append(uw.proj(hs[i], d_blobs[i], pl.pipeline, d_direct=d_planes[i], variant=pl.variant))
-            layers.append(trip)
-        arr = uw.mlp_layers(layers)
-        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
-        y = torch.empty(M, K, dtype=torch.float32, device=dev)
-        row = {"gate_up_plan": f"{uw.PIPELINE_NAMES[plans[0].pipeline]} / {uw.variant_name(plans[0].variant)}",
-               "down_plan": f"{uw.PIPELINE_NAMES[plans[2].pipeline]} / {uw.variant_name(plans[2].variant)}"}
-        for two in (False, True):
-            nb = uw.mlp_stack_workspace(arr, M, two_slots=two)
-            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-            fwd = lambda r: uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream, decode_stream=side if two else None)
-            fwd(0)
-            ms = timed(torch, stream, fwd, reps=3)
-            key = "two_streams" if two else "one_stream"
-            row[key] = {"ms": round(ms, 3), "tokens_per_s": round(M / (ms * 1e-3), 1),
-                        "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
-                        "tflops": round(2.0 * M * weight_bytes / 2 / (ms * 1e-3) / 1e12, 1)}
-            del ws
-        rows[str(M)] = row
-        log(f"[bench] stack M={M}: {row}")
-
-    # decode-first plans (the best of full / exponent / transcode per shape) with the
-    # preprocessing on one stream, on a second stream, and on CU-split stream pairs
-    split = {}
-    for M in (1, 16, 64):
-        plans = {}
-        for q, Kin, Nout in ((0, K, Nff), (2, Nff, K)):
-            xq = torch.from_numpy(synth.gen_x(cfg, M, Kin).view(np.int16)).to(dev)
-            yq = torch.empty(M, Nout, dtype=torch.float32, device=dev)
-            plans[q] = uw.autotune(hs[q], d_blobs[q], xq, yq, [M], d_ws=ws_t, ws_bytes=ws_t.numel(), reps=5,
-                                   warmup=2, pipeline_mask=0b0111)[0]
-        arr = uw.mlp_layers([[uw.proj(hs[3 * l + q], d_blobs[3 * l + q], plans[0 if q < 2 else 2].pipeline,
-                                      variant=plans[0 if q < 2 else 2].variant) for q in range(3)] for l in range(L)])
-        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
-        y = torch.empty(M, K, dtype=torch.float32, device=dev)
-        row = {"gate_up_plan": f"{uw.PIPELINE_NAMES[plans[0].pipeline]} / {uw.variant_name(plans[0].variant)}",
-               "down_plan": f"{uw.PIPELINE_NAMES[plans[2].pipeline]} / {uw.variant_name(plans[2].variant)}"}
-        for mode in ("one_stream", "two_streams", "cu_split_32", "cu_split_64", "cu_split_128"):
-            two = mode != "one_stream"
-            nb = uw.mlp_stack_workspace(arr, M, two_slots=two)
-            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-            pair = uw.stream_pair_create(int(mode.rsplit("_", 1)[1])) if mode.startswith("cu_split") else None
-            main = torch.cuda.ExternalStream(pair[0]) if pair else stream
-            dec = pair[1] if pair else (side if two else None)
-            torch.cuda.synchronize()
-            fwd = lambda r: uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=main, decode_stream=dec)
-            fwd(0)
-            ms = timed(torch, main, fwd, reps=3)
-            torch.cuda.synchronize()
-            if pair:
-                uw.stream_destroy(pair[0])
-                uw.stream_destroy(pair[1])
-            row[mode] = {"ms": round(ms, 3), "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
-            del ws
-        split[str(M)] = row
-        log(f"[bench] stack decode-first M={M}: {row}")
-
-    # hard / easy layers: every 4th layer keeps only its Huffman blobs (no direct planes, so
-    # it always needs preprocessing); the others hold direct planes. Start: direct palette on
-    # the easy layers, full decode on the hard ones; uw_mlp_stack_autotune then tunes the
-    # per-class, per-role pipelines and the decode order end to end (decode stream, 3 slots).
-    hard = {}
-    for M in (1, 16, 64, 256):
-        layers = []
-        for l in range(L):
-            is_hard = l % 4 == 3
-            layers.append([uw.proj(hs[3 * l + q], d_blobs[3 * l + q], uw.PIPE_FULL if is_hard else uw.PIPE_DIRECT,
-                                   d_direct=None if is_hard else d_planes[3 * l + q]) for q in range(3)])
-        arr = uw.mlp_layers(layers)
-        full = uw.mlp_layers([[uw.proj(hs[3 * l + q], d_blobs[3 * l + q], uw.PIPE_FULL) for q in range(3)]
-                              for l in range(L)])
-        nb = uw.mlp_stack_workspace_ex(full, M, slots=3)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
-        y = torch.empty(M, K, dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-        t0 = time.time()
-        a = uw.mlp_stack_autotune(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3, reps=3, warmup=1)
-        torch.cuda.synchronize()
-        tune_s = time.time() - t0
-        plan = {}
-        for cls, l in (("easy", 0), ("hard", 3)):
-            plan[cls] = {r: uw.PIPELINE_NAMES[getattr(arr[l], r).pipeline] for r in ("gate", "up", "down")}
-        fwd = lambda r: uw.mlp_stack_forward_ex(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3,
-                                                down_first=bool(a.opts.down_first))
-        fwd(0)
-        ms = timed(torch, stream, fwd, reps=3)
-        hard[str(M)] = {"hard_layers": L // 4, "plan": plan, "down_first": bool(a.opts.down_first),
-                        "start_ms": round(a.t_start_ms, 3), "tuned_ms": round(ms, 3), "passes": a.passes,
-                        "trials": a.trials, "tune_seconds": round(tune_s, 1),
-                        "uncompressed_GBs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
-        del ws
-        log(f"[bench] stack hard/easy M={M}: {hard[str(M)]}")
-    return {"layers": L, "shapes": {"gate_up": [Nff, K], "down": [K, Nff]}, "by_M": rows, "decode_first": split,
-            "hard_easy_tuned": hard}
-
-
-def configs_sweep(uw, synth, torch, dev, stream, log):
-    """The other workloads: down_proj (M 256..4096), the 70B-shaped layer (gate and down,
-    M 1..2048), the 32-layer stack (M sweep), and PyTorch's bf16 matmul on plain bf16
-    weights of the large-M shapes as a reference point."""
-    out = {}
-    out["down"] = shape_sweep(uw, synth, torch, dev, stream, log, synth.CONFIGS["down"], "down", (256, 1024, 4096))
-    c70 = synth.CONFIGS["70b"]
-    out["70b_gate"] = shape_sweep(uw, synth, torch, dev, stream, log, c70, "gate", c70.Ms)
-    out["70b_down"] = shape_sweep(uw, synth, torch, dev, stream, log, c70, "down", c70.Ms)
-    torch.cuda.empty_cache()
-    out["stack"] = stack_sweep(uw, synth, torch, dev, stream, log, (1, 4, 16, 64, 256, 1024, 4096))
-    ref = {}
-    for (N, K, M) in ((4096, 14336, 4096), (14336, 4096, 4096), (8192, 28672, 2048)):
-        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
-        b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
-        ms = timed(torch, stream, lambda r: torch.matmul(a, b.t()), reps=10)
-        ref[f"M={M} N={N} K={K}"] = {"us": round(ms * 1e3, 1), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
-        del a, b
-    # small M on the gate shape: plain bf16 weights (2 B/w) over 6 rotated copies, launches
-    # back to back between two events, as the headline step is timed
-    ws = [torch.randn(14336, 4096, device=dev, dtype=torch.bfloat16) for _ in range(6)]
-    for M in (1, 16, 64):
-        a = torch.randn(M, 4096, device=dev, dtype=torch.bfloat16)
-        for r in range(6):
-            torch.matmul(a, ws[r].t())
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(48):
-            torch.matmul(a, ws[r % 6].t())
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / 48 * 1e3
-        ref[f"M={M} N=14336 K=4096 (bf16 weights, rotated)"] = {
-            "us": round(us, 2), "weight_GBs": round(2 * 14336 * 4096 / (us * 1e-6) / 1e9, 1)}
-    del ws
-    out["vendor_bf16_matmul_reference"] = ref
-    log(f"[bench] vendor reference: {ref}")
-    return out
-
-
-def large_m_line(uw, synth, torch, dev, stream, log):
-    """TFLOP/s on the down_proj shape at M = 4096 (MFMA-bound) of the direct-palette pipeline,
-    the full-decode pipeline and the expand pipeline (bf16 weights rebuilt in HBM from the
-    Huffman stream or from the direct plane, then the best plain bf16 GEMM: ours or the vendor
-    library's), each with its autotuned variant, vs the 2.5 PFLOP/s bf16 peak."""
-    cfg = synth.CONFIGS["down"]
-    w = synth.gen_weight(cfg, "down")
-    blob = uw.encode(w)
-    h = uw.inspect(blob)
-    N, K, M = h.N, h.K, 4096
-    b = torch.from_numpy(blob).to(dev)
-    idx = torch.empty(uw.direct_plane_bytes(h), dtype=torch.uint8, device=dev)
-    uw.prepare_direct(h, b, idx)
-    x = torch.from_numpy(synth.gen_x(cfg, M, K).view(np.int16)).to(dev)
-    y = torch.empty(M, N, dtype=torch.float32, device=dev)
-    ws = torch.empty(uw.workspace_bytes(h, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
-    res = {}
-    for p in (uw.PIPE_DIRECT, uw.PIPE_FULL, uw.PIPE_EXPAND):
-        pl = uw.autotune(h, b, x, y, [M], d_direct=idx, d_ws=ws, ws_bytes=ws.numel(), reps=5, warmup=2,
-                         pipeline_mask=1 << p)[0]
-        ts = []
-        for _ in range(10):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            uw.run_pipeline(p, h, b, x, y, M, d_direct=idx, d_ws=ws, ws_bytes=ws.numel(), variant=pl.variant, stream=stream)
-            e1.record(stream)
-            ts.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(c) for a, c in ts]))
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        res[uw.PIPELINE_NAMES[p]] = {"variant": uw.variant_name(pl.variant), "ms": round(ms, 4), "tflops": round(tf, 1),
-                                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
-    log(f"[bench] large M: {res}")
-    return {"workload": "down_proj shape W 4096x14336, M=4096", "unit": "TFLOP/s", **res}
-
-
-def cpu_baseline(synth, cfg, w, Ms, log, steps=3):
-    """The CPU oracle on `steps` full steps of the same workload: for each M, bit-serial
-    decode of the Huffman blob to bf16 W, then the fp64 GEMM; single-threaded C (about
-    15 s on the host cores)."""
-    import oracle
-
-    blob = oracle.encode(w, chunk=256)
-    xs = {M: synth.gen_x(cfg, M, w.shape[1]) for M in Ms}
-    t = time.time()
-    for _ in range(steps):
-        for M in Ms:
+    def work(item):
+        blob, xs, _ = item
+        for M in SMALL_MS:
             d = oracle.decode(blob, want=("w",))
             oracle.gemm(xs[M], d["w"])
-    dt = time.time() - t
-    N, K = w.shape
-    v = 2.0 * N * K * len(Ms) * steps / dt / 1e9
-    log(f"[bench] cpu oracle {steps} steps {dt:.1f}s -> {v:.3f} GB/s")
-    return {"value": round(v, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full steps (M in {{{', '.join(map(str, Ms))}}}: decode + fp64 GEMM each), {dt:.1f} s"}
+
+    one = prep(0)
+    N, K = one[2]
+    two = prep(2)
+    t = time.perf_counter()
+    work(one)
+    work(two)
+    t1 = time.perf_counter() - t
+    v1 = 2 * len(SMALL_MS) * 2.0 * N * K / t1 / 1e9
+    # M = 1024: decode once, GEMM on 16 of its 1024 rows, scaled by 64
+    x16 = synth.gen_x(cfg, 1024, K)[:16]
+    t = time.perf_counter()
+    d = oracle.decode(one[0], want=("w",))
+    td = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.gemm(x16, d["w"])
+    tg = time.perf_counter() - t
+    del d
+    t1024 = td + 64 * tg
+    log(f"[bench] cpu oracle, 1 thread: {t1:.1f}s -> {v1:.4f} GB/s; M=1024 extrapolated {t1024:.1f}s")
+    del one, two
+    threads = max(1, min(16, os.cpu_count() or 1))
+    per = 2  # projections per thread
+    with cf.ThreadPoolExecutor(threads) as ex:
+        items = list(ex.map(prep, range(per * threads)))
+    barrier = threading.Barrier(threads)
+    ends = [0.0] * threads
+
+    def run(i):
+        barrier.wait()
+        for k in range(per):
+            work(items[per * i + k])
+        ends[i] = time.perf_counter()
+
+    start = [0.0]
+
+    def run0():
+        barrier.wait()
+        start[0] = time.perf_counter()
+        for k in range(per):
+            work(items[k])
+        ends[0] = time.perf_counter()
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        futs = [ex.submit(run0)] + [ex.submit(run, i) for i in range(1, threads)]
+        for f in futs:
+            f.result()
+    tall = max(ends) - start[0]
+    vall = per * threads * len(SMALL_MS) * 2.0 * N * K / tall / 1e9
+    log(f"[bench] cpu oracle, {threads} threads: {tall:.1f}s -> {vall:.4f} GB/s")
+    return {"value": round(vall, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{per * threads} projections of the stack (layers 0..{(per * threads - 1) // 3}), {per} per "
+                      f"thread, each a forward at M = 1, 16, 64 (bit-serial decode + fp64 GEMM per forward), {tall:.1f} s",
+            "single_thread": {"value": round(v1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"layer 0 gate 14336x4096 and down 4096x14336 at M = 1, 16, 64, {t1:.1f} s"},
+            "large_m_extrapolated": {
+                "tflops": round(2.0 * 1024 * N * K / t1024 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                "sample": f"layer 0 gate at M = 1024: decode {td:.1f} s + fp64 GEMM on 16 of the 1024 rows "
+                          f"{tg:.1f} s x 64 (extrapolated)"}}
 
 
 if __name__ == "__main__":

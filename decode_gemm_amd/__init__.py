@@ -20,8 +20,8 @@ __all__ = [
     "decode_exponent", "transcode_palette", "prepare_direct", "recon_gemm", "run_pipeline", "autotune", "swiglu",
     "workspace_bytes", "direct_plane_bytes", "variant_count", "variant_name", "variant_supports", "version",
     "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT", "PIPE_EXPAND",
-    "expand_direct",
-    "DERR_BADCODE", "DERR_CHUNKLEN", "STATUS", "Proj", "MlpLayer", "proj", "mlp_layers", "mlp_stack_workspace",
+    "expand_direct", "split_count",
+    "DERR_BADCODE", "DERR_CHUNKLEN", "DERR_RAWINDEX", "STATUS", "Proj", "MlpLayer", "proj", "mlp_layers", "mlp_stack_workspace",
     "mlp_stack_forward",
 ]
 
@@ -33,7 +33,7 @@ OK, EINVAL, ESHAPE, EFORMAT, ERANGE, ENOSPACE, EHIP, EUNSUPPORTED, EINTERNAL = r
 W_BF16, W_EXP, W_IDX, W_DIRECT = 0, 1, 2, 3
 PIPE_FULL, PIPE_EXP, PIPE_TRANSCODE, PIPE_DIRECT, PIPE_EXPAND = 0, 1, 2, 3, 4
 PIPELINE_NAMES = {0: "full", 1: "exp", 2: "transcode", 3: "direct", 4: "expand"}
-DERR_BADCODE, DERR_CHUNKLEN = 1, 2
+DERR_BADCODE, DERR_CHUNKLEN, DERR_RAWINDEX = 1, 2, 4
 
 
 class UwError(RuntimeError):
@@ -62,22 +62,23 @@ class GemmArgs(ctypes.Structure):
     _fields_ = [
         ("M", ctypes.c_int64), ("d_x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("h", ctypes.POINTER(Header)),
         ("d_blob", ctypes.c_void_p), ("src", ctypes.c_int32), ("d_wplane", ctypes.c_void_p),
-        ("d_y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("variant", ctypes.c_int32),
+        ("d_y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("variant", ctypes.c_int32), ("split_k", ctypes.c_int32),
     ]
 
 
 class Plan(ctypes.Structure):
     _fields_ = [("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32), ("t_ms", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32)]
 
     def __repr__(self):
-        return f"Plan(pipeline={PIPELINE_NAMES.get(self.pipeline, self.pipeline)}, variant={self.variant}, t_ms={self.t_ms:.4f})"
+        return (f"Plan(pipeline={PIPELINE_NAMES.get(self.pipeline, self.pipeline)}, variant={self.variant}, "
+                f"split_k={self.split_k}, t_ms={self.t_ms:.4f})")
 
 
 class Proj(ctypes.Structure):
-    """uw_proj: one projection of an MLP layer and the pipeline / variant it runs with."""
+    """uw_proj: one projection of a model and the pipeline / variant / K split it runs with."""
     _fields_ = [("h", ctypes.POINTER(Header)), ("d_blob", ctypes.c_void_p), ("d_direct", ctypes.c_void_p),
-                ("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("pipeline", ctypes.c_int32), ("variant", ctypes.c_int32), ("split_k", ctypes.c_int32)]
 
 
 class MlpLayer(ctypes.Structure):
@@ -105,6 +106,8 @@ class TuneArgs(ctypes.Structure):
         ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p), ("d_ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("reps", ctypes.c_int32), ("warmup", ctypes.c_int32), ("pipeline_mask", ctypes.c_uint32),
         ("variant_mask", ctypes.c_int32), ("d_scrub", ctypes.c_void_p), ("scrub_bytes", ctypes.c_size_t),
+        ("rot", ctypes.POINTER(Proj)), ("n_rot", ctypes.c_int32), ("trials", ctypes.c_int32),
+        ("tune_split", ctypes.c_int32),
     ]
 
 
@@ -149,7 +152,8 @@ def _load():
         "uw_variant_name": ([ctypes.c_int], ctypes.c_char_p),
         "uw_variant_supports": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
         "uw_workspace_bytes": ([H, i32, ctypes.POINTER(sz)], ctypes.c_int),
-        "uw_run_pipeline": ([i32, i32, H, P, P, i64, P, i64, P, i64, P, sz, P, P], ctypes.c_int),
+        "uw_run_pipeline": ([i32, i32, i32, H, P, P, i64, P, i64, P, i64, P, sz, P, P], ctypes.c_int),
+        "uw_split_count": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
         "uw_autotune": ([ctypes.POINTER(TuneArgs), ctypes.POINTER(i64), ctypes.c_int, P, ctypes.POINTER(Plan)],
                         ctypes.c_int),
         "uw_swiglu": ([P, P, i64, P, P], ctypes.c_int),
@@ -281,39 +285,52 @@ def direct_plane_bytes(h: Header) -> int:
     return out.value
 
 
+def split_count(v: int, N: int, K: int, M: int, split_k: int = 0) -> int:
+    """uw_split_count: K slices a launch of variant v (-1 = default) with split_k uses."""
+    return lib.uw_split_count(v, N, K, M, split_k)
+
+
 def recon_gemm(h: Header, d_blob, src: int, d_wplane, d_x, d_y, M: int, ldx: int | None = None,
-               ldy: int | None = None, variant: int = -1, stream=None) -> None:
+               ldy: int | None = None, variant: int = -1, stream=None, split_k: int = 0) -> None:
     a = GemmArgs(M, _ptr(d_x), h.K if ldx is None else ldx, ctypes.pointer(h), _ptr(d_blob), src, _ptr(d_wplane),
-                 _ptr(d_y), h.N if ldy is None else ldy, variant)
+                 _ptr(d_y), h.N if ldy is None else ldy, variant, split_k)
     _check(lib.uw_recon_gemm(ctypes.byref(a), _stream(stream)))
 
 
 def recon_gemm_gate_up(hg: Header, d_blob_g, d_direct_g, hu: Header, d_blob_u, d_direct_u, d_x, d_yg, d_yu, d_h,
                        M: int, ldx: int | None = None, ldf: int | None = None, variant: int = -1,
-                       stream=None) -> None:
+                       stream=None, split_k: int = 0) -> None:
     """uw_recon_gemm_gate_up: gate and up (direct planes, same X) and h = bf16(silu(g) * u)
     in one launch; raises UwError(EUNSUPPORTED) where the fused form does not apply."""
     lx = hg.K if ldx is None else ldx
     lf = hg.N if ldf is None else ldf
     ag = GemmArgs(M, _ptr(d_x), lx, ctypes.pointer(hg), _ptr(d_blob_g), W_DIRECT, _ptr(d_direct_g), _ptr(d_yg), lf,
-                  variant)
+                  variant, split_k)
     au = GemmArgs(M, _ptr(d_x), lx, ctypes.pointer(hu), _ptr(d_blob_u), W_DIRECT, _ptr(d_direct_u), _ptr(d_yu), lf,
-                  variant)
+                  variant, split_k)
     _check(lib.uw_recon_gemm_gate_up(ctypes.byref(ag), ctypes.byref(au), _ptr(d_h), lf, _stream(stream)))
 
 
 def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_direct=None, d_ws=None, ws_bytes: int = 0,
-                 variant: int = -1, d_err=None, ldx: int | None = None, ldy: int | None = None, stream=None) -> None:
-    _check(lib.uw_run_pipeline(pipeline, variant, ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), M, _ptr(d_x),
+                 variant: int = -1, d_err=None, ldx: int | None = None, ldy: int | None = None, stream=None,
+                 split_k: int = 0) -> None:
+    _check(lib.uw_run_pipeline(pipeline, variant, split_k, ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), M, _ptr(d_x),
                                h.K if ldx is None else ldx, _ptr(d_y), h.N if ldy is None else ldy, _ptr(d_ws),
                                ws_bytes, _ptr(d_err), _stream(stream)))
 
 
 def autotune(h: Header, d_blob, d_x, d_y, Ms, d_direct=None, d_ws=None, ws_bytes: int = 0, reps: int = 0,
              warmup: int = 0, pipeline_mask: int = 0, variant_mask: int = 0, d_scrub=None, scrub_bytes: int = 0,
-             stream=None) -> list:
+             stream=None, rot=None, trials: int = 0, tune_split: bool = False) -> list:
+    """uw_autotune. rot: optional list of Proj (same N, K) cycled through by every timed
+    forward, as a model's layers are; without it the one matrix (h, d_blob, d_direct)."""
+    rarr = None
+    if rot:
+        rarr = (Proj * len(rot))(*rot)
     a = TuneArgs(ctypes.pointer(h), _ptr(d_blob), _ptr(d_direct), _ptr(d_x), _ptr(d_y), _ptr(d_ws), ws_bytes, reps,
-                 warmup, pipeline_mask, variant_mask, _ptr(d_scrub), scrub_bytes)
+                 warmup, pipeline_mask, variant_mask, _ptr(d_scrub), scrub_bytes,
+                 ctypes.cast(rarr, ctypes.POINTER(Proj)) if rarr is not None else None, len(rot) if rot else 0,
+                 trials, int(tune_split))
     ms = (ctypes.c_int64 * len(Ms))(*Ms)
     out = (Plan * len(Ms))()
     _check(lib.uw_autotune(ctypes.byref(a), ms, len(Ms), _stream(stream), out))
@@ -324,9 +341,9 @@ def swiglu(d_g, d_u, d_h, n: int, stream=None) -> None:
     _check(lib.uw_swiglu(_ptr(d_g), _ptr(d_u), n, _ptr(d_h), _stream(stream)))
 
 
-def proj(h: Header, d_blob, pipeline: int, d_direct=None, variant: int = -1) -> Proj:
+def proj(h: Header, d_blob, pipeline: int = PIPE_DIRECT, d_direct=None, variant: int = -1, split_k: int = 0) -> Proj:
     """A uw_proj; keep `h` alive as long as the layer array is used."""
-    return Proj(ctypes.pointer(h), _ptr(d_blob), _ptr(d_direct), pipeline, variant)
+    return Proj(ctypes.pointer(h), _ptr(d_blob), _ptr(d_direct), pipeline, variant, split_k)
 
 
 def mlp_layers(layers) -> ctypes.Array:

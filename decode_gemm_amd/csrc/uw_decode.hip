@@ -252,6 +252,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
 // (tile, group) it writes the mask of raw rows and the side-table index of the first raw
 // row, copies those rows' verbatim exponents from the blob's raw table into the side
 // table (ordered by tile, group, row), and zeroes the block bytes of rows past N.
+// The side table has n_raw entries (the header's count). A blob whose bitmap / row_base
+// place a raw group at or past that count is corrupt: such a row is left out of its
+// block's mask (nothing is written for it) and UW_DERR_RAWINDEX is reported, so no write
+// leaves the plane whatever the blob holds.
 struct MetaArgs {
     const uint32_t* bitmap;
     const uint32_t* row_base;
@@ -259,8 +263,9 @@ struct MetaArgs {
     uint8_t* blocks;
     uint32_t* meta;
     uint8_t* side;
+    uint32_t* err;
     int64_t N, G;
-    uint32_t T, words, raw_max;
+    uint32_t T, words, raw_max, n_raw;
 };
 
 __device__ inline uint32_t lanes_below(uint64_t ballot, uint32_t lane)
@@ -304,11 +309,7 @@ __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
             total += static_cast<uint32_t>(__popcll(bal)) << b;
         }
         const uint32_t first = running + prefix;
-        if (valid) {
-            uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
-            m[0] = mask;
-            m[1] = first;
-        }
+        uint32_t kept = mask;  // the mask less the rows whose slot lies past the side table
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const bool bit = (mask >> r) & 1u;
@@ -316,15 +317,27 @@ __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
             if (bit) {
                 uint32_t ri = rb[r] + carry[r] + lanes_below(bal, lane);
                 ri = ri < a.raw_max ? ri : a.raw_max;
+                // slots grow with r, so dropping the rows past the end leaves the base +
+                // popcount addressing of the rows below them unchanged
                 const uint32_t dst = first + __popc(mask & ((1u << r) - 1u));
-                const u32x4* src = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64);
-                u32x4* out = reinterpret_cast<u32x4*>(a.side + static_cast<uint64_t>(dst) * 64);
-                out[0] = src[0];
-                out[1] = src[1];
-                out[2] = src[2];
-                out[3] = src[3];
+                if (dst < a.n_raw) {
+                    const u32x4* src = reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64);
+                    u32x4* out = reinterpret_cast<u32x4*>(a.side + static_cast<uint64_t>(dst) * 64);
+                    out[0] = src[0];
+                    out[1] = src[1];
+                    out[2] = src[2];
+                    out[3] = src[3];
+                } else {
+                    kept &= ~(1u << r);
+                }
             }
             carry[r] += static_cast<uint32_t>(__popcll(bal));
+        }
+        if (valid) {
+            uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
+            m[0] = kept;
+            m[1] = first;
+            if (kept != mask && a.err) atomicOr(a.err, UW_DERR_RAWINDEX);
         }
         running += total;
         if (valid && nrows < 16) {  // last tile: rows past N are zero
@@ -1033,6 +1046,8 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
         m.T = static_cast<uint32_t>(T);
         m.words = h->bitmap_words;
         m.raw_max = a.raw_max;
+        m.n_raw = static_cast<uint32_t>(h->n_raw);
+        m.err = d_err;
         hipLaunchKernelGGL(direct_meta_kernel, dim3((m.T + 3) / 4), dim3(256), 0, s, m);
     }
     hipError_t e = hipGetLastError();

@@ -33,11 +33,6 @@
 
 namespace uw {
 
-// Y = X * W^T on bf16 weights with the vendor GEMM (uw_vendor.hip); hipErrorNotSupported
-// when the library offers no algorithm for the problem.
-hipError_t vendor_gemm_bf16(const uint16_t* w, const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
-                            int64_t ldx, int64_t ldy, hipStream_t s);
-
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -239,11 +234,14 @@ __device__ __forceinline__ void rebuild16_raw(const W16& w, const u32x4& ex, u32
 }
 
 // Side-table address of this lane's 16 raw exponents for a block with meta (mask, base),
-// or `dummy` (any readable 16 bytes) when its row is not raw there.
+// or `dummy` (any readable 16 bytes) when its row is not raw there. The index is clamped
+// to the last side-table entry, so a corrupt meta word cannot move the read outside the
+// plane (with no raw group at all, dside points at the meta section, which is readable).
 __device__ __forceinline__ const u32x4* raw_exp_addr(const GemmArgs& a, u32x2 meta, int r, int g, const uint8_t* dummy)
 {
     const bool raw = (meta.x >> r) & 1u;
-    const uint32_t ri = meta.y + __popc(meta.x & ((1u << r) - 1u));
+    uint32_t ri = meta.y + __popc(meta.x & ((1u << r) - 1u));
+    ri = ri < a.raw_max ? ri : a.raw_max;
     return reinterpret_cast<const u32x4*>(raw ? a.dside + static_cast<uint64_t>(ri) * 64 + 16 * g : dummy);
 }
 
@@ -259,6 +257,7 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
     // what rebuild16 produced for them, (sign, palette[0], mantissa) -> flip the signs.
     // MFMA(T) + MFMA(U) adds (true - rebuilt) * X exactly: both are bf16 values.
     const int64_t off = row * a.K + 64 * static_cast<int64_t>(j) + 16 * g;
+    ri = ri < a.raw_max ? ri : a.raw_max;  // a corrupt row_base / bitmap stays inside the raw table
     const u32x4 sm = *reinterpret_cast<const u32x4*>(a.sm + off);
     const u32x4 ex = *reinterpret_cast<const u32x4*>(a.raw + static_cast<uint64_t>(ri) * 64 + 16 * g);
     uint32_t ea, eb;
@@ -499,7 +498,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
             if constexpr (XNEAR) {
                 (load_slot(jc(us), std::integral_constant<int, us>{}), ...);
                 if (DIRECT) ((us < U / 2 ? load_raw(jc(us), std::integral_constant<int, us>{}) : void()), ...);
-                load_x(wave, xr[0]);
+                load_x(jc(0), xr[0]);  // the slice's first group of this wave
             } else {
                 // the steady state's issue order: (XT: slot k's X,) the raw exponents of slot
                 // k - U/2, slot k's meta and W, (otherwise: slot k's X)
@@ -1181,7 +1180,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
 
 struct Variant {
     const char* name;
-    int kind;  // 0 skinny, 1 tiled, 2 wide, 3 the vendor GEMM (plain bf16 weights only)
+    int kind;  // 0 skinny, 1 tiled, 2 wide
     int rt, nw, u;
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
@@ -1198,7 +1197,7 @@ const Variant kVariants[] = {
     {"skinny rt4 u4 w4", 0, 4, 4, 4, 0, 0},  {"skinny rt4 u2 w8 x1", 0, 4, 8, 2, 0, 0, 1},
     {"skinny rt4 u2 w4 x1", 0, 4, 4, 2, 0, 0, 1}, {"skinny rt2 u4 w8 x1", 0, 2, 8, 4, 0, 0, 1},
     {"skinny rt4 u2 w4 xt", 0, 4, 4, 2, 0, 0, 0, 1}, {"skinny rt4 u4 w4 xt", 0, 4, 4, 4, 0, 0, 0, 1},
-    {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1}, {"vendor hipblaslt", 3, 0, 0, 0, 0, 0},
+    {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1},
     {"skinny rt4 u2 w4 ks", 0, 4, 4, 2, 0, 0, 0, 0, 1}, {"skinny rt4 u2 w4 xt ks", 0, 4, 4, 2, 0, 0, 0, 1, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -1280,14 +1279,17 @@ SlicePlan plan_slices(const SliceModel& mdl, int64_t N, int64_t K, int64_t M, in
     return best;
 }
 
-hipError_t launch_sliced(const void* fn, GemmArgs g, uint32_t tiles, uint32_t ks, uint32_t threads, size_t lds, hipStream_t s)
+// K slices of a launch whose arguments carry kgroups (0 = one slice).
+uint32_t slices_of(const GemmArgs& g)
 {
     const uint32_t G = static_cast<uint32_t>(g.K / 64);
-    g.kgroups = (G + ks - 1) / ks;
-    ks = (G + g.kgroups - 1) / g.kgroups;
-    if (ks > 1) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
+    return g.kgroups ? (G + g.kgroups - 1) / g.kgroups : 1;
+}
+
+hipError_t launch_sliced(const void* fn, GemmArgs g, uint32_t tiles, uint32_t threads, size_t lds, hipStream_t s)
+{
     void* args[] = {&g};
-    return hipLaunchKernel(fn, dim3(tiles, ks), dim3(threads), args, lds, s);
+    return hipLaunchKernel(fn, dim3(tiles, slices_of(g)), dim3(threads), args, lds, s);
 }
 
 template <int SRC, bool CONTIG, int BN, int BM>
@@ -1299,8 +1301,7 @@ hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
     hipError_t e = allow_lds(fn, C::LDS, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM));
-    const uint32_t ks = BN == 128 && BM == 128 ? plan_slices(kTiledModel, g.N, g.K, g.M, BN, BM).ks : 1;
-    e = launch_sliced(fn, g, tiles, ks, 256, C::LDS, s);
+    e = launch_sliced(fn, g, tiles, 256, C::LDS, s);
     return e != hipSuccess ? e : hipGetLastError();
 }
 
@@ -1312,8 +1313,7 @@ hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), lds, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
-    e = launch_sliced(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), g, tiles,
-                      plan_slices(kWideModel, g.N, g.K, g.M, 256, 256).ks, 512, lds, s);
+    e = launch_sliced(reinterpret_cast<const void*>(&gemm_wide<SRC, CONTIG>), g, tiles, 512, lds, s);
     return e != hipSuccess ? e : hipGetLastError();
 }
 
@@ -1330,24 +1330,33 @@ uint32_t skinny_slices(int64_t N, int64_t K, int rt)
     return (G + kg - 1) / kg;
 }
 
+// The K slices a launch of variant v uses on (N, K, M): split_k when it is positive, else
+// the variant's own choice (the time model for the 128x128 and 256x256 tiles, enough
+// slices to fill the CUs for the skinny "ks" variants, none for the others), rounded so
+// that every slice has the same whole number of 64-groups.
+uint32_t resolve_split(const Variant& v, int64_t N, int64_t K, int64_t M, int32_t split_k)
+{
+    const uint32_t G = static_cast<uint32_t>(K / 64);
+    uint32_t ks;
+    if (split_k > 0)
+        ks = static_cast<uint32_t>(split_k);
+    else if (v.kind == 0)
+        ks = v.ks ? skinny_slices(N, K, v.rt) : 1;
+    else if (v.kind == 1)
+        ks = v.bn == 128 && v.bm == 128 ? plan_slices(kTiledModel, N, K, M, 128, 128).ks : 1;
+    else
+        ks = plan_slices(kWideModel, N, K, M, 256, 256).ks;
+    ks = ks < 1 ? 1 : ks > G ? G : ks;
+    const uint32_t kg = (G + ks - 1) / ks;
+    return (G + kg - 1) / kg;
+}
+
 template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
-    if (v.kind == 3) {
-        if (SRC != UW_W_BF16) return hipErrorNotSupported;
-        return vendor_gemm_bf16(static_cast<const uint16_t*>(g.wplane), g.x, g.y, g.M, g.N, g.K, g.ldx, g.ldy, s);
-    }
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
-    if (v.kind == 0 && v.ks) {
-        // Y is zeroed first and every slice adds its part with fp32 atomics
-        const uint32_t G = static_cast<uint32_t>(g.K / 64);
-        const uint32_t ks = skinny_slices(g.N, g.K, v.rt);
-        GemmArgs g2 = g;
-        g2.kgroups = ks > 1 ? (G + ks - 1) / ks : 0;
-        if (g2.kgroups) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
-        if (v.xt) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, true>(g2, s);
-        return launch_skinny_rt<SRC, CONTIG, 4, 2, 4>(g2, s);
-    }
+    // (a "ks" variant is its neighbour's kernel with a K split chosen for it; the split is
+    // in g.kgroups, set by the caller)
     if (v.kind == 0) {
         if (v.rt == 1 && v.u == 8) return launch_skinny_rt<SRC, CONTIG, 1, 8, 4>(g, s);
         if (v.rt == 1 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 1, 4, 8>(g, s);
@@ -1397,8 +1406,9 @@ hipError_t launch_gate_up_rt(const GateUpArgs& ga, hipStream_t s)
 hipError_t launch_gate_up(const GateUpArgs& ga, const Variant& v, hipStream_t s)
 {
     if (v.kind != 0) return hipErrorNotSupported;
-    // a "ks" variant that cuts nothing on this shape is its unsplit neighbour, which has a fused form
-    if (v.ks && skinny_slices(ga.gate.N, ga.gate.K, v.rt) > 1) return hipErrorNotSupported;
+    // one K slice only (a "ks" variant that cuts nothing on this shape is its unsplit
+    // neighbour, which has a fused form)
+    if (ga.gate.kgroups || ga.up.kgroups) return hipErrorNotSupported;
     if (v.xt && v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4, false, true>(ga, s);
     if (v.xt || v.xnear) return hipErrorNotSupported;
     if (v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4>(ga, s);
@@ -1430,7 +1440,8 @@ uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, 
     bool cg = false, cu = false;
     int vg = 0, vu = 0;
     uw_gemm_args upv = *up;
-    upv.variant = gate->variant;  // one launch, one variant: the gate's
+    upv.variant = gate->variant;  // one launch, one variant and split: the gate's
+    upv.split_k = gate->split_k;
     uw_status st = make_args(gate, ga.gate, cg, vg);
     if (st == UW_OK) st = make_args(&upv, ga.up, cu, vu);
     if (st != UW_OK) return st;
@@ -1477,6 +1488,7 @@ uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
     v = p->variant < 0 ? default_variant(h->N, h->K, p->M, p->src) : p->variant;
     if (v >= kNumVariants) return fail(UW_EINVAL, "variant %d out of range", v);
     if (!uw_variant_supports(v, h->N, h->K, p->M, p->src)) return fail(UW_EUNSUPPORTED, "variant %d does not support this problem", v);
+    if (p->split_k < 0 || p->split_k > h->K / 64) return fail(UW_EINVAL, "split_k %d outside 0..K/64", p->split_k);
     if (kVariants[v].kind == 0 && 2 * p->M * p->ldx + 32 * h->K >= (int64_t{1} << 32))
         return fail(UW_EUNSUPPORTED, "variant %d addresses X and W with 32-bit offsets: ldx or K too large", v);
     std::memset(&g, 0, sizeof g);
@@ -1488,6 +1500,9 @@ uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
     g.M = p->M;
     g.N = h->N;
     g.K = h->K;
+    const uint32_t G = static_cast<uint32_t>(h->K / 64);
+    const uint32_t ks = resolve_split(kVariants[v], h->N, h->K, p->M, p->split_k);
+    g.kgroups = ks > 1 ? (G + ks - 1) / ks : 0;  // zero: one slice, Y written, not added into
     contig = false;
     if (p->src != UW_W_BF16) {
         if (!p->d_blob) return fail(UW_EINVAL, "d_blob needed for this src");
@@ -1510,7 +1525,9 @@ uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
         const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
         g.tiles = static_cast<uint32_t>(T);
         g.dmeta = static_cast<const uint8_t*>(p->d_wplane) + 1536 * T * G;
-        g.dside = g.dmeta + (8 * T * G + 63) / 64 * 64;
+        // with no raw group the side table is empty: point it at the meta section (at least
+        // 64 readable bytes) so that a clamped index still reads inside the plane
+        g.dside = h->n_raw > 0 ? g.dmeta + (8 * T * G + 63) / 64 * 64 : g.dmeta;
     }
     return UW_OK;
 }
@@ -1534,7 +1551,8 @@ uw_status launch_expand_direct(const uw_header* h, const uint8_t* d_direct, uint
     const uint64_t T = static_cast<uint64_t>((h->N + 15) / 16), G = static_cast<uint64_t>(h->K / 64);
     g.tiles = static_cast<uint32_t>(T);
     g.dmeta = d_direct + 1536 * T * G;
-    g.dside = g.dmeta + (8 * T * G + 63) / 64 * 64;
+    g.dside = h->n_raw > 0 ? g.dmeta + (8 * T * G + 63) / 64 * 64 : g.dmeta;
+    g.raw_max = h->n_raw > 0 ? static_cast<uint32_t>(h->n_raw - 1) : 0;
     if (T * G == 0) return UW_OK;
     const dim3 grid(static_cast<uint32_t>((T * G + 3) / 4));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1561,13 +1579,15 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const Variant& var = kVariants[v];
+    // K split: Y is zeroed first (a kernel, not a memset, so the launch can be captured in
+    // a graph) and every slice adds its part with fp32 atomics
+    if (g.kgroups) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
     switch (p->src) {
     case UW_W_BF16: e = launch_src<UW_W_BF16, false>(g, var, s); break;
     case UW_W_EXP: e = launch_src<UW_W_EXP, false>(g, var, s); break;
     case UW_W_IDX: e = launch_src<UW_W_IDX, false>(g, var, s); break;
     default: e = contig ? launch_src<UW_W_DIRECT, true>(g, var, s) : launch_src<UW_W_DIRECT, false>(g, var, s); break;
     }
-    if (e == hipErrorNotSupported && var.kind == 3) return fail(UW_EUNSUPPORTED, "the vendor GEMM offers no algorithm for this problem");
     if (e != hipSuccess) return fail(UW_EHIP, "GEMM launch failed: %s", hipGetErrorString(e));
     return UW_OK;
 }
@@ -1591,6 +1611,13 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
 
 int uw_variant_count(void) { return uw::kNumVariants; }
 
+int uw_split_count(int variant, int64_t N, int64_t K, int64_t M, int32_t split_k)
+{
+    if (K < 64 || K % 64 || N < 1 || M < 0 || split_k < 0 || split_k > K / 64 || variant >= uw::kNumVariants) return 0;
+    const int v = variant < 0 ? uw::default_variant(N, K, M, UW_W_DIRECT) : variant;
+    return static_cast<int>(uw::resolve_split(uw::kVariants[v], N, K, M, split_k));
+}
+
 const char* uw_variant_name(int variant)
 {
     if (variant < 0 || variant >= uw::kNumVariants) return "";
@@ -1601,7 +1628,6 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
 {
     if (variant < 0 || variant >= uw::kNumVariants || K % 64 || K < 64) return 0;
     const uw::Variant& v = uw::kVariants[variant];
-    if (v.kind == 3) return M >= 1 && src == UW_W_BF16;
     // a "ks" variant exists only where it cuts K (elsewhere it would be its unsplit neighbour)
     if (v.kind == 0 && v.ks && uw::skinny_slices(N, K, v.rt) < 2) return 0;
     if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X

@@ -91,9 +91,9 @@ using namespace uw;
 
 extern "C" {
 
-uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob, const uint8_t* d_direct,
-                          int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y, int64_t ldy, void* d_ws,
-                          size_t ws_bytes, uint32_t* d_err, void* stream)
+uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, int32_t split_k, const uw_header* h, const void* d_blob,
+                          const uint8_t* d_direct, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y, int64_t ldy,
+                          void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream)
 {
     clear_error();
     if (!h) return fail(UW_EINVAL, "NULL header");
@@ -111,6 +111,7 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h,
     g.d_y = d_y;
     g.ldy = ldy;
     g.variant = variant;
+    g.split_k = split_k;
     switch (pipeline) {
     case UW_PIPE_FULL:
         if ((st = uw_decode_full(h, d_blob, static_cast<uint16_t*>(d_ws), d_err, stream)) != UW_OK) return st;
@@ -149,10 +150,31 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
         clear_error();
         if (!a || !a->h || !Ms || !out || nM < 0) return fail(UW_EINVAL, "NULL argument");
         const uw_header* h = a->h;
-        const int reps = a->reps > 0 ? a->reps : 20;
-        const int warmup = a->warmup > 0 ? a->warmup : 3;
+        const int reps = a->reps > 0 ? a->reps : 10;
+        const int warmup = a->warmup > 0 ? a->warmup : 2;
+        const int trials = a->trials > 0 ? a->trials : 3;
         const uint32_t pmask = a->pipeline_mask ? a->pipeline_mask : 0x1Fu;
         const uint32_t vmask = a->variant_mask ? static_cast<uint32_t>(a->variant_mask) : 0xFFFFFFFFu;
+        // the rotation set: the caller's matrices of this shape, or the single one
+        std::vector<uw_proj> rot;
+        if (a->rot && a->n_rot > 0) {
+            rot.assign(a->rot, a->rot + a->n_rot);
+        } else {
+            uw_proj one;
+            std::memset(&one, 0, sizeof one);
+            one.h = h;
+            one.d_blob = a->d_blob;
+            one.d_direct = a->d_direct;
+            rot.push_back(one);
+        }
+        bool all_direct = true;
+        for (const uw_proj& r : rot) {
+            if (!r.h || !r.d_blob) return fail(UW_EINVAL, "rotation entry with a NULL header or blob");
+            if (r.h->N != h->N || r.h->K != h->K) return fail(UW_EINVAL, "rotation entries must have the header's N and K");
+            all_direct = all_direct && r.d_direct;
+        }
+        for (int mi = 0; mi < nM; mi++)
+            if (Ms[mi] < 1) return fail(UW_ESHAPE, "M must be >= 1");
         hipStream_t s = static_cast<hipStream_t>(stream);
         hipEvent_t e0, e1;
         if (hipEventCreate(&e0) != hipSuccess) return fail(UW_EHIP, "hipEventCreate failed");
@@ -160,56 +182,81 @@ uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* st
             (void)hipEventDestroy(e0);
             return fail(UW_EHIP, "hipEventCreate failed");
         }
+        const uint32_t G = static_cast<uint32_t>(h->K / 64);
         uw_status result = UW_OK;
+        size_t next = 0;  // position in the rotation, carried across candidates
         for (int mi = 0; mi < nM && result == UW_OK; mi++) {
             const int64_t M = Ms[mi];
+            // one forward of candidate (p, v, ks) on the next matrix of the rotation
+            auto run = [&](int p, int v, int ks) -> uw_status {
+                const uw_proj& r = rot[next];
+                next = (next + 1) % rot.size();
+                return uw_run_pipeline(p, v, ks, r.h, r.d_blob, r.d_direct, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
+                                       a->ws_bytes, nullptr, stream);
+            };
             uw_plan best;
             best.pipeline = -1;
             best.variant = -1;
             best.t_ms = 3.0e38f;
-            best.reserved = 0;
+            best.split_k = 0;
             for (int p = 0; p < kPipelines && result == UW_OK; p++) {
                 if (!(pmask >> p & 1u)) continue;
-                if ((p == UW_PIPE_DIRECT || p == UW_PIPE_EXPAND) && !a->d_direct) continue;
+                if ((p == UW_PIPE_DIRECT || p == UW_PIPE_EXPAND) && !all_direct) continue;
                 size_t need = 0;
                 uw_workspace_bytes(h, p, &need);
-                if (need > a->ws_bytes) continue;
+                if (need > a->ws_bytes || (need > 0 && !a->d_ws)) continue;
                 const int32_t src = p == UW_PIPE_FULL || p == UW_PIPE_EXPAND ? UW_W_BF16 : p == UW_PIPE_EXP ? UW_W_EXP
                                     : p == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
                 for (int v = 0; v < uw_variant_count() && result == UW_OK; v++) {
                     if (!(vmask >> v & 1u) || !uw_variant_supports(v, h->N, h->K, M, src)) continue;
-                    std::vector<float> t;
-                    for (int r = 0; r < warmup + reps; r++) {
-                        if (a->d_scrub && r >= warmup) {
-                            if ((result = scrub(a->d_scrub, a->scrub_bytes, static_cast<uint32_t>(r), s)) != UW_OK) break;
+                    // the variant's own split, then (tune_split) the listed counts it does not
+                    // already cover; each count as the launch will round it
+                    std::vector<int> splits = {uw_split_count(v, h->N, h->K, M, 0)};
+                    if (a->tune_split) {
+                        for (int want : {1, 2, 3, 4, 6, 8}) {
+                            if (static_cast<uint32_t>(want) > G / 8 && want > 1) continue;
+                            const int got = uw_split_count(v, h->N, h->K, M, want);
+                            if (got > 0 && std::find(splits.begin(), splits.end(), got) == splits.end()) splits.push_back(got);
                         }
-                        if (r >= warmup && hipEventRecord(e0, s) != hipSuccess) { result = fail(UW_EHIP, "event record failed"); break; }
-                        uw_status st = uw_run_pipeline(p, v, h, a->d_blob, a->d_direct, M, a->d_x, h->K, a->d_y, h->N, a->d_ws,
-                                                       a->ws_bytes, nullptr, stream);
-                        if (st == UW_EUNSUPPORTED) {  // e.g. no vendor algorithm for this shape: not a candidate
-                            clear_error();
-                            t.clear();
-                            break;
+                    }
+                    for (int ks : splits) {
+                        std::vector<float> t;
+                        for (int r = 0; r < warmup && result == UW_OK; r++) {
+                            uw_status st = run(p, v, ks);
+                            if (st == UW_EUNSUPPORTED) {  // a variant this problem cannot use: not a candidate
+                                clear_error();
+                                result = UW_EUNSUPPORTED;
+                            } else if (st != UW_OK) {
+                                result = st;
+                            }
                         }
-                        if (st != UW_OK) { result = st; break; }
-                        if (r >= warmup) {
+                        if (result == UW_EUNSUPPORTED) {
+                            result = UW_OK;
+                            continue;
+                        }
+                        for (int tr = 0; tr < trials && result == UW_OK; tr++) {
+                            if (a->d_scrub && (result = scrub(a->d_scrub, a->scrub_bytes, static_cast<uint32_t>(tr), s)) != UW_OK)
+                                break;
+                            if (hipEventRecord(e0, s) != hipSuccess) { result = fail(UW_EHIP, "event record failed"); break; }
+                            for (int r = 0; r < reps && result == UW_OK; r++) result = run(p, v, ks);
+                            if (result != UW_OK) break;
                             if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
                                 result = fail(UW_EHIP, "event synchronize failed");
                                 break;
                             }
                             float ms = 0.f;
                             (void)hipEventElapsedTime(&ms, e0, e1);
-                            t.push_back(ms);
+                            t.push_back(ms / static_cast<float>(reps));
                         }
-                    }
-                    if (result != UW_OK) break;
-                    if (t.empty()) continue;
-                    std::sort(t.begin(), t.end());
-                    const float med = t[t.size() / 2];
-                    if (med < best.t_ms) {
-                        best.pipeline = p;
-                        best.variant = v;
-                        best.t_ms = med;
+                        if (result != UW_OK || t.empty()) break;
+                        std::sort(t.begin(), t.end());
+                        const float med = t[t.size() / 2];
+                        if (med < best.t_ms) {
+                            best.pipeline = p;
+                            best.variant = v;
+                            best.t_ms = med;
+                            best.split_k = ks;
+                        }
                     }
                 }
             }
@@ -319,6 +366,7 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     g.d_y = y;
     g.ldy = ldy;
     g.variant = p.variant;
+    g.split_k = p.split_k;
     g.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
           : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
     g.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
@@ -346,6 +394,7 @@ uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const u
         a[q].d_y = y[q];
         a[q].ldy = ldf;
         a[q].variant = pr[q]->variant;
+        a[q].split_k = pr[q]->split_k;
     }
     return uw_recon_gemm_gate_up(&a[0], &a[1], h, ldf, stream);
 }
@@ -653,7 +702,8 @@ uw_status uw_mlp_stack_autotune(uw_stack_tune_args* a, void* stream)
             trials++;
             return UW_OK;
         };
-        // coordinate (class, role): set every layer of the class to pipeline p (default variant)
+        // coordinate (class, role): set every layer of the class to pipeline p (default
+        // variant and K split)
         auto get = [&](int c, int r) -> int {
             for (int l = 0; l < n; l++)
                 if (cls[l] == c) return role_of(L[l], r).pipeline;
@@ -666,6 +716,7 @@ uw_status uw_mlp_stack_autotune(uw_stack_tune_args* a, void* stream)
                 uw_proj& pr = r == 0 ? L[l].gate : r == 1 ? L[l].up : L[l].down;
                 pr.pipeline = p;
                 pr.variant = -1;
+                pr.split_k = 0;
             }
         };
         float best = 0.f;

@@ -24,9 +24,8 @@
  *     with leading dimension ldx; Y = X * W^T is [M][N] fp32 with leading dimension ldy.
  *   - "d_" pointers are device (HBM) pointers; all others are host pointers.
  *   - The caller owns every buffer. The library never allocates or frees device memory
- *     and keeps no pointer after a call returns. (One exception: the first call of the
- *     "vendor hipblaslt" GEMM variant on a device creates a hipBLASLt handle, which the
- *     vendor library backs with resources of its own until the process ends.)
+ *     and keeps no pointer after a call returns. Every kernel is the library's own; it
+ *     links no vendor math library.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Device
  *     calls are asynchronous on that stream; their return value reports argument
  *     validation and launch errors only.
@@ -150,6 +149,9 @@ uw_status uw_validate_header(const uw_header* h, size_t blob_bytes);
  */
 #define UW_DERR_BADCODE 1u    /* a bit pattern that is no code of the table */
 #define UW_DERR_CHUNKLEN 2u   /* a chunk's symbols did not end at the next chunk offset */
+#define UW_DERR_RAWINDEX 4u   /* uw_prepare_direct: the bitmap / row_base place a raw group
+                                 at or past the header's n_raw (that row is left out of its
+                                 block's raw mask; nothing is written outside the plane) */
 uw_status uw_decode_full(const uw_header* h, const void* d_blob, uint16_t* d_w, uint32_t* d_err, void* stream);
 uw_status uw_decode_exponent(const uw_header* h, const void* d_blob, uint8_t* d_exp, uint32_t* d_err, void* stream);
 uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* d_idx, uint32_t* d_err,
@@ -204,13 +206,17 @@ uw_status uw_direct_plane_bytes(const uw_header* h, size_t* out);
  * 4-bit palette-index plane plus the sign/mantissa plane, the palette and the raw
  * groups. Weights are rebuilt in registers / LDS and fed to bf16 MFMA; they are never
  * written to memory. Accumulation is fp32; Y is overwritten (not accumulated into).
- * When a problem has too few output tiles to fill the GPU (long K, small N*M), the
- * 128x128 and 256x256 variants and the skinny variants named "... ks" cut K into slices:
- * Y is zeroed on the stream, then each slice adds its partial sums into Y with fp32
- * atomics. With three or more slices the order of those additions is not fixed, so Y may
- * differ in the last bits from run to run (always within the same error bound); one or
- * two slices give identical results. The default variant (-1) never picks a "ks" variant,
- * and uw_variant_supports reports one only for shapes it actually splits.
+ * K split: every variant can cut K into slices of whole 64-groups, one workgroup per
+ * (output tile, slice); Y is then zeroed on the stream and each slice adds its partial
+ * sums into Y with fp32 atomics. split_k = 0 takes the variant's own choice: the 128x128
+ * and 256x256 tiles and the skinny variants named "... ks" split when a problem has too
+ * few output tiles to fill the GPU (long K, small N*M), the others do not; split_k = s >= 1
+ * asks for s slices (rounded so that every slice has the same whole number of groups;
+ * uw_split_count gives the count a launch will use). With three or more slices the order
+ * of the additions is not fixed, so Y may differ in the last bits from run to run (always
+ * within the same error bound); one or two slices give identical results. The default
+ * variant (-1) never picks a "ks" variant, and uw_variant_supports reports one only for
+ * shapes it actually splits.
  */
 typedef enum { UW_W_BF16 = 0, UW_W_EXP = 1, UW_W_IDX = 2, UW_W_DIRECT = 3 } uw_wsrc;
 
@@ -226,9 +232,15 @@ typedef struct {
     float* d_y;            /* Y fp32 [M][ldy], 16-byte aligned */
     int64_t ldy;           /* >= N */
     int32_t variant;       /* kernel variant id, -1 = default for (N, K, M) */
+    int32_t split_k;       /* K slices, 0 = the variant's choice, 1..K/64 (see above) */
 } uw_gemm_args;
 
 uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream);
+
+/* uw_split_count (host): the number of K slices a launch of `variant` (-1 = default) with
+ * split_k uses on (N, K, M); 0 when the arguments are invalid (split_k < 0 or > K/64, an
+ * unknown variant, K not a positive multiple of 64). */
+int uw_split_count(int variant, int64_t N, int64_t K, int64_t M, int32_t split_k);
 
 /*
  * uw_recon_gemm_gate_up (device). The gate and up projections of a SwiGLU MLP and the
@@ -241,8 +253,8 @@ uw_status uw_recon_gemm(const uw_gemm_args* args, void* stream);
  * d_h[M][ldh] = bf16(silu(gate) * up), the same bits as uw_swiglu on those outputs.
  * Errors: UW_EINVAL / UW_ESHAPE as for uw_recon_gemm, and UW_EUNSUPPORTED when the fused
  * form does not apply (not both direct planes, M > 64, a palette whose exponents are not
- * consecutive, or a variant without a fused form); the caller then runs the two GEMMs and
- * uw_swiglu.
+ * consecutive, a variant without a fused form, or a K split); the caller then runs the
+ * two GEMMs and uw_swiglu.
  */
 uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
                                 void* stream);
@@ -250,15 +262,10 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
 /* Kernel variants of uw_recon_gemm (tile shape per CU and pipelining depth, "How the
  * reconstructive matmul works": wider tiles for large batches, deeper buffers for small
  * ones). uw_variant_count() variants exist; uw_variant_name() describes one;
- * uw_variant_supports() says whether a variant accepts (N, K, M, src). The variant named
- * "vendor hipblaslt" takes plain bf16 weights only (UW_W_BF16, the GEMM of the
- * full-decode pipeline, which hands the rebuilt weights to the vendor's standard matrix
- * multiply: "Four ways to use compressed weights"); it calls hipBLASLt with fp32
- * accumulation and fp32 output and returns UW_EUNSUPPORTED if that library offers no
- * algorithm for the problem (uw_autotune then skips it). Its first call on a device, and
- * its first call for each (M, N, K, ldx, ldy), set up hipBLASLt state on the host (a
- * handle, descriptors, a heuristic query); make those calls outside stream capture, e.g.
- * during uw_autotune or a warmup forward. */
+ * uw_variant_supports() says whether a variant accepts (N, K, M, src). Every variant
+ * takes every src, so the plain bf16 GEMM of the full-decode pipeline ("Four ways to use
+ * compressed weights": the decoded weights go to a standard matrix multiply) is the same
+ * kernel family on the UW_W_BF16 loader. */
 int uw_variant_count(void);
 const char* uw_variant_name(int variant);
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
@@ -273,7 +280,7 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
  *   UW_PIPE_EXPAND    uw_expand_direct of that direct plane into workspace, then plain
  *                     bf16 GEMM: the full-decode pipeline fed from the load-time plane
  *                     (a streaming kernel) instead of the Huffman stream, for batches
- *                     large enough that the vendor GEMM on bf16 weights wins
+ *                     large enough that the plain bf16 GEMM beats the reconstructive one
  */
 typedef enum {
     UW_PIPE_FULL = 0,
@@ -283,13 +290,13 @@ typedef enum {
     UW_PIPE_EXPAND = 4
 } uw_pipeline;
 
-/* A per-(matrix, M) execution plan: which pipeline and which GEMM variant ("Why no
- * single pipeline wins": the per-model profile). t_ms = measured median time. */
+/* A per-(matrix, M) execution plan: which pipeline, GEMM variant and K split ("Why no
+ * single pipeline wins": the per-model profile). t_ms = measured time per forward. */
 typedef struct {
     int32_t pipeline;
     int32_t variant;
     float t_ms;
-    int32_t reserved;
+    int32_t split_k; /* the slice count measured (as uw_split_count reports it) */
 } uw_plan;
 
 /* Workspace bytes a pipeline needs for a matrix (the preprocessing slot: 2, 1, 0.5, 0 or
@@ -297,39 +304,65 @@ typedef struct {
 uw_status uw_workspace_bytes(const uw_header* h, int32_t pipeline, size_t* out);
 
 /* Run one pipeline end to end on `stream`: decode into d_ws if the pipeline needs it,
- * then the GEMM. d_direct = the direct plane from uw_prepare_direct (UW_PIPE_DIRECT and
- * UW_PIPE_EXPAND only). */
-uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, const uw_header* h, const void* d_blob,
+ * then the GEMM with `variant` and `split_k` (as in uw_gemm_args). d_direct = the direct
+ * plane from uw_prepare_direct (UW_PIPE_DIRECT and UW_PIPE_EXPAND only). */
+uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, int32_t split_k, const uw_header* h, const void* d_blob,
                           const uint8_t* d_direct, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
                           int64_t ldy, void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream);
 
+/* One projection of a model and how it runs: its header and device blob, its direct plane
+ * (uw_prepare_direct) or NULL, and its plan (pipeline, GEMM variant, K split). Used by the
+ * autotuner's rotation set and by the MLP stack below. */
+typedef struct {
+    const uw_header* h;       /* the projection's header (host) */
+    const void* d_blob;       /* its blob on the device */
+    const uint8_t* d_direct;  /* its direct plane; required for UW_PIPE_DIRECT and UW_PIPE_EXPAND */
+    int32_t pipeline;         /* uw_pipeline */
+    int32_t variant;          /* GEMM variant, -1 = default */
+    int32_t split_k;          /* K split, 0 = the variant's choice */
+} uw_proj;
+
 /*
  * uw_autotune (device, synchronous). For each M in Ms, time every supported (pipeline,
- * variant) pair on the caller's buffers with HIP events (warmup untimed launches, then
- * the median of reps timed ones) and return the fastest in out[i] ("Why no single
- * pipeline wins", "Sharing the GPU between decode and compute": measured, not
- * heuristic). d_direct may be NULL, in which case UW_PIPE_DIRECT and UW_PIPE_EXPAND are
- * not candidates; pipeline_mask 0 means every pipeline (bits 0..4).
- * d_x must hold max(Ms) rows of K bf16, d_y max(Ms) rows of N fp32, and d_ws at least
- * the largest uw_workspace_bytes of the candidate pipelines (smaller workspaces drop
- * the pipelines that do not fit). Blocks until the measurements finish.
+ * variant, K split) candidate and return the fastest in out[i] ("Why no single pipeline
+ * wins", "Sharing the GPU between decode and compute": measured, not heuristic).
+ *
+ * A candidate is timed the way a plan runs in a model: `reps` forwards launched back to
+ * back on `stream`, cycling through the rotation set (rot[0 .. n_rot-1]: matrices of the
+ * same N and K, e.g. the same projection of successive layers or copies of one matrix,
+ * so that caches hold none of the weights), between two HIP events; that is repeated
+ * `trials` times after `warmup` untimed forwards, and t_ms is the median over the trials
+ * of the mean time per forward. Without a rotation set (rot NULL or n_rot 0) the single
+ * matrix (h, d_blob, d_direct) is used. With tune_split, every candidate variant is also
+ * timed at the K splits 1, 2, 3, 4, 6, 8 (those that keep at least 8 groups per slice
+ * and that differ from each other), besides its own choice; otherwise only its own choice.
+ *
+ * Direct-palette and expand candidates need a direct plane for every matrix of the set;
+ * pipeline_mask 0 means every pipeline (bits 0..4). d_x must hold max(Ms) rows of K bf16,
+ * d_y max(Ms) rows of N fp32, and d_ws at least the largest uw_workspace_bytes of the
+ * candidate pipelines (smaller workspaces drop the pipelines that do not fit). Blocks
+ * until the measurements finish. Errors: UW_EINVAL (arguments, a rotation entry of
+ * another shape), UW_EUNSUPPORTED (no candidate for some M), UW_EHIP.
  */
 typedef struct {
-    const uw_header* h;
+    const uw_header* h;      /* shape (N, K); the matrix timed when there is no rotation set */
     const void* d_blob;
     const uint8_t* d_direct; /* direct plane (uw_prepare_direct) or NULL */
     const uint16_t* d_x;  /* [max M][K] bf16 */
     float* d_y;           /* [max M][N] fp32 */
     void* d_ws;
     size_t ws_bytes;
-    int32_t reps;   /* timed launches per candidate, >= 1 (0 = 20) */
-    int32_t warmup; /* untimed launches per candidate (0 = 3) */
+    int32_t reps;   /* forwards per trial, >= 1 (0 = 10) */
+    int32_t warmup; /* untimed forwards per candidate (0 = 2) */
     uint32_t pipeline_mask; /* bit p set = pipeline p is a candidate (0 = all) */
     int32_t variant_mask;   /* bit v set = GEMM variant v is a candidate (0 = all) */
-    void* d_scrub;          /* optional device buffer overwritten before every timed
-                               launch (outside the timed region) so that candidates are
-                               timed with cold caches; NULL = no scrubbing */
+    void* d_scrub;          /* optional device buffer overwritten before every trial
+                               (outside the timed region); NULL = no scrubbing */
     size_t scrub_bytes;     /* multiple of 16 */
+    const uw_proj* rot;     /* rotation set (pipeline / variant fields ignored), or NULL */
+    int32_t n_rot;
+    int32_t trials;         /* timed trials per candidate (0 = 3) */
+    int32_t tune_split;     /* nonzero: also time the K splits listed above */
 } uw_tune_args;
 
 uw_status uw_autotune(const uw_tune_args* args, const int64_t* Ms, int nM, void* stream, uw_plan* out);
@@ -343,8 +376,8 @@ uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h
 
 /*
  * MLP stack (device). One SwiGLU MLP per layer, layers in order: g = X Wg^T, u = X Wu^T,
- * h = bf16(silu(g) u) (uw_swiglu), Y = h Wd^T, each projection through its own pipeline
- * and GEMM variant (e.g. from uw_autotune), all launched on `stream` ("Bundles and
+ * h = bf16(silu(g) u) (uw_swiglu), Y = h Wd^T, each projection through its own pipeline,
+ * GEMM variant and K split (e.g. from uw_autotune), all launched on `stream` ("Bundles and
  * results": gate, activation, up and down per layer; "Sharing the GPU between decode and
  * compute": the next matrix is prepared while the current one multiplies).
  *
@@ -363,14 +396,6 @@ uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h
  * Errors: UW_EINVAL (NULL pointers, bad pipeline, direct plane missing), UW_ESHAPE
  * (shapes differ or do not chain), UW_ENOSPACE (workspace too small), UW_EHIP.
  */
-typedef struct {
-    const uw_header* h;       /* the projection's header (host) */
-    const void* d_blob;       /* its blob on the device */
-    const uint8_t* d_direct;  /* its direct plane; required for UW_PIPE_DIRECT and UW_PIPE_EXPAND */
-    int32_t pipeline;         /* uw_pipeline */
-    int32_t variant;          /* GEMM variant, -1 = default */
-} uw_proj;
-
 typedef struct {
     uw_proj gate, up, down;
 } uw_mlp_layer;

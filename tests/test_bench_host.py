@@ -56,3 +56,32 @@ def test_measured_traffic_needs_the_profiled_sources(tmp_path, monkeypatch):
     f.write_text(json.dumps({"sources_sha256": "0" * 64, "kernels": {key: {"hbm_bytes_per_launch": 123456}}}))
     assert bench.measured_traffic(key) is None  # kernel changed since the counters were taken
     assert np.isfinite(bench.HBM_PEAK_GBS)
+
+
+def test_resident_and_fused_byte_accounting():
+    import decode_gemm_amd as uw
+
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    blob = uw.encode(w)
+    h = uw.inspect(blob)
+    N, K, M = h.N, h.K, 8
+    # B_res: the Huffman blob for the decode-first pipelines, the direct plane otherwise
+    for p in (0, 1, 2):
+        assert bench.resident_bytes(h, p, blob.size) == blob.size
+    for p in (3, 4):
+        assert bench.resident_bytes(h, p, blob.size) == uw.direct_plane_bytes(h)
+    # the fused gate/up launch: two planes, X once, g and u in fp32, h in bf16
+    assert bench.gate_up_bytes(h, h, M) == 2 * uw.direct_plane_bytes(h) + 2 * M * K + 10 * M * N
+
+
+def test_plans_json_round_trip():
+    import decode_gemm_amd as uw
+
+    plans = {1: {"gate": {"pipeline": uw.PIPE_DIRECT, "variant": 5, "split_k": 1, "t_ms": 0.0186},
+                 "down": {"pipeline": uw.PIPE_TRANSCODE, "variant": uw.variant_count() - 1, "split_k": 4, "t_ms": 0.02}}}
+    j = json.loads(json.dumps(bench.plans_to_json(uw, plans)))
+    assert j["1"]["gate"]["variant"] == uw.variant_name(5) and j["1"]["down"]["pipeline"] == "transcode"
+    back = bench.plans_from_json(uw, j)
+    for r in ("gate", "down"):
+        for k in ("pipeline", "variant", "split_k"):
+            assert back[1][r][k] == plans[1][r][k]

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 import synth
+from tests import direct_layout
 from tests.gpu_util import check_gemm, dev, empty_f32, empty_u8, empty_u16, host, log, torch_cuda, zeros_u32
 
 pytestmark = pytest.mark.gpu
@@ -77,10 +78,22 @@ def _check_decoders(m: Mat, what: str):
     assert err == 0 and (host(out).reshape(m.N, m.K) == ref["exp"]).all(), f"{what}: exponent plane differs"
     out, err = m.decode("idx")
     assert err == 0 and (host(out) == ref["idx"]).all(), f"{what}: index plane differs"
+    # the direct plane is a GPU operand layout, not a step of the method: it is checked by
+    # what it must hold (W itself through the format's reader, the raw-group rule of the
+    # oracle, the bytes the format fixes to zero), not against an oracle copy of the layout
     out, err = m.decode("direct")
-    dref = oracle.direct_plane(m.w)
-    assert out.numel() == dref.size, f"{what}: direct plane size"
-    assert err == 0 and (host(out) == dref).all(), f"{what}: direct plane differs"
+    plane = host(out)
+    assert err == 0, f"{what}: direct plane error flags {err}"
+    assert plane.size == direct_layout.plane_bytes(m.N, m.K, m.h.n_raw), f"{what}: direct plane size"
+    pal_sorted = sorted(int(v) for v in m.h.palette[: m.h.n_pal])
+    assert (direct_layout.rebuild(plane, pal_sorted, m.N, m.K) == m.w).all(), f"{what}: direct plane does not hold W"
+    assert direct_layout.zero_bytes_ok(plane, m.N, m.K) == [], f"{what}: direct plane format"
+    _, e_ref = oracle.split(m.w)
+    pal_ref, _ = oracle.palette(e_ref)
+    bitmap, _, _ = oracle.raw_groups(e_ref.reshape(m.N, m.K), pal_ref)
+    G = m.K // 64
+    raw_ref = ((bitmap[:, np.arange(G) // 32] >> (np.arange(G) % 32).astype(np.uint32)) & 1).astype(bool)
+    assert (direct_layout.raw_masks(plane, m.N, m.K) == raw_ref).all(), f"{what}: raw rows of the direct plane"
     # the direct plane expanded back to bf16 is the original matrix, bit for bit
     wx = empty_u16(m.N * m.K)
     wx.fill_(0x5A5A)  # every weight must be written
@@ -140,6 +153,59 @@ def test_decoder_reports_corruption():
     bad[ms.h.off_stream + 3] |= 0x80  # bit 0 of the first word (MSB) set
     _, err = Mat(ws, blob=bad).decode("exp")
     assert err & uw.DERR_BADCODE
+
+
+def test_corrupt_raw_bookkeeping_stays_inside_the_buffers():
+    """A device blob whose row_base and bitmap claim raw groups past the raw table (only the
+    header is validated for device blobs): uw_prepare_direct drops those rows, reports
+    UW_DERR_RAWINDEX and writes nothing past the plane (a sentinel guard region after it
+    is untouched); the GEMMs that read raw groups through the corrupt blob or plane clamp
+    their reads and finish (their values are meaningless)."""
+    w = synth.gen_weight(synth.CONFIGS["tiny"], "w")
+    m = Mat(w, 256)
+    assert m.h.n_raw > 0
+    bad = m.blob.copy()
+    N, K = m.N, m.K
+    rb = np.frombuffer(bad[m.h.off_rowbase: m.h.off_rowbase + 4 * (N + 1)].tobytes(), "<u4").copy()
+    rb[300:] += 10000  # rows 300.. claim raw groups far past the table
+    bad[m.h.off_rowbase: m.h.off_rowbase + 4 * (N + 1)] = np.frombuffer(rb.tobytes(), np.uint8)
+    bw = m.h.bitmap_words
+    bm = np.frombuffer(bad[m.h.off_bitmap: m.h.off_bitmap + 4 * N * bw].tobytes(), "<u4").copy().reshape(N, bw)
+    bm[N - 3:] = 0xFFFFFFFF  # the last rows: every group raw (more than the table holds)
+    bad[m.h.off_bitmap: m.h.off_bitmap + 4 * N * bw] = np.frombuffer(bm.tobytes(), np.uint8)
+    # uw_inspect rejects this blob on the host; a blob already on the device is only
+    # header-checked, so it is uploaded as is with the (unchanged) header
+    with pytest.raises(uw.UwError):
+        uw.inspect(bad)
+    d_bad = dev(bad)
+    pb = uw.direct_plane_bytes(m.h)
+    guard = 4096
+    buf = empty_u8(pb + guard)
+    buf.fill_(0xA5)
+    err = zeros_u32()
+    uw.prepare_direct(m.h, d_bad, buf, err)
+    _sync()
+    assert int(host(err)[0]) & uw.DERR_RAWINDEX
+    assert (host(buf)[pb:] == 0xA5).all(), "uw_prepare_direct wrote past the plane"
+    # GEMMs over the corrupt blob (index plane, raw groups from row_base / bitmap) and over
+    # the plane with corrupt side-table bases: every variant finishes, Y's guard is intact
+    idx = empty_u8(N * K // 2)
+    uw.transcode_palette(m.h, d_bad, idx, err)
+    meta_off = 1536 * ((N + 15) // 16) * (K // 64)
+    plane = host(buf)[:pb].copy()
+    meta = np.frombuffer(plane[meta_off: meta_off + 8 * ((N + 15) // 16) * (K // 64)].tobytes(), "<u4").copy()
+    meta[1::2] += 5000  # side-table bases past the table
+    plane[meta_off: meta_off + meta.size * 4] = np.frombuffer(meta.tobytes(), np.uint8)
+    d_plane = dev(plane)
+    for src, wp in ((uw.W_IDX, idx), (uw.W_DIRECT, d_plane)):
+        for M in (1, 16, 200):
+            x = dev(synth.gen_x(synth.CONFIGS["tiny"], M, K))
+            for v in _variants_for(m, M, src):
+                yg = empty_f32(M * N + guard // 4)
+                yg.fill_(1.5)
+                uw.recon_gemm(m.h, d_bad, src, wp, x, yg, M, variant=v)
+                _sync()
+                assert (host(yg)[M * N:] == 1.5).all(), f"src {src} variant {v} M={M} wrote past Y"
 
 
 # ---------------------------------------------------------------- GEMM
@@ -432,32 +498,75 @@ def test_swiglu_against_oracle():
 
 
 def test_autotune_picks_the_fastest_and_the_choice_is_correct():
+    """uw_autotune times candidates back to back over a rotation set (here four matrices of
+    one shape, as a model's layers): its pick is within 1.25x + 2 us of the best time each
+    pipeline reaches when tuned on its own, its K split is one the launch can use, and the
+    chosen plan computes the right Y on every matrix of the set."""
     cfg = synth.CONFIGS["tiny"]
-    w = synth.gen_weight(cfg, "w")
-    m = Mat(w)
-    direct, _ = m.decode("direct")
+    mats = []
+    for i in range(4):
+        w = synth.gen_weight(cfg, "w") if i == 0 else np.roll(synth.gen_weight(cfg, "w"), 37 * i, axis=1)
+        m = Mat(w)
+        m.direct, _ = m.decode("direct")
+        mats.append(m)
+    m0 = mats[0]
+    rot = [uw.proj(m.h, m.d_blob, d_direct=m.direct) for m in mats]
     Ms = [1, 64, 256]
-    x = synth.gen_x(cfg, max(Ms), m.K)
+    x = synth.gen_x(cfg, max(Ms), m0.K)
     d_x = dev(x)
-    y = empty_f32(max(Ms), m.N)
-    ws = empty_u8(uw.workspace_bytes(m.h, uw.PIPE_FULL))
-    plans = uw.autotune(m.h, m.d_blob, d_x, y, Ms, d_direct=direct, d_ws=ws, ws_bytes=ws.numel(), reps=15, warmup=3)
+    y = empty_f32(max(Ms), m0.N)
+    ws = empty_u8(uw.workspace_bytes(m0.h, uw.PIPE_FULL))
+    kw = dict(d_ws=ws, ws_bytes=ws.numel(), reps=20, warmup=3, trials=5, rot=rot, tune_split=True)
+    plans = uw.autotune(m0.h, m0.d_blob, d_x, y, Ms, **kw)
     log(f"  plans {plans}")
     for M, plan in zip(Ms, plans):
         assert 0 <= plan.pipeline <= 4 and plan.t_ms > 0
-        per = []
-        for p in range(5):
-            per.append(uw.autotune(m.h, m.d_blob, d_x, y, [M], d_direct=direct, d_ws=ws, ws_bytes=ws.numel(), reps=15,
-                                   warmup=3, pipeline_mask=1 << p)[0].t_ms)
-        # kernels here run ~10 us, so separate measurements differ by a few us of launch noise
-        assert plan.t_ms <= min(per) * 1.5 + 0.005, (M, plan, per)
-        # the chosen plan computes the right result
-        yy = empty_f32(M, m.N)
-        uw.run_pipeline(plan.pipeline, m.h, m.d_blob, dev(x[:M]), yy, M, d_direct=direct, d_ws=ws, ws_bytes=ws.numel(),
-                        variant=plan.variant)
-        _sync()
-        y_ref, a_ref = oracle.gemm(x[:M], w)
-        check_gemm(host(yy), y_ref, a_ref, f"autotuned M={M}")
+        assert plan.split_k == uw.split_count(plan.variant, m0.N, m0.K, M, plan.split_k) >= 1
+        per = [uw.autotune(m0.h, m0.d_blob, d_x, y, [M], pipeline_mask=1 << p, **kw)[0].t_ms for p in range(5)]
+        assert plan.t_ms <= min(per) * 1.25 + 0.002, (M, plan, per)
+        # the chosen plan computes the right result on every matrix it was timed on
+        for m in mats:
+            yy = empty_f32(M, m.N)
+            uw.run_pipeline(plan.pipeline, m.h, m.d_blob, dev(x[:M]), yy, M, d_direct=m.direct, d_ws=ws,
+                            ws_bytes=ws.numel(), variant=plan.variant, split_k=plan.split_k)
+            _sync()
+            y_ref, a_ref = oracle.gemm(x[:M], m.w)
+            check_gemm(host(yy), y_ref, a_ref, f"autotuned M={M}")
+
+
+def test_autotune_rejects_rotation_of_another_shape():
+    cfg = synth.CONFIGS["tiny"]
+    w = synth.gen_weight(cfg, "w")
+    m, m2 = Mat(w), Mat(w[:256])
+    x = dev(synth.gen_x(cfg, 4, m.K))
+    y = empty_f32(4, m.N)
+    with pytest.raises(uw.UwError) as e:
+        uw.autotune(m.h, m.d_blob, x, y, [4], rot=[uw.proj(m.h, m.d_blob), uw.proj(m2.h, m2.d_blob)],
+                    pipeline_mask=1 << uw.PIPE_TRANSCODE, d_ws=empty_u8(m.N * m.K), ws_bytes=m.N * m.K)
+    assert e.value.status == uw.EINVAL
+
+
+def test_explicit_k_splits_match_the_oracle():
+    """Every variant at several explicit K splits (1, 2, 3, 5 slices and the most the shape
+    allows) on a long-K shape, through each loader: Y within the bound of the oracle."""
+    rng = np.random.default_rng(83)
+    w = synth.f32_to_bf16_bits(rng.standard_normal((200, 64 * 23), dtype=np.float32) * 0.02)
+    w.reshape(-1)[rng.choice(w.size, 30, replace=False)] ^= 0x0A00  # out-of-palette exponents
+    m = Mat(w)
+    planes = _planes(m)
+    for M in (1, 33, 130):
+        x = synth.f32_to_bf16_bits(rng.standard_normal((M, m.K), dtype=np.float32))
+        y_ref, a_ref = oracle.gemm(x, w)
+        d_x = dev(x)
+        for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX, uw.W_DIRECT):
+            for v in _variants_for(m, M, src):
+                for ks in (1, 2, 3, 5, 23):
+                    assert uw.split_count(v, m.N, m.K, M, ks) == ks
+                    y = empty_f32(M, m.N)
+                    y.fill_(float("nan"))
+                    uw.recon_gemm(m.h, m.d_blob, src, planes[src], d_x, y, M, variant=v, split_k=ks)
+                    _sync()
+                    check_gemm(host(y), y_ref, a_ref, f"M={M} src={src} variant={v} split={ks}")
 
 
 def test_stack_layers_teacher_forced():

@@ -286,3 +286,22 @@ def test_stream_pair_argument_checks():
     assert e.value.status == uw.EINVAL
     assert uw.lib.uw_stream_destroy(None) == uw.EINVAL
     assert uw.lib.uw_stream_cu_count(None, None) == uw.EINVAL
+
+
+def test_split_count_rounds_to_whole_groups():
+    """uw_split_count: an explicit split is rounded so every slice has the same whole number
+    of 64-groups; out-of-range requests give 0."""
+    names = [uw.variant_name(v) for v in range(uw.variant_count())]
+    assert not any("vendor" in n for n in names)
+    v = names.index("tiled 128x128")
+    N, K = 4096, 14336  # 224 groups
+    assert uw.split_count(v, N, K, 1024, 1) == 1
+    assert uw.split_count(v, N, K, 1024, 3) == 3  # 75 groups per slice -> 3 slices
+    assert uw.split_count(v, N, K, 1024, 5) == 5
+    assert uw.split_count(v, N, K, 1024, 224) == 224
+    assert uw.split_count(v, N, K, 1024, 225) == 0
+    assert uw.split_count(v, N, K, 1024, -1) == 0
+    assert uw.split_count(v, 256, 448, 64, 5) == 4  # 7 groups: 2 per slice -> 4 slices
+    assert uw.split_count(v, 256, 448, 64, 0) >= 1
+    assert uw.split_count(len(names), N, K, 1024, 1) == 0
+    assert uw.split_count(v, N, 100, 1024, 1) == 0
