@@ -154,6 +154,8 @@ def _load():
         "uw_workspace_bytes": ([H, i32, ctypes.POINTER(sz)], ctypes.c_int),
         "uw_run_pipeline": ([i32, i32, i32, H, P, P, i64, P, i64, P, i64, P, sz, P, P], ctypes.c_int),
         "uw_split_count": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
+        "uw_run_pipeline_noalloc": ([i32, i32, i32, H, P, P, i64, P, i64, P, i64, P, P], ctypes.c_int),
+        "uw_noalloc_scratch_bytes": ([], sz),
         "uw_autotune": ([ctypes.POINTER(TuneArgs), ctypes.POINTER(i64), ctypes.c_int, P, ctypes.POINTER(Plan)],
                         ctypes.c_int),
         "uw_swiglu": ([P, P, i64, P, P], ctypes.c_int),
@@ -317,6 +319,20 @@ def run_pipeline(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_direct=No
     _check(lib.uw_run_pipeline(pipeline, variant, split_k, ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), M, _ptr(d_x),
                                h.K if ldx is None else ldx, _ptr(d_y), h.N if ldy is None else ldy, _ptr(d_ws),
                                ws_bytes, _ptr(d_err), _stream(stream)))
+
+
+def run_pipeline_noalloc(pipeline: int, h: Header, d_blob, d_x, d_y, M: int, d_direct=None, variant: int = -1,
+                         split_k: int = 0, d_err=None, ldx: int | None = None, ldy: int | None = None,
+                         stream=None) -> None:
+    """uw_run_pipeline_noalloc: the pipeline with its preprocessing slot in the library's
+    scratch array (noalloc_scratch_bytes()); calls that overlap on one GPU race on it."""
+    _check(lib.uw_run_pipeline_noalloc(pipeline, variant, split_k, ctypes.byref(h), _ptr(d_blob), _ptr(d_direct), M,
+                                       _ptr(d_x), h.K if ldx is None else ldx, _ptr(d_y), h.N if ldy is None else ldy,
+                                       _ptr(d_err), _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return lib.uw_noalloc_scratch_bytes()
 
 
 def autotune(h: Header, d_blob, d_x, d_y, Ms, d_direct=None, d_ws=None, ws_bytes: int = 0, reps: int = 0,

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "uw_internal.h"
@@ -72,6 +73,36 @@ __global__ void swiglu_kernel(const float* __restrict__ g, const float* __restri
     } else {
         for (int64_t i = i8; i < n; i++) h[i] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(g[i], u[i])));
     }
+}
+
+// Preprocessing slot of uw_run_pipeline_noalloc: a file-scope device array, one per GPU the
+// library runs on, held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from hipGetSymbolAddress, looked
+// up once per device (with that device current) and kept in scratch_ptrs.
+constexpr size_t kScratchBytes = size_t{128} << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptrs[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (a symbol lookup on the first call
+// per device, no allocation).
+uw_status scratch_ptr(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(UW_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(UW_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail(UW_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        scratch_ptrs[dev] = p;
+    }
+    *out = scratch_ptrs[dev];
+    return UW_OK;
 }
 
 uw_status scrub(void* d, size_t bytes, uint32_t value, hipStream_t s)
@@ -143,6 +174,27 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, int32_t split_k, co
     }
     return uw_recon_gemm(&g, stream);
 }
+
+uw_status uw_run_pipeline_noalloc(int32_t pipeline, int32_t variant, int32_t split_k, const uw_header* h,
+                                  const void* d_blob, const uint8_t* d_direct, int64_t M, const uint16_t* d_x,
+                                  int64_t ldx, float* d_y, int64_t ldy, uint32_t* d_err, void* stream)
+{
+    clear_error();
+    if (!h) return fail(UW_EINVAL, "NULL header");
+    size_t need = 0;
+    uw_status st = uw_workspace_bytes(h, pipeline, &need);
+    if (st != UW_OK) return st;
+    if (need > kScratchBytes)
+        return fail(UW_ENOSPACE, "pipeline %d needs %zu bytes of preprocessing slot; the allocation-free entry point has %zu",
+                    pipeline, need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_ptr(&ws)) != UW_OK) return st;
+    // the decoders overwrite every byte of the plane they write, so nothing is cleared
+    return uw_run_pipeline(pipeline, variant, split_k, h, d_blob, d_direct, M, d_x, ldx, d_y, ldy, ws, need, d_err,
+                           stream);
+}
+
+size_t uw_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 uw_status uw_autotune(const uw_tune_args* a, const int64_t* Ms, int nM, void* stream, uw_plan* out)
 {

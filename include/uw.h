@@ -310,6 +310,24 @@ uw_status uw_run_pipeline(int32_t pipeline, int32_t variant, int32_t split_k, co
                           const uint8_t* d_direct, int64_t M, const uint16_t* d_x, int64_t ldx, float* d_y,
                           int64_t ldy, void* d_ws, size_t ws_bytes, uint32_t* d_err, void* stream);
 
+/*
+ * uw_run_pipeline_noalloc (device). uw_run_pipeline for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels, with the preprocessing slot taken from a scratch array
+ * the library holds in device memory, uw_noalloc_scratch_bytes() bytes (128 MiB) per GPU,
+ * from the library's load until the process ends. No device memory is allocated or freed
+ * by the call; the first call on a device looks the array's address up. The caller still
+ * passes X, Y, the blob and the direct plane. Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from several threads)
+ * race on it and must be ordered by the caller. Errors: those of uw_run_pipeline, and
+ * UW_ENOSPACE when the pipeline's slot (uw_workspace_bytes) exceeds the array.
+ */
+uw_status uw_run_pipeline_noalloc(int32_t pipeline, int32_t variant, int32_t split_k, const uw_header* h,
+                                  const void* d_blob, const uint8_t* d_direct, int64_t M, const uint16_t* d_x,
+                                  int64_t ldx, float* d_y, int64_t ldy, uint32_t* d_err, void* stream);
+/* Bytes of the scratch array behind uw_run_pipeline_noalloc (the largest slot it takes). */
+size_t uw_noalloc_scratch_bytes(void);
+
 /* One projection of a model and how it runs: its header and device blob, its direct plane
  * (uw_prepare_direct) or NULL, and its plan (pipeline, GEMM variant, K split). Used by the
  * autotuner's rotation set and by the MLP stack below. */

@@ -305,3 +305,18 @@ def test_split_count_rounds_to_whole_groups():
     assert uw.split_count(v, 256, 448, 64, 0) >= 1
     assert uw.split_count(len(names), N, K, 1024, 1) == 0
     assert uw.split_count(v, N, 100, 1024, 1) == 0
+
+
+def test_noalloc_entry_point_rejects_slots_beyond_its_scratch():
+    """uw_run_pipeline_noalloc refuses, before any device call, a pipeline whose
+    preprocessing slot is larger than the library's scratch array (bf16 weights of a
+    8200 x 8192 matrix: 2 B/w > 128 MiB); a pipeline that needs no slot is not refused
+    for size."""
+    assert uw.noalloc_scratch_bytes() == 128 << 20
+    w = np.full((8200, 8192), 0x3C00, np.uint16)
+    h = uw.inspect(uw.encode(w))
+    assert uw.workspace_bytes(h, uw.PIPE_FULL) > uw.noalloc_scratch_bytes()
+    for p in (uw.PIPE_FULL, uw.PIPE_EXPAND):
+        with pytest.raises(uw.UwError) as e:
+            uw.run_pipeline_noalloc(p, h, 0x1000, 0x1000, 0x1000, 1, d_direct=0x1000, stream=0)
+        assert e.value.status == uw.ENOSPACE
