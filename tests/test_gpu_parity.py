@@ -445,7 +445,11 @@ def test_stream_read_sizes_and_argument_errors():
 
 
 # ---------------------------------------------------------------- full sizes
-def _full_size_case(cfg, proj, Ms, n_samples=4096):
+def _full_size_case(cfg, proj, Ms, n_samples=4096, splits=(0, 2)):
+    """Decoded planes in full, then every GEMM variant the shape and M allow (the ones the
+    plans pick among), through every loader, at the variant's own K split and at the
+    splits listed: a seeded sample of Y against the oracle, gathered on the device."""
+    torch = torch_cuda()
     w = synth.gen_weight(cfg, proj)
     log(f"  {cfg.name}/{proj}: encoding {w.shape}")
     m = Mat(w)
@@ -455,15 +459,21 @@ def _full_size_case(cfg, proj, Ms, n_samples=4096):
     rng = np.random.default_rng(12345)
     for M in Ms:
         x = synth.gen_x(cfg, M, m.K)
+        d_x = dev(x)
         mi = rng.integers(0, M, n_samples)
         ni = rng.integers(0, m.N, n_samples)
         y_ref, a_ref = oracle.gemm_pairs(x, w, mi, ni)
+        d_mi, d_ni = torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()
+        y = empty_f32(M, m.N)
         for src in (uw.W_BF16, uw.W_EXP, uw.W_IDX, uw.W_DIRECT):
-            v = -1  # the default variant, as launched by the pipelines and the bench
-            log(f"  {cfg.name}/{proj} M={M} src={src}")
-            y = _run_gemm(m, planes, src, x, v)
-            check_gemm(y[mi, ni], y_ref, a_ref, f"{cfg.name}/{proj} M={M} src={src}")
-            assert np.isfinite(y).all()
+            for v in _variants_for(m, M, src):
+                for ks in splits:
+                    what = f"{cfg.name}/{proj} M={M} src={src} {uw.variant_name(v)} split={ks}"
+                    log(f"  {what}")
+                    y.fill_(float("nan"))
+                    uw.recon_gemm(m.h, m.d_blob, src, planes[src], d_x, y, M, variant=v, split_k=ks)
+                    check_gemm(y[d_mi, d_ni].cpu().numpy(), y_ref, a_ref, what)
+                    assert bool(torch.isfinite(y).all().item()), f"{what}: unwritten outputs"
 
 
 def test_full_size_gate():
@@ -476,8 +486,8 @@ def test_full_size_down():
 
 def test_full_size_70b():
     cfg = synth.CONFIGS["70b"]
-    _full_size_case(cfg, "gate", (1, 64, 512, 2048))
-    _full_size_case(cfg, "down", (1, 64, 512, 2048), n_samples=2048)
+    _full_size_case(cfg, "gate", (1, 64, 512, 2048), splits=(0,))
+    _full_size_case(cfg, "down", (1, 64, 512, 2048), n_samples=2048, splits=(0,))
 
 
 # ---------------------------------------------------------------- glue, autotune
