@@ -20,7 +20,8 @@ __all__ = [
     "decode_exponent", "transcode_palette", "prepare_direct", "recon_gemm", "run_pipeline", "autotune", "swiglu",
     "workspace_bytes", "direct_plane_bytes", "variant_count", "variant_name", "variant_supports", "version",
     "W_BF16", "W_EXP", "W_IDX", "W_DIRECT", "PIPE_FULL", "PIPE_EXP", "PIPE_TRANSCODE", "PIPE_DIRECT", "PIPE_EXPAND",
-    "expand_direct", "split_count",
+    "expand_direct", "split_count", "run_pipeline_noalloc", "noalloc_scratch_bytes", "bundle_write", "bundle_open",
+    "bundle_items", "bundle_plans", "load_bundle", "variant_by_name",
     "DERR_BADCODE", "DERR_CHUNKLEN", "DERR_RAWINDEX", "STATUS", "Proj", "MlpLayer", "proj", "mlp_layers", "mlp_stack_workspace",
     "mlp_stack_forward",
 ]
@@ -111,6 +112,24 @@ class TuneArgs(ctypes.Structure):
     ]
 
 
+class BundleItem(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_size_t)]
+
+
+class BundlePlan(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("M", ctypes.c_int64), ("pipeline", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("t_ms", ctypes.c_float), ("variant", ctypes.c_char * 48)]
+
+
+class BundleInfo(ctypes.Structure):
+    _fields_ = [("n_items", ctypes.c_uint32), ("n_plans", ctypes.c_uint32), ("total_bytes", ctypes.c_uint64)]
+
+
+class BundleEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("offset", ctypes.c_uint64), ("blob_bytes", ctypes.c_uint64),
+                ("header", Header)]
+
+
 def _preload_torch_hip():
     """Load the HIP runtime that PyTorch ships, if PyTorch is installed, before libuw.so.
 
@@ -156,6 +175,12 @@ def _load():
         "uw_split_count": ([ctypes.c_int, i64, i64, i64, i32], ctypes.c_int),
         "uw_run_pipeline_noalloc": ([i32, i32, i32, H, P, P, i64, P, i64, P, i64, P, P], ctypes.c_int),
         "uw_noalloc_scratch_bytes": ([], sz),
+        "uw_bundle_write": ([ctypes.POINTER(BundleItem), ctypes.c_int, ctypes.POINTER(BundlePlan), ctypes.c_int, P,
+                             ctypes.POINTER(sz)], ctypes.c_int),
+        "uw_bundle_open": ([P, sz, ctypes.c_int, ctypes.POINTER(BundleInfo)], ctypes.c_int),
+        "uw_bundle_item_at": ([P, sz, u32, ctypes.POINTER(BundleEntry)], ctypes.c_int),
+        "uw_bundle_plan_at": ([P, sz, u32, ctypes.POINTER(BundlePlan)], ctypes.c_int),
+        "uw_variant_by_name": ([ctypes.c_char_p], ctypes.c_int),
         "uw_autotune": ([ctypes.POINTER(TuneArgs), ctypes.POINTER(i64), ctypes.c_int, P, ctypes.POINTER(Plan)],
                         ctypes.c_int),
         "uw_swiglu": ([P, P, i64, P, P], ctypes.c_int),
@@ -437,3 +462,80 @@ def stream_cu_count(stream=None) -> int:
     out = ctypes.c_int(0)
     _check(lib.uw_stream_cu_count(_stream(stream), ctypes.byref(out)))
     return out.value
+
+
+# ---------------------------------------------------------------- bundle
+def variant_by_name(name: str) -> int:
+    return lib.uw_variant_by_name(name.encode())
+
+
+def bundle_write(items, plans=()) -> np.ndarray:
+    """uw_bundle_write: items = [(name, host blob)], plans = [dict(N, K, M, pipeline,
+    split_k, t_ms, variant=<index or name, -1 / "" = default>)] -> the bundle bytes."""
+    blobs = [np.ascontiguousarray(b, dtype=np.uint8) for _, b in items]
+    arr = (BundleItem * max(1, len(items)))()
+    for i, ((name, _), b) in enumerate(zip(items, blobs)):
+        arr[i] = BundleItem(name.encode(), b.ctypes.data, b.size)
+    parr = (BundlePlan * max(1, len(plans)))()
+    for i, p in enumerate(plans):
+        v = p.get("variant", "")
+        vname = v if isinstance(v, str) else ("" if v < 0 else variant_name(v))
+        parr[i] = BundlePlan(p["N"], p["K"], p["M"], p["pipeline"], p.get("split_k", 0), p.get("t_ms", 0.0),
+                             vname.encode())
+    need = ctypes.c_size_t(0)
+    st = lib.uw_bundle_write(arr, len(items), parr, len(plans), None, ctypes.byref(need))
+    if st != ENOSPACE:
+        _check(st)
+    out = np.empty(need.value, np.uint8)
+    _check(lib.uw_bundle_write(arr, len(items), parr, len(plans), out.ctypes.data, ctypes.byref(need)))
+    return out
+
+
+def bundle_open(buf: np.ndarray, verify: bool = True) -> BundleInfo:
+    info = BundleInfo()
+    _check(lib.uw_bundle_open(buf.ctypes.data, buf.size, int(verify), ctypes.byref(info)))
+    return info
+
+
+def bundle_items(buf: np.ndarray) -> list:
+    """[(name, offset, blob_bytes, Header)] of a bundle in host memory."""
+    info = bundle_open(buf, verify=False)
+    out = []
+    for i in range(info.n_items):
+        e = BundleEntry()
+        _check(lib.uw_bundle_item_at(buf.ctypes.data, buf.size, i, ctypes.byref(e)))
+        out.append((e.name.decode(), e.offset, e.blob_bytes, e.header))
+    return out
+
+
+def bundle_plans(buf: np.ndarray) -> list:
+    """[dict(N, K, M, pipeline, split_k, t_ms, variant_name, variant)] of a bundle; variant
+    is the index in this build (-1 for the default or a name it lacks)."""
+    info = bundle_open(buf, verify=False)
+    out = []
+    for i in range(info.n_plans):
+        p = BundlePlan()
+        _check(lib.uw_bundle_plan_at(buf.ctypes.data, buf.size, i, ctypes.byref(p)))
+        name = p.variant.decode()
+        out.append({"N": p.N, "K": p.K, "M": p.M, "pipeline": p.pipeline, "split_k": p.split_k, "t_ms": p.t_ms,
+                    "variant_name": name, "variant": variant_by_name(name) if name else -1})
+    return out
+
+
+def load_bundle(buf: np.ndarray, device="cuda", direct=True, verify: bool = True) -> dict:
+    """Load every blob of a bundle into device memory (torch tensors) and, with direct,
+    transcode each into its direct-palette plane with uw_prepare_direct (the load-time
+    step of the direct pipeline). Returns {name: (Header, d_blob, d_direct or None)}."""
+    import torch
+
+    bundle_open(buf, verify=verify)
+    out = {}
+    for name, off, nbytes, h in bundle_items(buf):
+        d_blob = torch.from_numpy(buf[off: off + nbytes]).to(device)
+        d_direct = None
+        if direct:
+            d_direct = torch.empty(direct_plane_bytes(h), dtype=torch.uint8, device=device)
+            prepare_direct(h, d_blob, d_direct)
+        out[name] = (h, d_blob, d_direct)
+    return out
+

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libuw.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 HIP_SOURCES = ["uw_decode.hip", "uw_gemm.hip", "uw_runtime.hip"]
-HOST_SOURCES = ["uw_host.cpp"]
+HOST_SOURCES = ["uw_host.cpp", "uw_bundle.cpp"]
 # Packed fp32 VALU forms are kept out of the generated code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]

@@ -386,6 +386,65 @@ typedef struct {
 uw_status uw_autotune(const uw_tune_args* args, const int64_t* Ms, int nM, void* stream, uw_plan* out);
 
 /*
+ * Model bundle (host). One file for distribution and inference ("Bundles and results":
+ * every projection Huffman-coded in one package, transcoded at load into the form its
+ * pipeline reads, e.g. with uw_prepare_direct), together with the per-model profile of
+ * measured plans ("Sharing the GPU between decode and compute": pipeline, matmul variant
+ * and K split per projection shape and batch size). All calls work on caller buffers
+ * holding the whole bundle in host memory (a read file or a mapping of it).
+ *
+ * Layout (little-endian, offsets multiples of 256): a 64-byte header ("UWB1", version 1,
+ * counts, table offsets, total size, checksum of the tables); n_items records of 128
+ * bytes (name, blob offset, blob bytes, blob checksum); n_plans records of 96 bytes (N, K,
+ * M, pipeline, split_k, t_ms, variant name); then the blobs verbatim, each 256-byte
+ * aligned. Variants are stored by name so that a profile outlives a change of the
+ * variant table (uw_variant_by_name maps a name back; -1 when this build lacks it).
+ */
+#define UW_BUNDLE_NAME_MAX 64
+typedef struct {
+    const char* name;   /* NUL-terminated, 1..63 bytes, unique in the bundle */
+    const void* blob;   /* host blob from uw_encode */
+    size_t blob_bytes;
+} uw_bundle_item;
+
+typedef struct {
+    int64_t N, K;       /* the projection shape the plan is for */
+    int64_t M;          /* batch size */
+    int32_t pipeline;   /* uw_pipeline */
+    int32_t split_k;    /* as in uw_gemm_args */
+    float t_ms;         /* measured time per forward */
+    char variant[48];   /* uw_variant_name of the GEMM variant, "" = the default */
+} uw_bundle_plan;
+
+typedef struct {
+    uint32_t n_items, n_plans;
+    uint64_t total_bytes;
+} uw_bundle_info;
+
+typedef struct {
+    char name[UW_BUNDLE_NAME_MAX];
+    uint64_t offset;      /* of the blob from the start of the bundle (256-byte aligned) */
+    uint64_t blob_bytes;
+    uw_header header;     /* the blob's header (header-level checks passed) */
+} uw_bundle_entry;
+
+/* uw_bundle_write: write a bundle of n_items blobs (each validated with uw_inspect) and
+ * n_plans plans into out. Two-call size query as for uw_encode (out NULL or *out_bytes
+ * too small: UW_ENOSPACE with the size needed). Errors: UW_EINVAL (names empty, too long
+ * or repeated; a bad plan record), the blob's own validation status. */
+uw_status uw_bundle_write(const uw_bundle_item* items, int n_items, const uw_bundle_plan* plans, int n_plans, void* out,
+                          size_t* out_bytes);
+/* uw_bundle_open: validate a bundle in memory (header, tables and their checksum, every
+ * item's place and blob header; with verify != 0 also each blob's checksum and full
+ * uw_inspect validation) and report its counts. UW_EFORMAT on any inconsistency. */
+uw_status uw_bundle_open(const void* bundle, size_t bytes, int verify, uw_bundle_info* info);
+/* Item i (name, where its blob sits, its header) and plan i of a bundle. */
+uw_status uw_bundle_item_at(const void* bundle, size_t bytes, uint32_t i, uw_bundle_entry* out);
+uw_status uw_bundle_plan_at(const void* bundle, size_t bytes, uint32_t i, uw_bundle_plan* out);
+/* Index of the variant named `name`, or -1. */
+int uw_variant_by_name(const char* name);
+
+/*
  * uw_swiglu (device). The activation between the MLP projections of a SwiGLU layer:
  * h[i] = bf16(silu(g[i]) * u[i]), silu(z) = z / (1 + e^-z), fp32 math, rounded to
  * nearest-even bf16. g, u fp32 [n], h bf16 [n], all 16-byte aligned.

@@ -187,3 +187,69 @@ def test_stack_32_layers_forward_teacher_forced():
             torch.cuda.synchronize()
             _check_last(st, last, x, y, ws, M, rng, f"M={M}")
             del ws
+
+
+class _Loaded:
+    """Stack layers taken from a loaded bundle ({name: (Header, d_blob, d_direct)})."""
+
+    def __init__(self, loaded):
+        self.h, self.blob, self.plane = {}, {}, {}
+        for l in range(CFG.layers):
+            for q in range(3):
+                h, b, p = loaded[f"layers.{l}.mlp.{ROLES[q]}_proj"]
+                self.h[(l, q)], self.blob[(l, q)], self.plane[(l, q)] = h, b, p
+
+    arr = _Stack.arr
+
+
+def test_stack_bundle_round_trip_load_and_forward():
+    """The 32-layer stack written as one bundle (96 Huffman blobs and the plans at M = 64
+    and 1024), opened with full verification and loaded with transcode at load
+    (uw_prepare_direct per projection): the planes equal those made from the original
+    blobs, and the forward on the bundle's own plans matches the oracle (last layer
+    teacher-forced)."""
+    torch = torch_cuda()
+
+    def make(i):
+        layer, q = divmod(i, 3)
+        return uw.encode(_weight(layer, ROLES[q]))
+
+    with cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 8))) as ex:
+        blobs = list(ex.map(make, range(3 * CFG.layers)))
+    names = [f"layers.{l}.mlp.{r}_proj" for l in range(CFG.layers) for r in ROLES]
+    F, K = 14336, 4096
+    plans = [dict(N=F, K=K, M=64, pipeline=uw.PIPE_DIRECT, split_k=0, variant="skinny rt4 u2 w4 xt"),
+             dict(N=K, K=F, M=64, pipeline=uw.PIPE_DIRECT, split_k=4, variant="skinny rt4 u2 w4 xt ks"),
+             dict(N=F, K=K, M=1024, pipeline=uw.PIPE_EXPAND, split_k=0, variant="wide 256x256"),
+             dict(N=K, K=F, M=1024, pipeline=uw.PIPE_DIRECT, split_k=4, variant="wide 256x256")]
+    buf = uw.bundle_write(list(zip(names, blobs)), plans)
+    total = sum(b.size for b in blobs)
+    log(f"  bundle {buf.size / 1e9:.2f} GB for {total / 1e9:.2f} GB of blobs")
+    assert total <= buf.size < total + 256 * (len(blobs) + 64)
+    info = uw.bundle_open(buf, verify=True)
+    assert info.n_items == 96 and info.n_plans == 4
+    loaded = uw.load_bundle(buf)
+    st = _Loaded(loaded)
+    for l, q in ((0, 0), (17, 2), (31, 1)):
+        ref = empty_u8(uw.direct_plane_bytes(st.h[(l, q)]))
+        uw.prepare_direct(st.h[(l, q)], dev(blobs[3 * l + q]), ref)
+        assert torch.equal(ref, st.plane[(l, q)]), f"layer {l} {ROLES[q]}: plane from the bundle differs"
+    del blobs
+    bplans = uw.bundle_plans(buf)
+    rng = np.random.default_rng(11)
+    xs = synth.gen_x(CFG, 1024, K)
+    for M in (64, 1024):
+        by = {(p["N"], p["K"]): p for p in bplans if p["M"] == M}
+        plan_of = lambda l, q: (lambda p: (p["pipeline"], p["variant"], p["split_k"]))(by[(K, F)] if q == 2 else by[(F, K)])
+        order = list(range(CFG.layers))
+        arr = st.arr(order, plan_of)
+        nb = uw.mlp_stack_workspace(arr, M)
+        ws = empty_u8(nb)
+        y = empty_f32(M, K)
+        y.fill_(float("nan"))
+        x = xs[:M]
+        log(f"  bundle stack forward M={M}")
+        uw.mlp_stack_forward(arr, M, dev(x), y, ws, nb)
+        torch.cuda.synchronize()
+        _check_last(st, CFG.layers - 1, x, y, ws, M, rng, f"bundle M={M}")
+        del ws
