@@ -1049,18 +1049,27 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
     // covers tile rows 8 (4 wave + q) .. +7, lane l takes row + l % 8 and 16 bytes l / 8, so
     // eight consecutive lanes store eight rows of one column of the operand-order LDS
     // stage (distinct banks). A row-sliced operand load would touch twice the cache lines.
+    // Load q of this wave covers tile rows 8 (4 wave + q) .. +7: lane l takes row + l / 8 and
+    // 16-byte chunk l % 8, so consecutive lanes read consecutive bytes of a row (a wave reads
+    // eight whole 128-byte row segments). Chunk kap = 2 g + h goes to fragment block (16-row
+    // tile, h) at slot 16 g + (row % 16 ^ 2 g ^ 8 h) instead of 16 g + row % 16: each group of
+    // 16 lanes then stores into 16 distinct 16-byte bank groups, and a fragment read (lane
+    // 16 g + r of block h reads that slot) still does.
     const uint8_t* xseg[4];
     const uint8_t* wseg[4];
     int sdst[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        const int rho = 8 * (4 * wave + q) + (lane & 7), kap = lane >> 3;
+        const int rho = 8 * (4 * wave + q) + (lane >> 3), kap = lane & 7;
         const int64_t m = m0 + rho, n = n0 + rho;
         xseg[q] = reinterpret_cast<const uint8_t*>(a.x + (m < a.M ? m : a.M - 1) * a.ldx) + 16 * kap;
         wseg[q] = static_cast<const uint8_t*>(a.wplane) + 2 * (n < a.N ? n : a.N - 1) * a.K + 16 * kap;
-        sdst[q] = (2 * (rho >> 4) + (kap & 1)) * 64 + 16 * (kap >> 1) + (rho & 15);
+        const int gq = kap >> 1, hq = kap & 1;
+        sdst[q] = (2 * (rho >> 4) + hq) * 64 + 16 * gq + ((rho & 15) ^ (2 * gq) ^ (8 * hq));
     }
     constexpr bool WSEG = SRC == UW_W_BF16;
+    // fragment slot of this lane in a block staged from row segments (X, and bf16 W), per h
+    const int fslot[2] = {16 * g + (r ^ (2 * g)), 16 * g + (r ^ (2 * g) ^ 8)};
 
     floatx4 acc[TN][TM];
 #pragma unroll
@@ -1138,10 +1147,10 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         for (int h = 0; h < 2; h++) {
             u32x4 bf[TM];
 #pragma unroll
-            for (int c = 0; c < TM; c++) bf[c] = B[((TM * wm + c) * 2 + h) * 64 + lane];
+            for (int c = 0; c < TM; c++) bf[c] = B[((TM * wm + c) * 2 + h) * 64 + fslot[h]];
 #pragma unroll
             for (int i = 0; i < TN; i++) {
-                const u32x4 af = A[((TN * wn + i) * 2 + h) * 64 + lane];
+                const u32x4 af = A[((TN * wn + i) * 2 + h) * 64 + (WSEG ? fslot[h] : lane)];
 #pragma unroll
                 for (int c = 0; c < TM; c++) acc[i][c] = mfma16(af, bf[c], acc[i][c]);
             }
