@@ -46,7 +46,7 @@ ROLES = ("gate", "up", "down")
 # measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by the counters of a copy of known size); used only while the GEMM sources
 # still hash to what was profiled
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_direct_gate_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_stack_traffic.json")
 GEMM_SOURCES = ["decode_gemm_amd/csrc/uw_gemm.hip", "decode_gemm_amd/csrc/uw_recon.h",
                 "decode_gemm_amd/csrc/uw_internal.h"]
 
