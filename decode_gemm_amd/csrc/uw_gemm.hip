@@ -62,6 +62,26 @@ __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// s_waitcnt that waits for LDS reads only (lgkmcnt 0; vmcnt and expcnt at their maxima).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// LDS byte offset of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void* p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// One LDS DMA of 16 bytes per lane: lane l's bytes at base + voff go to LDS at lds + 16 l.
+// Issued from asm so that the compiler's wait counting does not make every later LDS read
+// wait for the newest transfer; the compiler then undercounts outstanding loads, which
+// only ever makes its own waits stricter. Callers order the reads of the target
+// themselves (a wait for a load issued after the transfer).
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+                 : "memory");
+}
+
 // Rank of raw group j among the raw groups of row `row` (the row's bitmap words before
 // j's word are popcounted; only reached for raw groups).
 __device__ __forceinline__ uint32_t raw_index(const GemmArgs& a, int64_t row, uint32_t j, uint32_t bw)
@@ -281,16 +301,21 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // wave-uniform, so the compiler waits for exactly the slot it consumes. Lanes of columns
 // m >= M read row M-1 (their outputs are never stored). CT = ceil(M / 16).
 //
-// Raw groups. Direct plane: each slot also carries its block's raw-row mask (requested
-// with the slot, a full ring turn ahead) and, half a turn ahead, the lane's verbatim
-// exponents when its row is raw (any readable address otherwise), so a raw row is just a
-// per-lane select in the rebuild. Index plane: the rebuild yields (sign, palette[0],
-// mantissa) for raw groups and the exact difference to the true weights is added after
-// the loop with extra MFMAs, from metadata fetched when the kernel starts.
+// Raw groups. Direct plane: each slot also carries its blocks' metas (raw-row mask,
+// side-table base; requested with the slot, a full ring turn ahead) and, half a turn
+// ahead, one load that brings the verbatim exponents of the first raw rows of all its
+// row tiles at once (lane 16i + 4k + p: raw row k of tile i, piece p, for RT = 4); a
+// lane of a raw row fetches its piece from there with a cross-lane read and substitutes
+// it in the rebuild. Every vector load in the loop costs address and data-return cycles
+// whatever it carries, and most blocks have no raw row, so one load per group instead of
+// one per row tile. Rows past those a slot covers are read directly (rare). Index
+// plane: the rebuild yields (sign, palette[0], mantissa) for raw groups and the exact
+// difference to the true weights is added after the loop with extra MFMAs, from
+// metadata fetched when the kernel starts.
 // The block's tile: everything up to its reduced outputs, which go to sink(o, n, m, y) for
 // each Y element (o = the element's index in the block tile) inside [0, N) x [0, M).
 // red: the block's LDS (the cross-wave reduction, and the X tiles with XT).
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT, class Sink>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT, class Sink>
 __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&& sink)
 {
     static_assert(U % 2 == 0, "ring depth must be even");
@@ -317,12 +342,14 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     PlaneS<SRC> pl[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) pl[i] = PlaneS<SRC>(a, nb + 16 * i, r, g);
-    // direct plane: lane i < RT fetches the meta (raw-row mask, side base) of row tile i,
-    // so a slot's metas are one vector load, retired in order with the slot's other loads
-    // (scalar loads may return out of order and would have to be waited for at once)
+    // direct plane: the lanes LPT i .. LPT i + LPT - 1 fetch the meta (raw-row mask, side
+    // base) of row tile i, so a slot's metas are one vector load, retired in order with the
+    // slot's other loads (scalar loads may return out of order and would have to be waited
+    // for at once), and each lane holds the meta of the tile whose raw exponents it fetches
+    constexpr int LPT = 64 / RT, RAWK = LPT / 4;
     const uint8_t* pmeta = nullptr;
     if (DIRECT) {
-        int64_t t = (nb >> 4) + (lane < RT ? lane : 0);
+        int64_t t = (nb >> 4) + lane / LPT;
         t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
         pmeta = a.dmeta + 8 * t * G;
     }
@@ -350,6 +377,30 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     }
     u32x4* const xs = reinterpret_cast<u32x4*>(red) + wave * (16 * CT * XS_PITCH);
     const uint8_t* const xb = reinterpret_cast<const uint8_t*>(a.x);
+    // XT 2: the same row segments, but sent by LDS DMA straight into a wave-private ring of U
+    // tiles (16 CT rows x 128 bytes each). Load q fills rows 8q .. 8q+7; lane l fetches the
+    // 16 bytes of row rho = 8q + l/8 that go to position l % 8, chunk (l % 8) ^ ((rho / 2) % 8),
+    // so the 8 lanes of a row still read its whole segment, and a fragment read (row 16c + r,
+    // chunk 2g + s2, found at position (2g + s2) ^ (r / 2)) hits 16 distinct bank groups
+    // per 16 lanes. No register holds X on the way.
+    uint8_t* const xd = reinterpret_cast<uint8_t*>(red) + wave * (U * CT * 2048);
+    uint32_t xofd[XT == 2 ? 2 * CT : 1], xfo[2];
+    if (XT == 2) {
+#pragma unroll
+        for (int q = 0; q < 2 * CT; q++) {
+            const int rho = 8 * q + (lane >> 3);
+            const int64_t m = rho < a.M ? rho : a.M - 1;
+            xofd[q] = static_cast<uint32_t>(2 * m * a.ldx + 16 * ((lane & 7) ^ ((rho >> 1) & 7)));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) xfo[s2] = static_cast<uint32_t>(128 * r + 16 * ((2 * g + s2) ^ (r >> 1)));
+    }
+    const uint32_t xd_lds = lds_offset(xd);
+    auto dma_x = [&](uint32_t j, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 2 * CT; q++)
+            dma16(xb + 128 * static_cast<int64_t>(j), xofd[XT == 2 ? q : 0], xd_lds + (slot * 2 * CT + q) * 1024);
+    };
 
     // Index plane: raw-group metadata of this wave's rows (local rows wave + NW * q),
     // fetched now and consumed after the main loop: lane q holds row_base of row q, and
@@ -398,8 +449,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     };
     W16 ring[U][RT];
     u32x4 xr[XNEAR ? 1 : U][CT][2];
-    u32x2 mr[DIRECT ? U : 1];  // direct: lane i holds the slot's (raw-row mask, side base) of row tile i
-    u32x4 rx[DIRECT ? U : 1][RT];  // direct: this lane's raw exponents for the slot's group
+    // direct plane: the slot's metas, and one load of raw exponents per slot: lane
+    // LPT i + 4k + p holds piece p of raw row k of tile i (k < RAWK)
+    u32x2 mr[DIRECT ? U : 1];
+    u32x4 rx[DIRECT ? U : 1];
     auto load_slot = [&](uint32_t j, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         // the meta goes first: it is read half a ring turn later, and waiting for it must
@@ -408,21 +461,20 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
 #pragma unroll
         for (int i = 0; i < RT; i++) pl[i].load(j, ring[u][i]);
     };
-    auto load_raw = [&](uint32_t j, auto vc) __attribute__((always_inline)) {
+    auto load_raw = [&](auto vc) __attribute__((always_inline)) {
         constexpr int v = decltype(vc)::value % (DIRECT ? U : 1);
-#pragma unroll
-        for (int i = 0; i < RT; i++)
-        {
-            // the block's raw-row mask is the same in every lane, and most blocks have no raw
-            // row: then skip the address arithmetic and read the (always readable) meta
-            // section instead. The load itself is always issued, so every wait in the loop
-            // stays a counted one.
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.dmeta);
-            const u32x2 meta = {static_cast<uint32_t>(__builtin_amdgcn_readlane(mr[v].x, i)),
-                                static_cast<uint32_t>(__builtin_amdgcn_readlane(mr[v].y, i))};
-            if (meta.x) src = raw_exp_addr(a, meta, r, g, a.dmeta);
-            rx[v][i] = *src;
+        // every lane holds the meta of its tile; a lane past the tile's raw rows, or of a
+        // tile with none, reads the (always readable) meta section instead. The load is
+        // always issued, so every wait in the loop stays a counted one.
+        const int k = (lane % LPT) >> 2, p4 = lane & 3;
+        const uint32_t mx = mr[v].x, my = mr[v].y;
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.dmeta);
+        if (static_cast<uint32_t>(k) < static_cast<uint32_t>(__popc(mx))) {
+            uint32_t ri = my + k;
+            ri = ri < a.raw_max ? ri : a.raw_max;
+            src = reinterpret_cast<const u32x4*>(a.dside + static_cast<uint64_t>(ri) * 64 + 16 * p4);
         }
+        rx[v] = *src;
     };
     // one group: rebuild ring slot u (group t), refill it with group t + U, request the
     // raw exponents of group t + U/2, multiply, then refill the X pieces
@@ -430,7 +482,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         constexpr int u = decltype(uc)::value;
         const uint32_t j = j0 + wave + NW * t;
         u32x4 XF[XT ? CT : 1][2];  // XT: this step's X fragments, back from the LDS tile
-        if (XT) {
+        if (XT == 2) {
+            // the slot's X transfer was issued before its W loads, and loads retire in
+            // order: once the slot's first W register is waited for, its X is in LDS
+            asm volatile("" ::"v"(ring[u][0].a.x));
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t* const xs2 = xd + u * (CT * 2048);
+#pragma unroll
+            for (int c = 0; c < CT; c++)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; s2++) XF[XT ? c : 0][s2] = *reinterpret_cast<const u32x4*>(xs2 + 2048 * c + xfo[s2]);
+        }
+        if (XT == 1) {
 #pragma unroll
             for (int q = 0; q < 2 * CT; q++) xs[(8 * q + (lane >> 3)) * XS_PITCH + (lane & 7)] = xr[XNEAR ? 0 : u][q >> 1][q & 1];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -450,8 +513,25 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         for (int i = 0; i < RT; i++) {
             rebuild16<SRC, CONTIG>(a, ring[u][i], A[i][0], A[i][1]);
             if (DIRECT) {
-                const uint32_t mask = __builtin_amdgcn_readlane(mr[u % (DIRECT ? U : 1)].x, i);
-                if (mask && ((mask >> r) & 1u)) rebuild16_raw(ring[u][i], rx[u % (DIRECT ? U : 1)][i], A[i][0], A[i][1]);
+                const uint32_t mask = __builtin_amdgcn_readlane(mr[u % (DIRECT ? U : 1)].x, LPT * i);
+                if (mask) {
+                    // raw rows in this tile: row r's piece g comes from lane LPT i + 4k + g
+                    // (k = its rank among the tile's raw rows), or straight from the side
+                    // table past the first RAWK
+                    const uint32_t k = __popc(mask & ((1u << r) - 1u));
+                    const u32x4 v = rx[u % (DIRECT ? U : 1)];
+                    const int sl = 4 * (LPT * i + 4 * static_cast<int>(k < RAWK ? k : 0) + g);
+                    u32x4 ex = {static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl, v.x)),
+                                static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl, v.y)),
+                                static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl, v.z)),
+                                static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl, v.w))};
+                    const bool raw = (mask >> r) & 1u;
+                    if (__builtin_expect(__popc(mask) > RAWK, 0) && raw && k >= RAWK) {
+                        const u32x2 m = {mask, static_cast<uint32_t>(__builtin_amdgcn_readlane(mr[u % (DIRECT ? U : 1)].y, LPT * i))};
+                        ex = *raw_exp_addr(a, m, r, g, a.dmeta);
+                    }
+                    if (raw) rebuild16_raw(ring[u][i], ex, A[i][0], A[i][1]);
+                }
             }
         }
         if constexpr (XNEAR) {
@@ -466,13 +546,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                     for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[0][c][s2], acc[i][c]);
             if (refill || t + 1 < T) load_x(j + NW, xr[0]);  // unconditional in the steady state
             if (refill) load_slot(j + NW * U, uc);
-            if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+            if (DIRECT && rawpf) load_raw(std::integral_constant<int, (u + U / 2) % U>{});
         } else {
             // issue order is pinned: (XT: the X refill,) the raw exponents consumed half a
             // turn from now, the W slot refill (a full turn ahead), the MFMAs, the X refill;
             // waiting for any of them then never waits for a younger request
             __builtin_amdgcn_sched_barrier(0);
-            if (DIRECT && rawpf) load_raw(j + NW * (U / 2), std::integral_constant<int, (u + U / 2) % U>{});
+            if (XT == 2 && refill) {
+                // the fragment reads of this slot are done before its next X lands there
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                dma_x(j + NW * U, u);
+            }
+            if (DIRECT && rawpf) load_raw(std::integral_constant<int, (u + U / 2) % U>{});
             if (refill) load_slot(j + NW * U, uc);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -497,7 +582,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         [&]<int... us>(std::integer_sequence<int, us...>) {
             if constexpr (XNEAR) {
                 (load_slot(jc(us), std::integral_constant<int, us>{}), ...);
-                if (DIRECT) ((us < U / 2 ? load_raw(jc(us), std::integral_constant<int, us>{}) : void()), ...);
+                if (DIRECT) ((us < U / 2 ? load_raw(std::integral_constant<int, us>{}) : void()), ...);
                 load_x(jc(0), xr[0]);  // the slice's first group of this wave
             } else {
                 // the steady state's issue order: (XT: slot k's X,) the raw exponents of slot
@@ -507,9 +592,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                     // (pinned: the loop head's wait counts are the minimum over this path
                     // and the loop's own, so a reordered prologue would weaken them)
                     __builtin_amdgcn_sched_barrier(0);
-                    if (XT) load_x(jc(k), xr[XNEAR ? 0 : k]);
+                    if (XT == 1) load_x(jc(k), xr[XNEAR ? 0 : k]);
+                    if (XT == 2) dma_x(jc(k), k);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (DIRECT && k >= U / 2) load_raw(jc(k - U / 2), std::integral_constant<int, (k + U / 2) % U>{});
+                    if (DIRECT && k >= U / 2) load_raw(std::integral_constant<int, (k + U / 2) % U>{});
                     __builtin_amdgcn_sched_barrier(0);
                     load_slot(jc(k), kc);
                     __builtin_amdgcn_sched_barrier(0);
@@ -584,6 +670,8 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
 
     // cross-wave reduction: red[w][i][c][q][lane] (XT: over the X tiles, once every wave
     // is done with its own)
+    // (XT 2: every transfer has landed, those of ring slots past the wave's last group too)
+    if (XT == 2) __builtin_amdgcn_s_waitcnt(0);
     if (XT) __syncthreads();
     constexpr int TILES = RT * CT;
 #pragma unroll
@@ -607,7 +695,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     }
 }
 
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 {
     extern __shared__ float red[];
@@ -619,12 +707,15 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
     });
 }
 
-// LDS of a skinny block: the cross-wave reduction, or the X tiles with XT (aliased).
-template <int CT, int RT, int NW, bool XT>
+// LDS of a skinny block: the cross-wave reduction, or the X tiles (aliased): XT 1, one
+// padded tile per wave; XT 2, a ring of U DMA targets per wave.
+template <int CT, int RT, int U, int NW, int XT>
 constexpr size_t skinny_lds()
 {
     constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
-    constexpr size_t xt_bytes = XT ? static_cast<size_t>(NW) * 16 * CT * 9 * 16 : 0;
+    constexpr size_t xt_bytes = XT == 1 ? static_cast<size_t>(NW) * 16 * CT * 9 * 16
+                              : XT == 2 ? static_cast<size_t>(NW) * U * CT * 2048
+                                        : 0;
     return red_bytes > xt_bytes ? red_bytes : xt_bytes;
 }
 
@@ -638,11 +729,11 @@ struct GateUpArgs {
     int64_t ldh;
 };
 
-template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, int XT>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
 {
     extern __shared__ float red[];
-    float* const gbuf = red + skinny_lds<CT, RT, NW, XT>() / 4;  // RT * CT * 256 gate outputs
+    float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT>() / 4;  // RT * CT * 256 gate outputs
     skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT>(ga.gate, red, [&](int o, int64_t n, int64_t m, float v) {
         ga.gate.y[m * ga.gate.ldy + n] = v;
         gbuf[o] = v;
@@ -756,12 +847,28 @@ __device__ __forceinline__ void add_tile(const GemmArgs& a, float* ep, const flo
     }
 }
 
-__global__ void zero_rows(float* y, int64_t ldy, int64_t M, int64_t N)
+// Y[0, M) x [0, N) = 0: rows m = blockIdx.y + k gridDim.y, four columns per thread (one
+// 16-byte store when ldy keeps the rows 16-byte aligned).
+__global__ void __launch_bounds__(256) zero_rows(float* y, int64_t ldy, int64_t M, int64_t N)
 {
-    const int64_t total = M * N;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-         e += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        y[(e / N) * ldy + e % N] = 0.f;
+    const int64_t n = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+    if (n >= N) return;
+    const bool vec = (ldy & 3) == 0 && n + 4 <= N;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        float* row = y + m * ldy + n;
+        if (vec) {
+            *reinterpret_cast<floatx4*>(row) = floatx4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            for (int64_t q = 0; q < 4 && n + q < N; q++) row[q] = 0.f;
+        }
+    }
+}
+
+hipError_t launch_zero_rows(float* y, int64_t ldy, int64_t M, int64_t N, hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>((N + 1023) / 1024), static_cast<uint32_t>(M < 65535 ? M : 65535));
+    hipLaunchKernelGGL(zero_rows, grid, dim3(256), 0, s, y, ldy, M, N);
+    return hipGetLastError();
 }
 
 template <int BN, int BM>
@@ -1193,7 +1300,8 @@ struct Variant {
     int rt, nw, u;
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
-    int xt;     // skinny: X read as whole row segments and put in operand order through LDS
+    int xt;     // skinny: X read as whole row segments and put in operand order through LDS:
+                // 1 staged in registers ("xt"), 2 by LDS DMA into a ring of tiles ("xd")
     int ks;     // skinny: K cut into slices so that row blocks x slices fill the CUs (fp32 atomics into Y)
 };
 
@@ -1208,6 +1316,8 @@ const Variant kVariants[] = {
     {"skinny rt4 u2 w4 xt", 0, 4, 4, 2, 0, 0, 0, 1}, {"skinny rt4 u4 w4 xt", 0, 4, 4, 4, 0, 0, 0, 1},
     {"skinny rt2 u4 w4 xt", 0, 2, 4, 4, 0, 0, 0, 1},
     {"skinny rt4 u2 w4 ks", 0, 4, 4, 2, 0, 0, 0, 0, 1}, {"skinny rt4 u2 w4 xt ks", 0, 4, 4, 2, 0, 0, 0, 1, 1},
+    {"skinny rt4 u2 w8 xd", 0, 4, 8, 2, 0, 0, 0, 2},    {"skinny rt4 u2 w4 xd", 0, 4, 4, 2, 0, 0, 0, 2},
+    {"skinny rt4 u2 w8 xd ks", 0, 4, 8, 2, 0, 0, 0, 2, 1},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1225,13 +1335,13 @@ hipError_t allow_lds(const void* fn, size_t bytes, uint64_t& done)
     return e;
 }
 
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT>
 hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
 {
     const uint32_t G = static_cast<uint32_t>(g.K / 64);
     const uint32_t ks = g.kgroups ? (G + g.kgroups - 1) / g.kgroups : 1;
     const dim3 grid(static_cast<uint32_t>((g.N + 16 * RT - 1) / (16 * RT)), ks);
-    constexpr size_t lds = skinny_lds<CT, RT, NW, XT>();
+    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT>();
     static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(reinterpret_cast<const void*>(&gemm_skinny<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>), lds, attr_done);
     if (e != hipSuccess) return e;
@@ -1239,7 +1349,7 @@ hipError_t launch_skinny_ct(const GemmArgs& g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int SRC, bool CONTIG, int RT, int U, int NW, bool XNEAR = false, bool XT = false>
+template <int SRC, bool CONTIG, int RT, int U, int NW, bool XNEAR = false, int XT = 0>
 hipError_t launch_skinny_rt(const GemmArgs& g, hipStream_t s)
 {
     const int ct = static_cast<int>((g.M + 15) / 16);
@@ -1372,9 +1482,16 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
         if (v.rt == 1) return launch_skinny_rt<SRC, CONTIG, 1, 4, 4>(g, s);
         if (v.rt == 2 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8>(g, s);
         if (v.rt == 2) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4>(g, s);
-        if (v.xt && v.rt == 4 && v.u == 4) return launch_skinny_rt<SRC, CONTIG, 4, 4, 4, false, true>(g, s);
-        if (v.xt && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, true>(g, s);
-        if (v.xt) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4, false, true>(g, s);
+        if (v.xt == 2) {
+            if constexpr (SRC == UW_W_DIRECT) {
+                if (v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 4, 2, 8, false, 2>(g, s);
+                return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, 2>(g, s);
+            }
+            return hipErrorNotSupported;  // (rejected before: direct planes only)
+        }
+        if (v.xt && v.rt == 4 && v.u == 4) return launch_skinny_rt<SRC, CONTIG, 4, 4, 4, false, 1>(g, s);
+        if (v.xt && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, false, 1>(g, s);
+        if (v.xt) return launch_skinny_rt<SRC, CONTIG, 2, 4, 4, false, 1>(g, s);
         if (v.xnear && v.rt == 4 && v.nw == 8) return launch_skinny_rt<SRC, CONTIG, 4, 2, 8, true>(g, s);
         if (v.xnear && v.rt == 4) return launch_skinny_rt<SRC, CONTIG, 4, 2, 4, true>(g, s);
         if (v.xnear) return launch_skinny_rt<SRC, CONTIG, 2, 4, 8, true>(g, s);
@@ -1386,11 +1503,11 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
     return launch_tiled_t<SRC, CONTIG, 256, 128>(g, s);
 }
 
-template <int CT, int RT, int U, int NW, bool XNEAR, bool XT>
+template <int CT, int RT, int U, int NW, bool XNEAR, int XT>
 hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((ga.gate.N + 16 * RT - 1) / (16 * RT)));
-    constexpr size_t lds = skinny_lds<CT, RT, NW, XT>() + static_cast<size_t>(RT) * CT * 256 * 4;
+    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT>() + static_cast<size_t>(RT) * CT * 256 * 4;
     const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
     static uint64_t attr_done = 0;  // devices the LDS limit was raised on
     hipError_t e = allow_lds(fn, lds, attr_done);
@@ -1399,7 +1516,7 @@ hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int RT, int U, int NW, bool XNEAR = false, bool XT = false>
+template <int RT, int U, int NW, bool XNEAR = false, int XT = 0>
 hipError_t launch_gate_up_rt(const GateUpArgs& ga, hipStream_t s)
 {
     const int ct = static_cast<int>((ga.gate.M + 15) / 16);
@@ -1418,7 +1535,9 @@ hipError_t launch_gate_up(const GateUpArgs& ga, const Variant& v, hipStream_t s)
     // one K slice only (a "ks" variant that cuts nothing on this shape is its unsplit
     // neighbour, which has a fused form)
     if (ga.gate.kgroups || ga.up.kgroups) return hipErrorNotSupported;
-    if (v.xt && v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4, false, true>(ga, s);
+    if (v.xt == 2 && v.nw == 8) return launch_gate_up_rt<4, 2, 8, false, 2>(ga, s);
+    if (v.xt == 2) return launch_gate_up_rt<4, 2, 4, false, 2>(ga, s);
+    if (v.xt && v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4, false, 1>(ga, s);
     if (v.xt || v.xnear) return hipErrorNotSupported;
     if (v.rt == 4 && v.u == 2 && v.nw == 4) return launch_gate_up_rt<4, 2, 4>(ga, s);
     if (v.rt == 2 && v.u == 4 && v.nw == 4) return launch_gate_up_rt<2, 4, 4>(ga, s);
@@ -1590,7 +1709,10 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     const Variant& var = kVariants[v];
     // K split: Y is zeroed first (a kernel, not a memset, so the launch can be captured in
     // a graph) and every slice adds its part with fp32 atomics
-    if (g.kgroups) hipLaunchKernelGGL(zero_rows, dim3(1024), dim3(256), 0, s, g.y, g.ldy, g.M, g.N);
+    if (g.kgroups) {
+        e = launch_zero_rows(g.y, g.ldy, g.M, g.N, s);
+        if (e != hipSuccess) return fail(UW_EHIP, "zeroing Y failed: %s", hipGetErrorString(e));
+    }
     switch (p->src) {
     case UW_W_BF16: e = launch_src<UW_W_BF16, false>(g, var, s); break;
     case UW_W_EXP: e = launch_src<UW_W_EXP, false>(g, var, s); break;
@@ -1639,6 +1761,7 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
     const uw::Variant& v = uw::kVariants[variant];
     // a "ks" variant exists only where it cuts K (elsewhere it would be its unsplit neighbour)
     if (v.kind == 0 && v.ks && uw::skinny_slices(N, K, v.rt) < 2) return 0;
+    if (v.kind == 0 && v.xt == 2 && src != UW_W_DIRECT) return 0;  // X by LDS DMA: built for direct planes only
     if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }
