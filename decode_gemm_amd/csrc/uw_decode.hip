@@ -41,6 +41,7 @@ struct DecodeArgs {
     uint32_t* err;
     int64_t K;
     int64_t n_elems;
+    int64_t tiles;  // direct plane: 16-row tiles (blocks are group-major)
     uint32_t chunk, n_chunks, lmax, words;
     uint32_t max_word;  // index of the last readable stream word
     uint32_t raw_max;   // n_raw - 1 (0 when there is no raw group)
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
                 }
             }
         } else {
-            // direct plane: tile-major blocks. Item (segment s, lane group g): the 16
+            // direct plane: group-major blocks. Item (segment s, lane group g): the 16
             // sign/mantissa bytes of weights 16g..16g+15 of the segment's group, rearranged
             // as (mantissa << 1) | sign of the pair partner, and the two staged index
             // dwords of those weights, stored where MFMA lane 16g + r of the row's tile
@@ -229,7 +230,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a)
                 const int64_t fs = static_cast<int64_t>(wave_c0 + s) * a.chunk + 64 * static_cast<int64_t>(gi);
                 if (wave_c0 + s < a.n_chunks && fs < a.n_elems) {
                     const int64_t n = fs / a.K, j = (fs - n * a.K) >> 6;
-                    const int64_t blk = 1536 * ((n >> 4) * (a.K >> 6) + j);
+                    const int64_t blk = 1536 * (j * a.tiles + (n >> 4));
                     const uint32_t l = 16 * g + static_cast<uint32_t>(n & 15);
                     u32x4 v = *reinterpret_cast<const u32x4*>(a.sm + fs + 16 * g);
                     v = (v & 0x7F7F7F7Fu) << 1 | ((v << 1) & 0x01000100u) | ((v >> 15) & 0x00010001u);
@@ -334,14 +335,14 @@ __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
             carry[r] += static_cast<uint32_t>(__popcll(bal));
         }
         if (valid) {
-            uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
+            uint32_t* m = a.meta + 2 * (j * a.T + t);
             m[0] = kept;
             m[1] = first;
             if (kept != mask && a.err) atomicOr(a.err, UW_DERR_RAWINDEX);
         }
         running += total;
         if (valid && nrows < 16) {  // last tile: rows past N are zero
-            uint8_t* blk = a.blocks + 1536 * (static_cast<int64_t>(t) * a.G + j);
+            uint8_t* blk = a.blocks + 1536 * (j * a.T + t);
             for (int r = nrows; r < 16; r++)
                 for (int g = 0; g < 4; g++) {
                     *reinterpret_cast<u32x4*>(blk + 16 * (16 * g + r)) = u32x4{0, 0, 0, 0};
@@ -402,6 +403,7 @@ struct Args {
     uint8_t* out;
     uint32_t* err;
     uint32_t K, Gr, words, chunk, n_chunks, n_tasks, n_elems;
+    uint32_t tiles;       // direct plane: 16-row tiles (blocks are group-major)
     uint32_t lmax, n_words, raw_max;
     uint32_t simple;     // chunk is a power of two dividing K: a chunk's groups share one bitmap word
     uint32_t ranges[16];  // canonical rank r: first entry | length << 16 | value << 20 (length 0: unused)
@@ -829,7 +831,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t fs = el + 64 * q;
                         const uint32_t fg = fs >> 6, n = fg / a.Gr, j = fg - n * a.Gr;
-                        uint8_t* blk = a.out + 1536ull * (static_cast<uint64_t>(n >> 4) * a.Gr + j);
+                        uint8_t* blk = a.out + 1536ull * (static_cast<uint64_t>(j) * a.tiles + (n >> 4));
                         const uint32_t ll = 16 * p + (n & 15);
                         u32x4 v = smv[it];
                         v = (v & 0x7F7F7F7Fu) << 1 | ((v << 1) & 0x01000100u) | ((v >> 15) & 0x00010001u);
@@ -946,6 +948,7 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
     a.err = d_err;
     a.K = h->K;
     a.n_elems = h->N * h->K;
+    a.tiles = (h->N + 15) / 16;
     a.chunk = h->chunk;
     a.n_chunks = h->n_chunks;
     a.lmax = h->lmax;
@@ -983,6 +986,7 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
         f.err = d_err;
         f.K = static_cast<uint32_t>(h->K);
         f.Gr = static_cast<uint32_t>(h->K / 64);
+        f.tiles = static_cast<uint32_t>((h->N + 15) / 16);
         f.words = h->bitmap_words;
         f.chunk = h->chunk;
         f.n_chunks = h->n_chunks;

@@ -99,8 +99,9 @@ __device__ __forceinline__ uint32_t raw_index(const GemmArgs& a, int64_t row, ui
 //   bf16:   32 B of weights                          (stride 128 B per group)
 //   exp:    16 B sign/mantissa + 16 B exponents       (64 + 64)
 //   idx:    16 B sign/mantissa + 8 B nibbles           (64 + 32)
-//   direct: 16 B sm' + 8 B nibbles of the (tile, group) block (1536 + 1536), so a
-//           wave's loads are 1 KB and 512 B contiguous
+//   direct: 16 B sm' + 8 B nibbles of the (tile, group) block (stride 1536 T between
+//           groups: blocks are group-major), so a wave's loads are 1 KB and 512 B
+//           contiguous
 struct W16 {
     u32x4 a, b;
 };
@@ -111,6 +112,7 @@ struct Plane {
     static constexpr int S1 = SRC == UW_W_BF16 ? 128 : SRC == UW_W_IDX ? 32 : SRC == UW_W_DIRECT ? 1536 : 64;
     const uint8_t* p0;
     const uint8_t* p1;
+    int64_t s0 = S0, s1 = S1;  // bytes between consecutive groups
 
     Plane() = default;
     // lane's pointers for weights [row][16*g ..] of group 0
@@ -127,22 +129,24 @@ struct Plane {
             p0 = a.sm + row * a.K + 16 * g;
             p1 = static_cast<const uint8_t*>(a.wplane) + (row * a.K + 16 * g) / 2;
         } else {
-            // tile-major blocks: rows past N exist (zero) up to the last tile
+            // group-major blocks: rows past N exist (zero) up to the last tile
+            (void)G;
             int64_t t = row >> 4;
             t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
             const int64_t l = 16 * g + (row & 15);
-            p0 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * G) + 16 * l;
-            p1 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * G) + 1024 + 8 * l;
+            p0 = static_cast<const uint8_t*>(a.wplane) + 1536 * t + 16 * l;
+            p1 = static_cast<const uint8_t*>(a.wplane) + 1536 * t + 1024 + 8 * l;
+            s0 = s1 = 1536 * static_cast<int64_t>(a.tiles);
         }
     }
 
     __device__ __forceinline__ void load(uint32_t j, W16& w) const
     {
-        w.a = *reinterpret_cast<const u32x4*>(p0 + static_cast<int64_t>(S0) * j);
+        w.a = *reinterpret_cast<const u32x4*>(p0 + (SRC == UW_W_DIRECT ? s0 : static_cast<int64_t>(S0)) * j);
         if (SRC == UW_W_BF16 || SRC == UW_W_EXP) {
             w.b = *reinterpret_cast<const u32x4*>(p1 + static_cast<int64_t>(S1) * j + (SRC == UW_W_BF16 ? 16 : 0));
         } else {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(p1 + static_cast<int64_t>(S1) * j);
+            const u32x2 v = *reinterpret_cast<const u32x2*>(p1 + (SRC == UW_W_DIRECT ? s1 : static_cast<int64_t>(S1)) * j);
             w.b.x = v.x;
             w.b.y = v.y;
         }
@@ -158,6 +162,7 @@ struct PlaneS {
     const uint8_t* b0;
     const uint8_t* b1;
     uint32_t o0, o1;
+    int64_t s0 = S0;  // direct: bytes between consecutive groups (1536 T)
 
     PlaneS() = default;
     // tile rows [r0, r0 + 16) (r0 wave-uniform), this lane's row r0 + r, weights 16g ..
@@ -166,8 +171,9 @@ struct PlaneS {
         if (SRC == UW_W_DIRECT) {
             int64_t t = r0 >> 4;
             t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-            b0 = static_cast<const uint8_t*>(a.wplane) + 1536 * (t * (a.K >> 6));
+            b0 = static_cast<const uint8_t*>(a.wplane) + 1536 * t;
             b1 = b0;
+            s0 = 1536 * static_cast<int64_t>(a.tiles);
             const uint32_t l = 16 * g + r;
             o0 = 16 * l;
             o1 = 1024 + 8 * l;
@@ -195,8 +201,8 @@ struct PlaneS {
 
     __device__ __forceinline__ void load(uint32_t j, W16& w) const
     {
-        w.a = *reinterpret_cast<const u32x4*>(b0 + static_cast<int64_t>(S0) * j + o0);
-        const uint8_t* q = b1 + static_cast<int64_t>(S1) * j + o1;
+        w.a = *reinterpret_cast<const u32x4*>(b0 + (SRC == UW_W_DIRECT ? s0 : static_cast<int64_t>(S0)) * j + o0);
+        const uint8_t* q = b1 + (SRC == UW_W_DIRECT ? s0 : static_cast<int64_t>(S1)) * j + o1;
         if (SRC == UW_W_BF16 || SRC == UW_W_EXP) {
             w.b = *reinterpret_cast<const u32x4*>(q);
         } else {
@@ -351,7 +357,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     if (DIRECT) {
         int64_t t = (nb >> 4) + lane / LPT;
         t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-        pmeta = a.dmeta + 8 * t * G;
+        pmeta = a.dmeta + 8 * t;
     }
     // X: uniform base a.x + 64 j, lane offset of row min(16c + r, M - 1), k 16g (bytes;
     // the host keeps 2 * M * ldx below 2^32 for this kernel)
@@ -457,7 +463,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         constexpr int u = decltype(uc)::value;
         // the meta goes first: it is read half a ring turn later, and waiting for it must
         // not wait for the slot's W loads
-        if (DIRECT) mr[u % (DIRECT ? U : 1)] = *reinterpret_cast<const u32x2*>(pmeta + 8 * static_cast<int64_t>(j));
+        if (DIRECT) mr[u % (DIRECT ? U : 1)] = *reinterpret_cast<const u32x2*>(pmeta + 8 * static_cast<int64_t>(a.tiles) * j);
 #pragma unroll
         for (int i = 0; i < RT; i++) pl[i].load(j, ring[u][i]);
     };
@@ -756,9 +762,9 @@ __global__ void __launch_bounds__(256) expand_direct_kernel(GemmArgs a, uint16_t
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t G = static_cast<uint64_t>(a.K >> 6);
-    const uint64_t blk = static_cast<uint64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t * G + j
+    const uint64_t blk = static_cast<uint64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // j * T + t
     if (blk >= static_cast<uint64_t>(a.tiles) * G) return;
-    const uint64_t t = blk / G, j = blk - t * G;
+    const uint64_t j = blk / a.tiles, t = blk - j * a.tiles;
     const uint8_t* b = static_cast<const uint8_t*>(a.wplane) + 1536 * blk;
     W16 wv;
     wv.a = *reinterpret_cast<const u32x4*>(b + 16 * lane);
@@ -947,8 +953,8 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
         if (DIRECT) {
             int64_t tt = rr >> 4;
             tt = tt < static_cast<int64_t>(a.tiles) ? tt : a.tiles - 1;
-            pmeta[it] = a.dmeta + 8 * tt * G;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
+            pmeta[it] = a.dmeta + 8 * tt;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * j0);
         }
     }
     const uint16_t* xsrc[C::XITEMS];
@@ -996,8 +1002,8 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
                 israw[it] = (mcur[it].x >> (R & 15)) & 1u;
 #pragma unroll
                 for (int q = 0; q < 2; q++)
-                    rex[it][q] = *raw_exp_addr(a, mcur[it], R & 15, 2 * h + q, wpl[it][q].p0 + 1536 * static_cast<int64_t>(j));
-                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
+                    rex[it][q] = *raw_exp_addr(a, mcur[it], R & 15, 2 * h + q, a.dmeta);
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * (j + 1));
             }
             if (RAW) {
                 israw[it] = (bword[it] >> (j & 31)) & 1u;
@@ -1146,8 +1152,8 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         if (DIRECT) {
             int64_t t = (n0 >> 4) + i;
             t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-            pmeta[it] = a.dmeta + 8 * t * G;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
+            pmeta[it] = a.dmeta + 8 * t;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * j0);
         }
         const int64_t m = m0 + 16 * i + r;
         xsrc[it] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
@@ -1202,8 +1208,8 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
             if (DIRECT) {
                 const u32x2 mcur = mnext[it];
                 israw[it] = (mcur.x >> r) & 1u;
-                rex[it] = *raw_exp_addr(a, mcur, r, g, wpl[it].p0 + 1536 * static_cast<int64_t>(j));
-                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
+                rex[it] = *raw_exp_addr(a, mcur, r, g, a.dmeta);
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * (j + 1));
             }
             if (RAW) {
                 israw[it] = (bword[it] >> (j & 31)) & 1u;

@@ -164,7 +164,8 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
  * preprocessing). Decodes the Huffman stream into the direct plane d_direct
  * (uw_direct_plane_bytes, 16-byte aligned), laid out for the reconstructive GEMM's
  * operand registers. With T = ceil(N/16) row tiles and G = K/64 groups:
- *   blocks  T*G blocks of 1536 bytes, block (t, j) at 1536*(t*G + j). Lane l = 16*g + r
+ *   blocks  T*G blocks of 1536 bytes, group-major: block (t, j) at 1536*(j*T + t), so
+ *           the blocks of one 64-weight group are adjacent for all row tiles. Lane l = 16*g + r
  *           (g = 0..3, r = 0..15) of the MFMA operand owns row 16t+r, weights
  *           64j+16g .. 64j+16g+15:
  *             bytes 16l .. 16l+15    weight x: (mantissa_x << 1) | sign of weight x^1
@@ -177,12 +178,13 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
  *           The index is the position of the weight's exponent in the palette sorted by
  *           exponent value (ascending); in a raw group it is 0 and the sign/mantissa
  *           bytes are still those of the weights. Rows >= N are zero.
- *   meta    at 1536*T*G: per block two u32: a mask whose bit r says row 16t+r's group j
- *           is raw, and the side-table index of the block's first raw row.
+ *   meta    at 1536*T*G: per block, at 8*(j*T + t), two u32: a mask whose bit r says row
+ *           16t+r's group j is raw, and the side-table index of the block's first raw row.
  *   side    at 1536*T*G + round_up(8*T*G, 64) (the bytes in between are zero): 64
  *           exponent bytes per raw (row, group), ordered by tile, then group, then row.
- * A wave therefore reads one contiguous kilobyte per operand load, and a raw row only
- * swaps in its verbatim exponents. d_err as for the decoders.
+ * A wave therefore reads one contiguous kilobyte per operand load, a small-batch GEMM whose
+ * workgroups step through the groups together reads one contiguous region of the plane at
+ * a time, and a raw row only swaps in its verbatim exponents. d_err as for the decoders.
  */
 uw_status uw_prepare_direct(const uw_header* h, const void* d_blob, uint8_t* d_direct, uint32_t* d_err, void* stream);
 /*
