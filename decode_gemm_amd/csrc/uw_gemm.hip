@@ -321,13 +321,20 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // The block's tile: everything up to its reduced outputs, which go to sink(o, n, m, y) for
 // each Y element (o = the element's index in the block tile) inside [0, N) x [0, M).
 // red: the block's LDS (the cross-wave reduction, and the X tiles with XT).
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT, class Sink>
-__device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&& sink)
+// PAIR: a and a1 are the gate and up projections of one SwiGLU MLP (same shape, same X).
+// The wave's steps run over a's groups and then a1's with one ring, so a1's first groups
+// are in flight while the block reduces a's outputs into sink (after a's last group; every
+// wave takes part once, also one with no group) and restarts its accumulators; a1's
+// outputs go to sink1 at the end.
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT, bool PAIR, class Sink, class Sink1>
+__device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a1, float* red, Sink&& sink,
+                                            Sink1&& sink1)
 {
     static_assert(U % 2 == 0, "ring depth must be even");
     static_assert(!(XNEAR && XT), "one X scheme");
     constexpr bool DIRECT = SRC == UW_W_DIRECT;
     constexpr bool POSTRAW = SRC == UW_W_IDX;
+    static_assert(!(PAIR && POSTRAW), "pairs of direct planes only");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
@@ -338,6 +345,14 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     const uint32_t j0 = blockIdx.y * kgs;
     const uint32_t Gs = (j0 + kgs < G ? j0 + kgs : G) - j0;
     const uint32_t T = Gs > static_cast<uint32_t>(wave) ? (Gs - wave + NW - 1) / NW : 0;  // groups of this wave
+    const uint32_t T2 = PAIR ? 2 * T : T;                                                    // its steps
+    // step k of the wave: a1's group k - T for PAIR steps k >= T, else a's group k
+    const auto second = [&](uint32_t k) __attribute__((always_inline)) { return PAIR && k >= T; };
+    const auto jc = [&](uint32_t k) __attribute__((always_inline)) {  // the step's group (clamped to the last step)
+        k = k < T2 ? k : T2 - 1;
+        return j0 + wave + NW * (second(k) ? k - T : k);
+    };
+    const auto pick = [&](uint32_t k) __attribute__((always_inline)) -> const GemmArgs& { return second(k) ? a1 : a; };
 
     floatx4 acc[RT][CT];
 #pragma unroll
@@ -345,19 +360,23 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
 #pragma unroll
         for (int c = 0; c < CT; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    PlaneS<SRC> pl[RT];
+    PlaneS<SRC> pl[RT], pl1[PAIR ? RT : 1];
 #pragma unroll
     for (int i = 0; i < RT; i++) pl[i] = PlaneS<SRC>(a, nb + 16 * i, r, g);
+    if (PAIR) {
+#pragma unroll
+        for (int i = 0; i < RT; i++) pl1[PAIR ? i : 0] = PlaneS<SRC>(a1, nb + 16 * i, r, g);
+    }
     // direct plane: the lanes LPT i .. LPT i + LPT - 1 fetch the meta (raw-row mask, side
     // base) of row tile i, so a slot's metas are one vector load, retired in order with the
     // slot's other loads (scalar loads may return out of order and would have to be waited
     // for at once), and each lane holds the meta of the tile whose raw exponents it fetches
     constexpr int LPT = 64 / RT, RAWK = LPT / 4;
-    const uint8_t* pmeta = nullptr;
+    int64_t moff = 0;  // this lane's tile's meta in a group's row of metas
     if (DIRECT) {
         int64_t t = (nb >> 4) + lane / LPT;
         t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-        pmeta = a.dmeta + 8 * t;
+        moff = 8 * t;
     }
     // X: uniform base a.x + 64 j, lane offset of row min(16c + r, M - 1), k 16g (bytes;
     // the host keeps 2 * M * ldx below 2^32 for this kernel)
@@ -459,16 +478,30 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     // LPT i + 4k + p holds piece p of raw row k of tile i (k < RAWK)
     u32x2 mr[DIRECT ? U : 1];
     u32x4 rx[DIRECT ? U : 1];
-    auto load_slot = [&](uint32_t j, auto uc) __attribute__((always_inline)) {
+    // slot u <- step k: its metas, then its W
+    auto load_slot = [&](uint32_t k, auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
+        const uint32_t j = jc(k);
+        const bool s2nd = second(k);
         // the meta goes first: it is read half a ring turn later, and waiting for it must
         // not wait for the slot's W loads
-        if (DIRECT) mr[u % (DIRECT ? U : 1)] = *reinterpret_cast<const u32x2*>(pmeta + 8 * static_cast<int64_t>(a.tiles) * j);
+        if (DIRECT)
+            mr[u % (DIRECT ? U : 1)] =
+                *reinterpret_cast<const u32x2*>((s2nd ? a1.dmeta : a.dmeta) + moff + 8 * static_cast<int64_t>(a.tiles) * j);
 #pragma unroll
-        for (int i = 0; i < RT; i++) pl[i].load(j, ring[u][i]);
+        for (int i = 0; i < RT; i++) {
+            PlaneS<SRC> pw = pl[i];
+            if (PAIR && s2nd) {
+                pw.b0 = pl1[PAIR ? i : 0].b0;
+                pw.b1 = pl1[PAIR ? i : 0].b1;
+            }
+            pw.load(j, ring[u][i]);
+        }
     };
-    auto load_raw = [&](auto vc) __attribute__((always_inline)) {
+    // the raw exponents of slot v, which holds step ks
+    auto load_raw = [&](uint32_t ks, auto vc) __attribute__((always_inline)) {
         constexpr int v = decltype(vc)::value % (DIRECT ? U : 1);
+        const GemmArgs& a = pick(ks);
         // every lane holds the meta of its tile; a lane past the tile's raw rows, or of a
         // tile with none, reads the (always readable) meta section instead. The load is
         // always issued, so every wait in the loop stays a counted one.
@@ -482,11 +515,47 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         }
         rx[v] = *src;
     };
+    // cross-wave reduction of acc into snk: red[w][i][c][q][lane]; then output element
+    // o = ((tile * 16 + m_local) * 16 + n_local), consecutive threads on consecutive n of one
+    // Y row. The caller has made red free (a barrier after any other use of it).
+    constexpr int TILES = RT * CT;
+    float* const redp = red + (PAIR && XT == 2 ? (NW * U * CT * 2048) / 4 : 0);  // PAIR: past the X rings
+    auto reduce_into = [&](const GemmArgs& ar, auto&& snk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RT; i++)
+#pragma unroll
+            for (int c = 0; c < CT; c++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) redp[((wave * TILES + i * CT + c) * 4 + q) * 64 + lane] = acc[i][c][q];
+        __syncthreads();
+        for (int o = threadIdx.x; o < TILES * 256; o += 64 * NW) {
+            const int tile = o >> 8, ml = (o >> 4) & 15, nl = o & 15;
+            const int i = tile / CT, c = tile % CT;
+            const int src_lane = (nl >> 2) * 16 + ml, q = nl & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; w++) sum += redp[((w * TILES + tile) * 4 + q) * 64 + src_lane];
+            const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
+            if (n < ar.N && m < ar.M) snk(o, n, m, sum);
+        }
+    };
+    // PAIR, after a's last group: a's outputs to sink, a fresh start for a1. The X rings stay
+    // untouched (they are not in redp), XT 1's tiles alias it: every wave is past its own
+    // step first, and past the reads of red before anything writes it again.
+    auto mid_reduce = [&]() __attribute__((always_inline)) {
+        if (XT == 1) __syncthreads();
+        reduce_into(a, sink);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RT; i++)
+#pragma unroll
+            for (int c = 0; c < CT; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
     // one group: rebuild ring slot u (group t), refill it with group t + U, request the
     // raw exponents of group t + U/2, multiply, then refill the X pieces
     auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        const uint32_t j = j0 + wave + NW * t;
+        const GemmArgs& a = pick(t);  // (only the consumed matrix's palette and side table)
         u32x4 XF[XT ? CT : 1][2];  // XT: this step's X fragments, back from the LDS tile
         if (XT == 2) {
             // the slot's X transfer was issued before its W loads, and loads retire in
@@ -511,7 +580,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                 for (int s2 = 0; s2 < 2; s2++) XF[XT ? c : 0][s2] = xs[(16 * c + r) * XS_PITCH + 2 * g + s2];
             // the slot's X registers are free once stored: refill them first, so the X of
             // group t + U has U whole steps to arrive and is never queued behind W
-            if (!XNEAR && refill) load_x(j + NW * U, xr[XNEAR ? 0 : u]);
+            if (!XNEAR && refill) load_x(jc(t + U), xr[XNEAR ? 0 : u]);
             __builtin_amdgcn_sched_barrier(0);
         }
         u32x4 A[RT][2];
@@ -550,9 +619,9 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                 for (int i = 0; i < RT; i++)
 #pragma unroll
                     for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[0][c][s2], acc[i][c]);
-            if (refill || t + 1 < T) load_x(j + NW, xr[0]);  // unconditional in the steady state
-            if (refill) load_slot(j + NW * U, uc);
-            if (DIRECT && rawpf) load_raw(std::integral_constant<int, (u + U / 2) % U>{});
+            if (refill || t + 1 < T2) load_x(jc(t + 1), xr[0]);  // unconditional in the steady state
+            if (refill) load_slot(t + U, uc);
+            if (DIRECT && rawpf) load_raw(t + U / 2, std::integral_constant<int, (u + U / 2) % U>{});
         } else {
             // issue order is pinned: (XT: the X refill,) the raw exponents consumed half a
             // turn from now, the W slot refill (a full turn ahead), the MFMAs, the X refill;
@@ -561,10 +630,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
             if (XT == 2 && refill) {
                 // the fragment reads of this slot are done before its next X lands there
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                dma_x(j + NW * U, u);
+                dma_x(jc(t + U), u);
             }
-            if (DIRECT && rawpf) load_raw(std::integral_constant<int, (u + U / 2) % U>{});
-            if (refill) load_slot(j + NW * U, uc);
+            if (DIRECT && rawpf) load_raw(t + U / 2, std::integral_constant<int, (u + U / 2) % U>{});
+            if (refill) load_slot(t + U, uc);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++)
@@ -574,21 +643,20 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                     for (int c = 0; c < CT; c++)
                         acc[i][c] = mfma16(A[i][s2], XT ? XF[XT ? c : 0][s2] : xr[u][c][s2], acc[i][c]);
             __builtin_amdgcn_sched_barrier(0);
-            if (!XT && refill) load_x(j + NW * U, xr[u]);
+            if (!XT && refill) load_x(jc(t + U), xr[u]);
         }
+        if (PAIR && t + 1 == T) mid_reduce();  // a's last group: its outputs, while a1's first are in flight
     };
     // The ring is filled with no conditions (slots past the wave's last group reload that
     // group): the compiler's wait counts at the loop head are the minimum over every path
     // into it, so a skipped load on any path would make it wait for nearly all loads in
     // flight, once per ring turn.
+    if (PAIR && T == 0) mid_reduce();  // (a wave with no group still takes part)
     if (T > 0) {
-        const auto jc = [&](int k) __attribute__((always_inline)) {
-            return j0 + wave + NW * (static_cast<uint32_t>(k) < T ? static_cast<uint32_t>(k) : T - 1);
-        };
         [&]<int... us>(std::integer_sequence<int, us...>) {
             if constexpr (XNEAR) {
-                (load_slot(jc(us), std::integral_constant<int, us>{}), ...);
-                if (DIRECT) ((us < U / 2 ? load_raw(std::integral_constant<int, us>{}) : void()), ...);
+                (load_slot(us, std::integral_constant<int, us>{}), ...);
+                if (DIRECT) ((us < U / 2 ? load_raw(us, std::integral_constant<int, us>{}) : void()), ...);
                 load_x(jc(0), xr[0]);  // the slice's first group of this wave
             } else {
                 // the steady state's issue order: (XT: slot k's X,) the raw exponents of slot
@@ -601,9 +669,9 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
                     if (XT == 1) load_x(jc(k), xr[XNEAR ? 0 : k]);
                     if (XT == 2) dma_x(jc(k), k);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (DIRECT && k >= U / 2) load_raw(std::integral_constant<int, (k + U / 2) % U>{});
+                    if (DIRECT && k >= U / 2) load_raw(k - U / 2, std::integral_constant<int, (k + U / 2) % U>{});
                     __builtin_amdgcn_sched_barrier(0);
-                    load_slot(jc(k), kc);
+                    load_slot(k, kc);
                     __builtin_amdgcn_sched_barrier(0);
                     if (!XT) load_x(jc(k), xr[XNEAR ? 0 : k]);
                     __builtin_amdgcn_sched_barrier(0);
@@ -615,15 +683,15 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
     uint32_t t0 = 0;
     // steady state: every slot is consumed and refilled, no guards, so the compiler waits
     // for exactly the slot it needs
-    for (; t0 + 2 * U <= T; t0 += U) {
+    for (; t0 + 2 * U <= T2; t0 += U) {
         [&]<int... us>(std::integer_sequence<int, us...>) {
             (step(t0 + us, std::integral_constant<int, us>{}, true, true), ...);
         }(std::make_integer_sequence<int, U>{});
     }
     // tail: the last one or two turns of the ring
-    for (; t0 < T; t0 += U) {
+    for (; t0 < T2; t0 += U) {
         [&]<int... us>(std::integer_sequence<int, us...>) {
-            ((t0 + us < T ? step(t0 + us, std::integral_constant<int, us>{}, t0 + us + U < T, t0 + us + U / 2 < T)
+            ((t0 + us < T2 ? step(t0 + us, std::integral_constant<int, us>{}, t0 + us + U < T2, t0 + us + U / 2 < T2)
                           : void()),
              ...);
         }(std::make_integer_sequence<int, U>{});
@@ -674,61 +742,43 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, float* red, Sink&
         }
     }
 
-    // cross-wave reduction: red[w][i][c][q][lane] (XT: over the X tiles, once every wave
-    // is done with its own)
     // (XT 2: every transfer has landed, those of ring slots past the wave's last group too)
     if (XT == 2) __builtin_amdgcn_s_waitcnt(0);
     if (XT) __syncthreads();
-    constexpr int TILES = RT * CT;
-#pragma unroll
-    for (int i = 0; i < RT; i++)
-#pragma unroll
-        for (int c = 0; c < CT; c++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) red[((wave * TILES + i * CT + c) * 4 + q) * 64 + lane] = acc[i][c][q];
-    __syncthreads();
-    // output element o = ((tile * 16 + m_local) * 16 + n_local): consecutive threads write
-    // consecutive n of one Y row
-    for (int o = threadIdx.x; o < TILES * 256; o += 64 * NW) {
-        const int tile = o >> 8, ml = (o >> 4) & 15, nl = o & 15;
-        const int i = tile / CT, c = tile % CT;
-        const int src_lane = (nl >> 2) * 16 + ml, q = nl & 3;
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; w++) sum += red[((w * TILES + tile) * 4 + q) * 64 + src_lane];
-        const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
-        if (n < a.N && m < a.M) sink(o, n, m, sum);
-    }
+    reduce_into(PAIR ? a1 : a, sink1);
 }
 
 template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
 {
     extern __shared__ float red[];
-    skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT>(a, red, [&](int, int64_t n, int64_t m, float v) {
+    auto store = [&](int, int64_t n, int64_t m, float v) {
         if (a.kgroups)
             atomicAdd(a.y + m * a.ldy + n, v);  // K split: Y was zeroed, every slice adds its part
         else
             a.y[m * a.ldy + n] = v;
-    });
+    };
+    skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT, false>(a, a, red, store, store);
 }
 
 // LDS of a skinny block: the cross-wave reduction, or the X tiles (aliased): XT 1, one
-// padded tile per wave; XT 2, a ring of U DMA targets per wave.
-template <int CT, int RT, int U, int NW, int XT>
+// padded tile per wave; XT 2, a ring of U DMA targets per wave (PAIR: the rings and the
+// reduction side by side, as the rings stay in use across the mid-stream reduction).
+template <int CT, int RT, int U, int NW, int XT, bool PAIR = false>
 constexpr size_t skinny_lds()
 {
     constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
     constexpr size_t xt_bytes = XT == 1 ? static_cast<size_t>(NW) * 16 * CT * 9 * 16
                               : XT == 2 ? static_cast<size_t>(NW) * U * CT * 2048
                                         : 0;
+    if (PAIR && XT == 2) return red_bytes + xt_bytes;
     return red_bytes > xt_bytes ? red_bytes : xt_bytes;
 }
 
 // gate and up of a SwiGLU MLP in one launch (direct planes, same X, same shape): each
-// block computes its rows of gate, keeps them in LDS, computes the same rows of up, and
-// writes g, u (fp32) and h = bf16(silu(g) * u). One ramp and one tail instead of three
-// launches, and no separate SwiGLU pass over g and u.
+// block streams its rows of gate and then of up through one ring, keeps gate's outputs in
+// LDS, and writes g, u (fp32) and h = bf16(silu(g) * u). One ramp and one tail instead of
+// three launches (and no second ramp between the two), no separate SwiGLU pass.
 struct GateUpArgs {
     GemmArgs gate, up;
     uint16_t* h;
@@ -738,17 +788,19 @@ struct GateUpArgs {
 template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, int XT>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
 {
+    static_assert(CG == CU, "one palette kind for both (the launcher takes consecutive exponents only)");
     extern __shared__ float red[];
-    float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT>() / 4;  // RT * CT * 256 gate outputs
-    skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT>(ga.gate, red, [&](int o, int64_t n, int64_t m, float v) {
-        ga.gate.y[m * ga.gate.ldy + n] = v;
-        gbuf[o] = v;
-    });
-    __syncthreads();  // the up pass reuses the reduction / X-tile LDS
-    skinny_tile<UW_W_DIRECT, CU, CT, RT, U, NW, XNEAR, XT>(ga.up, red, [&](int o, int64_t n, int64_t m, float v) {
-        ga.up.y[m * ga.up.ldy + n] = v;
-        ga.h[m * ga.ldh + n] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(gbuf[o], v)));
-    });
+    float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT, true>() / 4;  // RT * CT * 256 gate outputs
+    skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT, true>(
+        ga.gate, ga.up, red,
+        [&](int o, int64_t n, int64_t m, float v) {
+            ga.gate.y[m * ga.gate.ldy + n] = v;
+            gbuf[o] = v;
+        },
+        [&](int o, int64_t n, int64_t m, float v) {
+            ga.up.y[m * ga.up.ldy + n] = v;
+            ga.h[m * ga.ldh + n] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(gbuf[o], v)));
+        });
 }
 
 // ------------------------------------------------------------------------- expand
@@ -1513,13 +1565,20 @@ template <int CT, int RT, int U, int NW, bool XNEAR, int XT>
 hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((ga.gate.N + 16 * RT - 1) / (16 * RT)));
-    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT>() + static_cast<size_t>(RT) * CT * 256 * 4;
-    const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
-    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
-    hipError_t e = allow_lds(fn, lds, attr_done);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, ga);
-    return hipGetLastError();
+    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT, true>() + static_cast<size_t>(RT) * CT * 256 * 4;
+    if constexpr (lds > 160 * 1024) {
+        (void)ga;
+        (void)s;
+        (void)grid;
+        return hipErrorNotSupported;  // (8 waves with X rings beside the reduction at M > 32)
+    } else {
+        const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
+        static uint64_t attr_done = 0;  // devices the LDS limit was raised on
+        hipError_t e = allow_lds(fn, lds, attr_done);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, ga);
+        return hipGetLastError();
+    }
 }
 
 template <int RT, int U, int NW, bool XNEAR = false, int XT = 0>
@@ -1565,6 +1624,7 @@ uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, 
         return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM takes direct planes only");
     if (gate->M != up->M || gate->h->N != up->h->N || gate->h->K != up->h->K)
         return fail(UW_ESHAPE, "gate and up must have the same M, N and K");
+    if (gate->d_x != up->d_x || gate->ldx != up->ldx) return fail(UW_EINVAL, "gate and up must read the same X");
     if (gate->M < 0) return fail(UW_ESHAPE, "M < 0");
     if (gate->M == 0) return UW_OK;
     if (gate->M > 64) return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM takes M <= 64");

@@ -249,11 +249,13 @@ int uw_split_count(int variant, int64_t N, int64_t K, int64_t M, int32_t split_k
  * SwiGLU itself in one launch (the small-batch fixed cost the post lists among the
  * reconstructive matmul's overheads, "Bundles and results" / "Trade-offs": one launch for
  * gate and up). gate and up are two uw_gemm_args as for uw_recon_gemm, both on the
- * direct plane (src UW_W_DIRECT) with the same M (1..64), N and K; each block computes its
- * rows of gate, then the same rows of up, with gate's GEMM variant. Writes gate->d_y and
+ * direct plane (src UW_W_DIRECT) with the same M (1..64), N, K and X (d_x, ldx); each
+ * block streams its rows of gate and then the same rows of up through one load ring, with
+ * gate's GEMM variant. Writes gate->d_y and
  * up->d_y (fp32, exactly what uw_recon_gemm gives with that variant) and
  * d_h[M][ldh] = bf16(silu(gate) * up), the same bits as uw_swiglu on those outputs.
- * Errors: UW_EINVAL / UW_ESHAPE as for uw_recon_gemm, and UW_EUNSUPPORTED when the fused
+ * Errors: UW_EINVAL / UW_ESHAPE as for uw_recon_gemm (UW_EINVAL also when gate and up
+ * name different X), and UW_EUNSUPPORTED when the fused
  * form does not apply (not both direct planes, M > 64, a palette whose exponents are not
  * consecutive, a variant without a fused form, or a K split); the caller then runs the
  * two GEMMs and uw_swiglu.
