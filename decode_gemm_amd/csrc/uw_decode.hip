@@ -408,6 +408,8 @@ struct Args {
     uint32_t simple;     // chunk is a power of two dividing K: a chunk's groups share one bitmap word
     uint32_t ranges[16];  // canonical rank r: first entry | length << 16 | value << 20 (length 0: unused)
     uint32_t pal[4];      // palette exponents (byte i = exponent of index i)
+    uint32_t contig;      // full / exponent: indices in value order and pal[i] = pal[0] + i, so
+    uint32_t base4;       //   an exponent is base4 + index per byte (base4 = pal[0] in every byte)
 };
 
 // Multi-code entry: values in bits 0..23, total length 24..27, count 28..30, bit 31 set
@@ -692,7 +694,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
         };
         // the task body, instantiated for each word source so that the LDS one never
         // shares a path with pending global reads
-        auto run_task = [&](auto lds_tag) {
+        auto run_task = [&](auto lds_tag, auto contig_tag) {
+            constexpr bool CONTIG = decltype(contig_tag)::value;
+            // exponent bytes of four palette indices held one per byte
+            auto exps4 = [&](uint32_t x) __attribute__((always_inline)) { return CONTIG ? x + a.base4 : pal4(x, a.pal); };
             start(lds_tag);
             const uint32_t segs = (a.chunk + kSegElems - 1) / kSegElems;
             for (uint32_t s = 0; s < segs; s++) {
@@ -763,8 +768,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                         } else {
                             const uint32_t* sp = sym_of(l, rm, g) + 2 * p;
                             const uint32_t n0 = sp[0], n1 = sp[1];
-                            const uint32_t a0 = pal4(n0 & 0x0F0F0F0Fu, a.pal), b0 = pal4((n0 >> 4) & 0x0F0F0F0Fu, a.pal);
-                            const uint32_t a1 = pal4(n1 & 0x0F0F0F0Fu, a.pal), b1 = pal4((n1 >> 4) & 0x0F0F0F0Fu, a.pal);
+                            const uint32_t a0 = exps4(n0 & 0x0F0F0F0Fu), b0 = exps4((n0 >> 4) & 0x0F0F0F0Fu);
+                            const uint32_t a1 = exps4(n1 & 0x0F0F0F0Fu), b1 = exps4((n1 >> 4) & 0x0F0F0F0Fu);
                             v = u32x4{__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
                                       __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
                         }
@@ -793,10 +798,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                         } else {
                             const uint32_t* sp = sym_of(l, rm, g) + 2 * p;
                             const uint32_t n0 = sp[0], n1 = sp[1];
-                            ea0 = pal4(n0 & 0x0F0F0F0Fu, a.pal);
-                            eb0 = pal4((n0 >> 4) & 0x0F0F0F0Fu, a.pal);
-                            ea1 = pal4(n1 & 0x0F0F0F0Fu, a.pal);
-                            eb1 = pal4((n1 >> 4) & 0x0F0F0F0Fu, a.pal);
+                            ea0 = exps4(n0 & 0x0F0F0F0Fu);
+                            eb0 = exps4((n0 >> 4) & 0x0F0F0F0Fu);
+                            ea1 = exps4(n1 & 0x0F0F0F0Fu);
+                            eb1 = exps4((n1 >> 4) & 0x0F0F0F0Fu);
                         }
                         u32x4* o = reinterpret_cast<u32x4*>(a.out + 2 * static_cast<uint64_t>(e));
                         o[0] = piece_from_split(ea0, eb0, smv[it].x, smv[it].y);
@@ -852,10 +857,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 wave_sync();
             }
         };
-        if (in_lds)
-            run_task(std::true_type{});
-        else
-            run_task(std::false_type{});
+        // (full and exponent outputs: the exponents of a palette of consecutive values are
+        // one byte-wise add, so the write-out comes in a second form for it)
+        if (in_lds) {
+            if ((MODE == DEC_FULL || MODE == DEC_EXP) && a.contig)
+                run_task(std::true_type{}, std::true_type{});
+            else
+                run_task(std::true_type{}, std::false_type{});
+        } else {
+            if ((MODE == DEC_FULL || MODE == DEC_EXP) && a.contig)
+                run_task(std::false_type{}, std::true_type{});
+            else
+                run_task(std::false_type{}, std::false_type{});
+        }
         if (active) {
             const uint32_t consumed = (wp - (pos0 >> 5)) * 32 - (pos0 & 31) - static_cast<uint32_t>(nb);
             uint32_t bits = (err & kEntErr) ? UW_DERR_BADCODE : 0u;
@@ -995,13 +1009,17 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
         f.lmax = h->lmax;
         f.n_words = static_cast<uint32_t>(h->bytes_stream / 4);
         f.raw_max = a.raw_max;
+        // symbol values: the direct plane takes value-ordered indices; full and exponent
+        // decode too when the palette's exponents are consecutive (then an exponent is
+        // base + index); the index plane keeps the header's order
         uint8_t vmap[16];
         for (int i = 0; i < 16; i++) vmap[i] = static_cast<uint8_t>(i);
-        if (mode == DEC_DIRECT) {
-            ValueOrder vo;
-            value_order(h, &vo);
-            std::memcpy(vmap, vo.order, 16);
-        }
+        ValueOrder vo;
+        value_order(h, &vo);
+        const bool contig = (mode == DEC_FULL || mode == DEC_EXP) && vo.contiguous;
+        if (mode == DEC_DIRECT || contig) std::memcpy(vmap, vo.order, 16);
+        f.contig = contig ? 1u : 0u;
+        f.base4 = vo.sorted[0] * 0x01010101u;
         // the canonical codes in rank order: code of rank first_index[l] + k is first_code[l] + k
         for (uint32_t l = 1, r = 0; l <= h->lmax; l++)
             for (uint32_t k = 0; k < t.count[l] && r < 16; k++, r++)
