@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(256) direct_meta_kernel(MetaArgs a)
             carry[r] += static_cast<uint32_t>(__popcll(bal));
         }
         if (valid) {
-            uint32_t* m = a.meta + 2 * (j * a.T + t);
+            uint32_t* m = a.meta + 2 * (static_cast<int64_t>(t) * a.G + j);
             m[0] = kept;
             m[1] = first;
             if (kept != mask && a.err) atomicOr(a.err, UW_DERR_RAWINDEX);

@@ -372,11 +372,11 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     // slot's other loads (scalar loads may return out of order and would have to be waited
     // for at once), and each lane holds the meta of the tile whose raw exponents it fetches
     constexpr int LPT = 64 / RT, RAWK = LPT / 4;
-    int64_t moff = 0;  // this lane's tile's meta in a group's row of metas
+    int64_t moff = 0;  // this lane's tile's row of metas (tile-major: consecutive groups adjacent)
     if (DIRECT) {
         int64_t t = (nb >> 4) + lane / LPT;
         t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-        moff = 8 * t;
+        moff = 8 * t * G;
     }
     // X: uniform base a.x + 64 j, lane offset of row min(16c + r, M - 1), k 16g (bytes;
     // the host keeps 2 * M * ldx below 2^32 for this kernel)
@@ -487,7 +487,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
         // not wait for the slot's W loads
         if (DIRECT)
             mr[u % (DIRECT ? U : 1)] =
-                *reinterpret_cast<const u32x2*>((s2nd ? a1.dmeta : a.dmeta) + moff + 8 * static_cast<int64_t>(a.tiles) * j);
+                *reinterpret_cast<const u32x2*>((s2nd ? a1.dmeta : a.dmeta) + moff + 8 * static_cast<int64_t>(j));
 #pragma unroll
         for (int i = 0; i < RT; i++) {
             PlaneS<SRC> pw = pl[i];
@@ -825,7 +825,7 @@ __global__ void __launch_bounds__(256) expand_direct_kernel(GemmArgs a, uint16_t
     wv.b.y = v.y;
     wv.b.z = 0;
     wv.b.w = 0;
-    const u32x2 meta = *reinterpret_cast<const u32x2*>(a.dmeta + 8 * blk);
+    const u32x2 meta = *reinterpret_cast<const u32x2*>(a.dmeta + 8 * (t * G + j));
     const int r = static_cast<int>(lane & 15), g = static_cast<int>(lane >> 4);
     u32x4 p0, p1;
     rebuild16<UW_W_DIRECT, CONTIG>(a, wv, p0, p1);
@@ -1005,8 +1005,8 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
         if (DIRECT) {
             int64_t tt = rr >> 4;
             tt = tt < static_cast<int64_t>(a.tiles) ? tt : a.tiles - 1;
-            pmeta[it] = a.dmeta + 8 * tt;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * j0);
+            pmeta[it] = a.dmeta + 8 * tt * G;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
         }
     }
     const uint16_t* xsrc[C::XITEMS];
@@ -1055,7 +1055,7 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
 #pragma unroll
                 for (int q = 0; q < 2; q++)
                     rex[it][q] = *raw_exp_addr(a, mcur[it], R & 15, 2 * h + q, a.dmeta);
-                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * (j + 1));
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
             }
             if (RAW) {
                 israw[it] = (bword[it] >> (j & 31)) & 1u;
@@ -1204,8 +1204,8 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
         if (DIRECT) {
             int64_t t = (n0 >> 4) + i;
             t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
-            pmeta[it] = a.dmeta + 8 * t;
-            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * j0);
+            pmeta[it] = a.dmeta + 8 * t * G;
+            mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j0));
         }
         const int64_t m = m0 + 16 * i + r;
         xsrc[it] = a.x + (m < a.M ? m : a.M - 1) * a.ldx + 16 * g;
@@ -1261,7 +1261,7 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
                 const u32x2 mcur = mnext[it];
                 israw[it] = (mcur.x >> r) & 1u;
                 rex[it] = *raw_exp_addr(a, mcur, r, g, a.dmeta);
-                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(a.tiles) * (j + 1));
+                if (j + 1 < G) mnext[it] = *reinterpret_cast<const u32x2*>(pmeta[it] + 8 * static_cast<int64_t>(j + 1));
             }
             if (RAW) {
                 israw[it] = (bword[it] >> (j & 31)) & 1u;

@@ -178,8 +178,9 @@ uw_status uw_transcode_palette(const uw_header* h, const void* d_blob, uint8_t* 
  *           The index is the position of the weight's exponent in the palette sorted by
  *           exponent value (ascending); in a raw group it is 0 and the sign/mantissa
  *           bytes are still those of the weights. Rows >= N are zero.
- *   meta    at 1536*T*G: per block, at 8*(j*T + t), two u32: a mask whose bit r says row
- *           16t+r's group j is raw, and the side-table index of the block's first raw row.
+ *   meta    at 1536*T*G: per block, at 8*(t*G + j) (tile-major: a row tile's metas are
+ *           adjacent), two u32: a mask whose bit r says row 16t+r's group j is raw, and the
+ *           side-table index of the block's first raw row.
  *   side    at 1536*T*G + round_up(8*T*G, 64) (the bytes in between are zero): 64
  *           exponent bytes per raw (row, group), ordered by tile, then group, then row.
  * A wave therefore reads one contiguous kilobyte per operand load, a small-batch GEMM whose

@@ -19,12 +19,12 @@ def plane_bytes(N: int, K: int, n_raw: int) -> int:
 
 
 def _sections(plane: np.ndarray, N: int, K: int):
-    """Blocks and metas are stored group-major (block (t, j) at j*T + t); they are
-    returned indexed [t][j]."""
+    """Blocks are stored group-major (block (t, j) at j*T + t), metas tile-major (at
+    t*G + j); both are returned indexed [t][j]."""
     T, G = (N + 15) // 16, K // 64
     nb = 1536 * T * G
     blocks = plane[:nb].reshape(G, T, 1536).transpose(1, 0, 2)
-    meta = plane[nb: nb + 8 * T * G].view("<u4").reshape(G, T, 2).transpose(1, 0, 2)
+    meta = plane[nb: nb + 8 * T * G].view("<u4").reshape(T, G, 2)
     pad = plane[nb + 8 * T * G: nb + (8 * T * G + 63) // 64 * 64]
     side = plane[nb + (8 * T * G + 63) // 64 * 64:].reshape(-1, 64)
     return T, G, blocks, meta, pad, side
