@@ -201,9 +201,32 @@ class Stack:
         return uw.mlp_layers(rows)
 
 
+def fusable_mask(uw, torch, dev, stack, M):
+    """Bit v set: the fused gate/up/SwiGLU launch takes variant v (with the variant's own K
+    split) at M -- found by launching it once with each on layer 0."""
+    K, N = stack.K, stack.Nff
+    x = torch.zeros(M, K, dtype=torch.int16, device=dev)
+    g = torch.empty(M, N, dtype=torch.float32, device=dev)
+    u = torch.empty_like(g)
+    h = torch.empty(M * N, dtype=torch.int16, device=dev)
+    mask = 0
+    for v in range(uw.variant_count()):
+        try:
+            uw.recon_gemm_gate_up(stack.h[0][0], stack.blob[0][0], stack.plane[0][0], stack.h[0][1], stack.blob[0][1],
+                                  stack.plane[0][1], x, g, u, h, M, variant=v, split_k=0)
+            mask |= 1 << v
+        except uw.UwError as e:
+            if e.status != uw.EUNSUPPORTED:
+                raise
+    torch.cuda.synchronize()
+    return mask
+
+
 def tune_plans(uw, synth, torch, dev, stack, Ms, log):
     """uw_autotune per (M, role) with the 32 layers of that role as its rotation set, every
-    pipeline, variant and K split; up runs on gate's plan (same shape and statistics)."""
+    pipeline, variant and K split; up runs on gate's plan (same shape and statistics). For
+    M <= 64 the stack forward runs gate, up and the SwiGLU as one launch, so gate's plan is
+    chosen among the variants that launch takes (with their own K split)."""
     plans = {}
     for M in Ms:
         plans[M] = {}
@@ -213,9 +236,12 @@ def tune_plans(uw, synth, torch, dev, stack, Ms, log):
             y = torch.empty(M, h0.N, dtype=torch.float32, device=dev)
             ws = torch.empty(uw.workspace_bytes(h0, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
             reps, trials = (10, 3) if M <= 64 else (3, 2) if M <= 1024 else (2, 2)
+            fused = role == "gate" and M <= 64
+            vmask = fusable_mask(uw, torch, dev, stack, M) if fused else 0
             t0 = time.time()
             pl = uw.autotune(h0, stack.blob[0][q], x, y, [M], d_ws=ws, ws_bytes=ws.numel(), reps=reps, warmup=1,
-                             trials=trials, rot=stack.rot(uw, q), tune_split=True)[0]
+                             trials=trials, rot=stack.rot(uw, q), tune_split=not fused,
+                             pipeline_mask=(1 << uw.PIPE_DIRECT) if fused else 0, variant_mask=vmask)[0]
             plans[M][role] = {"pipeline": pl.pipeline, "variant": pl.variant, "split_k": pl.split_k, "t_ms": pl.t_ms}
             log(f"[bench] plan M={M} {role}: {uw.PIPELINE_NAMES[pl.pipeline]} / {uw.variant_name(pl.variant)} / "
                 f"split {pl.split_k}: {pl.t_ms * 1e3:.1f} us ({time.time() - t0:.1f}s)")
@@ -273,19 +299,42 @@ def step_ops(uw, torch, dev, stack, plans_m, M, x, bufs):
     return ops
 
 
-def time_op(torch, stream, stack, fn, reps):
+def time_op(torch, stream, stack, fn, reps, graph=False):
     """Mean duration (ms) of fn(layer) launched back to back over the layers, `reps` times
-    round, between two HIP events on the launch stream."""
+    round, between two HIP events on the launch stream. graph: also replay the 32 launches
+    from a HIP graph (fn must launch on the current stream), so that a launch shorter than
+    the Python call that issues it is not timed at the call's pace; the lower of the two is
+    returned."""
     for l in range(stack.L):
         fn(l)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for r in range(reps):
+    torch.cuda.synchronize()
+
+    def timed(run):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(reps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * stack.L)
+
+    def eager():
         for l in range(stack.L):
             fn(l)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / (reps * stack.L)
+
+    ms = timed(eager)
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for l in range(stack.L):
+                    fn(l)
+            g.replay()
+            torch.cuda.synchronize()
+            ms = min(ms, timed(g.replay))
+        except Exception as e:  # (eager timing stands)
+            print(f"[bench] graph timing unavailable: {e}", file=sys.stderr, flush=True)
+    return ms
 
 
 def main():
@@ -367,7 +416,7 @@ def main():
         yd = torch.empty(M, K, dtype=torch.float32, device=dev)
         wsp = torch.empty(uw.workspace_bytes(stack.h[0][0], uw.PIPE_FULL), dtype=torch.uint8, device=dev)
         for name, plan, fn, nbytes in step_ops(uw, torch, dev, stack, plans[M], M, xs[M], (g, u, hbuf, yd, wsp)):
-            ms = time_op(torch, stream, stack, fn, max(3, args.steps // 2))
+            ms = time_op(torch, stream, stack, fn, max(3, args.steps // 2), graph=True)
             pipe = uw.PIPELINE_NAMES[plan["pipeline"]] if plan else "-"
             var = uw.variant_name(plan["variant"]) if plan else "-"
             split = plan["split_k"] if plan else 1
@@ -478,7 +527,7 @@ def large_m(uw, synth, torch, dev, stream, stack, plans, log):
             fn = lambda l: uw.run_pipeline(p["pipeline"], stack.h[l][q], stack.blob[l][q], xin, out, M,
                                            d_direct=stack.plane[l][q], d_ws=wsp, ws_bytes=wsp.numel(),
                                            variant=p["variant"], split_k=p["split_k"])
-            oms = time_op(torch, stream, stack, fn, 1)
+            oms = time_op(torch, stream, stack, fn, 1, graph=True)
             otf = 2.0 * M * N * Kin / (oms * 1e-3) / 1e12
             row[role] = {"us": round(oms * 1e3, 1), "tflops": round(otf, 1), "mfma_frac": round(otf / BF16_PEAK_TFLOPS, 4)}
         del g, hb, wsp, x, y
