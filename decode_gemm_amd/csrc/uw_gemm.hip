@@ -783,6 +783,9 @@ struct GateUpArgs {
     GemmArgs gate, up;
     uint16_t* h;
     int64_t ldh;
+    float* zy;  // (or null) a Y that the blocks clear first: zM rows of zN floats, zld apart
+    int64_t zld;
+    uint32_t zM, zN;
 };
 
 template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, int XT>
@@ -790,6 +793,19 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
 {
     static_assert(CG == CU, "one palette kind for both (the launcher takes consecutive exponents only)");
     extern __shared__ float red[];
+    if (ga.zy) {
+        // the Y of the K-split launch that comes next on the stream, cleared here (16-byte
+        // stores; the host checked alignment) instead of by a launch of its own
+        const uint32_t n4 = (ga.zN + 3) / 4, units = ga.zM * n4;
+        for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < units; q += gridDim.x * blockDim.x) {
+            const uint32_t m = q / n4, n = 4 * (q - m * n4);
+            float* row = ga.zy + static_cast<int64_t>(m) * ga.zld + n;
+            if (n + 4 <= ga.zN)
+                *reinterpret_cast<floatx4*>(row) = floatx4{0.f, 0.f, 0.f, 0.f};
+            else
+                for (uint32_t c = 0; n + c < ga.zN; c++) row[c] = 0.f;
+        }
+    }
     float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT, true>() / 4;  // RT * CT * 256 gate outputs
     skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT, true>(
         ga.gate, ga.up, red,
@@ -1616,7 +1632,7 @@ hipError_t launch_gate_up(const GateUpArgs& ga, const Variant& v, hipStream_t s)
 uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v);
 
 uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
-                              void* stream)
+                              void* stream, const ZeroTarget* clear)
 {
     clear_error();
     if (!gate || !up || !gate->h || !up->h) return fail(UW_EINVAL, "NULL argument");
@@ -1642,6 +1658,17 @@ uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, 
     if (!cg || !cu) return fail(UW_EUNSUPPORTED, "the fused gate/up GEMM needs palettes of consecutive exponents");
     ga.h = d_h;
     ga.ldh = ldh;
+    ga.zy = nullptr;
+    ga.zld = 0;
+    ga.zM = ga.zN = 0;
+    if (clear && clear->y && clear->M > 0 && clear->N > 0) {
+        if (!aligned(clear->y, 16) || clear->ld % 4 || clear->ld < clear->N || clear->M * ((clear->N + 3) / 4) >= (int64_t{1} << 32))
+            return fail(UW_EINVAL, "bad Y to clear");
+        ga.zy = clear->y;
+        ga.zld = clear->ld;
+        ga.zM = static_cast<uint32_t>(clear->M);
+        ga.zN = static_cast<uint32_t>(clear->N);
+    }
     const hipError_t e = launch_gate_up(ga, kVariants[vg], static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(UW_EUNSUPPORTED, "variant %d has no fused gate/up form", vg);
     if (e != hipSuccess) return fail(UW_EHIP, "gate/up launch failed: %s", hipGetErrorString(e));
@@ -1759,7 +1786,7 @@ uw_status launch_expand_direct(const uw_header* h, const uint8_t* d_direct, uint
     return UW_OK;
 }
 
-uw_status launch_gemm(const uw_gemm_args* p, void* stream)
+uw_status launch_gemm(const uw_gemm_args* p, void* stream, bool y_zeroed)
 {
     clear_error();
     if (!p || !p->h) return fail(UW_EINVAL, "NULL argument");
@@ -1775,7 +1802,7 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream)
     const Variant& var = kVariants[v];
     // K split: Y is zeroed first (a kernel, not a memset, so the launch can be captured in
     // a graph) and every slice adds its part with fp32 atomics
-    if (g.kgroups) {
+    if (g.kgroups && !y_zeroed) {
         e = launch_zero_rows(g.y, g.ldy, g.M, g.N, s);
         if (e != hipSuccess) return fail(UW_EHIP, "zeroing Y failed: %s", hipGetErrorString(e));
     }

@@ -53,9 +53,16 @@ enum DecodeMode { DEC_FULL = 0, DEC_EXP = 1, DEC_IDX = 2, DEC_DIRECT = 3 };
 constexpr int kPipelines = 5;  // uw_pipeline values 0 .. kPipelines - 1
 uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int mode, uint32_t* d_err,
                         void* stream);
-uw_status launch_gemm(const uw_gemm_args* a, void* stream);
+// y_zeroed: the caller has already cleared Y (a K-split launch then skips its own clearing)
+uw_status launch_gemm(const uw_gemm_args* a, void* stream, bool y_zeroed = false);
+// An fp32 buffer Y[M][ld] (first N columns) that a fused gate/up launch clears on the way, for
+// the K-split launch that follows it on the same stream (16-byte aligned, ld a multiple of 4).
+struct ZeroTarget {
+    float* y;
+    int64_t ld, M, N;
+};
 uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, uint16_t* d_h, int64_t ldh,
-                              void* stream);
+                              void* stream, const ZeroTarget* clear = nullptr);
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src);
 uint32_t cu_count();  // compute units of the current device
 uint32_t stream_cu_count(void* stream);  // compute units a hipStream_t may use (its CU mask)

@@ -406,7 +406,7 @@ uw_status decode_proj(const uw_proj& p, void* slot, void* stream)
 
 // The GEMM of a projection whose plane is ready (in `slot`, or the direct plane).
 uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
-                    void* stream)
+                    void* stream, bool y_zeroed = false)
 {
     uw_gemm_args g;
     std::memset(&g, 0, sizeof g);
@@ -422,13 +422,13 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     g.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
           : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
     g.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
-    return uw_recon_gemm(&g, stream);
+    return launch_gemm(&g, stream, y_zeroed);
 }
 
 // gate, up and SwiGLU of a layer in one launch when both projections are direct planes
 // and the fused form applies; UW_EUNSUPPORTED otherwise (the caller runs them one by one).
 uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const uint16_t* x, int64_t ldx, float* g,
-                        float* u, uint16_t* h, int64_t ldf, void* stream)
+                        float* u, uint16_t* h, int64_t ldf, void* stream, const ZeroTarget* clear = nullptr)
 {
     if (gp.pipeline != UW_PIPE_DIRECT || up.pipeline != UW_PIPE_DIRECT || M > 64) return UW_EUNSUPPORTED;
     uw_gemm_args a[2];
@@ -448,7 +448,7 @@ uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const u
         a[q].variant = pr[q]->variant;
         a[q].split_k = pr[q]->split_k;
     }
-    return uw_recon_gemm_gate_up(&a[0], &a[1], h, ldf, stream);
+    return launch_gate_up_gemm(&a[0], &a[1], h, ldf, stream, clear);
 }
 
 // ---- the schedule of a forward with a decode stream
@@ -549,9 +549,12 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
             ldy = lay.Nff;
         }
     };
-    // gate, up and SwiGLU of a layer whose gate and up are direct planes
-    auto direct_pair = [&](const uw_mlp_layer& L, void* s) -> uw_status {
-        uw_status r = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, s);
+    // gate, up and SwiGLU of a layer whose gate and up are direct planes; with `clear`, the
+    // fused launch also clears that Y (*cleared tells whether it ran)
+    auto direct_pair = [&](const uw_mlp_layer& L, void* s, const ZeroTarget* clear = nullptr,
+                           bool* cleared = nullptr) -> uw_status {
+        uw_status r = gate_up_fused(L.gate, L.up, M, d_x, lay.K, g, u, h, lay.Nff, s, clear);
+        if (cleared) *cleared = r == UW_OK && clear;
         if (r != UW_EUNSUPPORTED) return r;
         clear_error();
         if ((r = gemm_proj(L.gate, nullptr, M, d_x, lay.K, g, lay.Nff, s)) != UW_OK) return r;
@@ -562,8 +565,14 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
     if (!decode_stream) {
         for (int l = 0; l < n_layers && st == UW_OK; l++) {
             const uw_mlp_layer& L = layers[l];
+            // a K-split down adds into Y: the fused gate/up launch before it clears Y, which
+            // saves the split launch a clearing launch of its own
+            const bool split_down =
+                lay.Nout % 4 == 0 && uw_split_count(L.down.variant, lay.Nout, lay.Nff, M, L.down.split_k) > 1;
+            const ZeroTarget clear_y = {d_y, lay.Nout, M, lay.Nout};
+            bool cleared = false;
             if (both_direct(L, M)) {
-                st = direct_pair(L, stream);
+                st = direct_pair(L, stream, split_down ? &clear_y : nullptr, &cleared);
             } else {
                 for (int r = 0; r < 2 && st == UW_OK; r++) {
                     const uint16_t* x;
@@ -577,7 +586,7 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
             }
             if (st != UW_OK) break;
             if ((st = decode_proj(L.down, slot(0), stream)) != UW_OK) break;
-            st = gemm_proj(L.down, slot(0), M, h, lay.Nff, d_y, lay.Nout, stream);
+            st = gemm_proj(L.down, slot(0), M, h, lay.Nff, d_y, lay.Nout, stream, cleared);
         }
         return st;
     }
