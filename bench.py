@@ -222,26 +222,54 @@ def fusable_mask(uw, torch, dev, stack, M):
     return mask
 
 
+def tune_fused(uw, torch, dev, stack, M, vmask, stream):
+    """The fused gate/up/SwiGLU launch's variant at M: each variant in vmask timed as the
+    stack runs it (the 32 layers back to back, HIP-graph replay), the fastest kept.
+    Returns (variant, ms per launch)."""
+    K, N = stack.K, stack.Nff
+    x = torch.from_numpy(np.zeros((M, K), np.int16)).to(dev)
+    g = torch.empty(M, N, dtype=torch.float32, device=dev)
+    u = torch.empty_like(g)
+    h = torch.empty(M * N, dtype=torch.int16, device=dev)
+    best = (None, float("inf"))
+    for v in range(uw.variant_count()):
+        if not (vmask >> v) & 1:
+            continue
+        fn = (lambda v: lambda l: uw.recon_gemm_gate_up(
+            stack.h[l][0], stack.blob[l][0], stack.plane[l][0], stack.h[l][1], stack.blob[l][1], stack.plane[l][1], x,
+            g, u, h, M, variant=v, split_k=0))(v)
+        ms = min(time_op(torch, stream, stack, fn, 3, graph=True) for _ in range(2))
+        if ms < best[1]:
+            best = (v, ms)
+    return best
+
+
 def tune_plans(uw, synth, torch, dev, stack, Ms, log):
     """uw_autotune per (M, role) with the 32 layers of that role as its rotation set, every
     pipeline, variant and K split; up runs on gate's plan (same shape and statistics). For
     M <= 64 the stack forward runs gate, up and the SwiGLU as one launch, so gate's plan is
-    chosen among the variants that launch takes (with their own K split)."""
+    that launch's: direct planes, the variant under which the fused launch itself runs
+    fastest (one K slice)."""
     plans = {}
+    stream = torch.cuda.current_stream()
     for M in Ms:
         plans[M] = {}
         for role, q in (("gate", 0), ("down", 2)):
             h0 = stack.h[0][q]
+            t0 = time.time()
+            if role == "gate" and M <= 64:
+                v, ms = tune_fused(uw, torch, dev, stack, M, fusable_mask(uw, torch, dev, stack, M), stream)
+                if v is not None:
+                    plans[M][role] = {"pipeline": uw.PIPE_DIRECT, "variant": v, "split_k": 0, "t_ms": ms}
+                    log(f"[bench] plan M={M} gate+up fused: direct / {uw.variant_name(v)}: {ms * 1e3:.1f} us "
+                        f"({time.time() - t0:.1f}s)")
+                    continue
             x = torch.from_numpy(synth.gen_x(stack.cfg, M, h0.K).view(np.int16)).to(dev)
             y = torch.empty(M, h0.N, dtype=torch.float32, device=dev)
             ws = torch.empty(uw.workspace_bytes(h0, uw.PIPE_FULL), dtype=torch.uint8, device=dev)
             reps, trials = (10, 3) if M <= 64 else (3, 2) if M <= 1024 else (2, 2)
-            fused = role == "gate" and M <= 64
-            vmask = fusable_mask(uw, torch, dev, stack, M) if fused else 0
-            t0 = time.time()
             pl = uw.autotune(h0, stack.blob[0][q], x, y, [M], d_ws=ws, ws_bytes=ws.numel(), reps=reps, warmup=1,
-                             trials=trials, rot=stack.rot(uw, q), tune_split=not fused,
-                             pipeline_mask=(1 << uw.PIPE_DIRECT) if fused else 0, variant_mask=vmask)[0]
+                             trials=trials, rot=stack.rot(uw, q))[0]
             plans[M][role] = {"pipeline": pl.pipeline, "variant": pl.variant, "split_k": pl.split_k, "t_ms": pl.t_ms}
             log(f"[bench] plan M={M} {role}: {uw.PIPELINE_NAMES[pl.pipeline]} / {uw.variant_name(pl.variant)} / "
                 f"split {pl.split_k}: {pl.t_ms * 1e3:.1f} us ({time.time() - t0:.1f}s)")

@@ -322,11 +322,13 @@ __device__ __forceinline__ void raw_pieces(const GemmArgs& a, int64_t row, uint3
 // each Y element (o = the element's index in the block tile) inside [0, N) x [0, M).
 // red: the block's LDS (the cross-wave reduction, and the X tiles with XT).
 // PAIR: a and a1 are the gate and up projections of one SwiGLU MLP (same shape, same X).
-// The wave's steps run over a's groups and then a1's with one ring, so a1's first groups
-// are in flight while the block reduces a's outputs into sink (after a's last group; every
-// wave takes part once, also one with no group) and restarts its accumulators; a1's
-// outputs go to sink1 at the end.
-template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT, bool PAIR, class Sink, class Sink1>
+// PAIR 1: the wave's steps run over a's groups and then a1's with one ring, so a1's first
+// groups are in flight while the block reduces a's outputs into sink (after a's last group;
+// every wave takes part once, also one with no group) and restarts its accumulators; a1's
+// outputs go to sink1 at the end. PAIR 2: every step takes group j of both (2 RT row tiles
+// per slot: a's, then a1's), so each X group is fetched once for both matrices; at the end
+// each output element goes to sink (a's value) and then sink1 (a1's), in one thread.
+template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT, int PAIR, class Sink, class Sink1>
 __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a1, float* red, Sink&& sink,
                                             Sink1&& sink1)
 {
@@ -335,6 +337,8 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     constexpr bool DIRECT = SRC == UW_W_DIRECT;
     constexpr bool POSTRAW = SRC == UW_W_IDX;
     static_assert(!(PAIR && POSTRAW), "pairs of direct planes only");
+    constexpr bool SEQ = PAIR == 1, IL = PAIR == 2;
+    constexpr int RTT = IL ? 2 * RT : RT;  // row tiles per ring slot
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
@@ -345,18 +349,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     const uint32_t j0 = blockIdx.y * kgs;
     const uint32_t Gs = (j0 + kgs < G ? j0 + kgs : G) - j0;
     const uint32_t T = Gs > static_cast<uint32_t>(wave) ? (Gs - wave + NW - 1) / NW : 0;  // groups of this wave
-    const uint32_t T2 = PAIR ? 2 * T : T;                                                    // its steps
-    // step k of the wave: a1's group k - T for PAIR steps k >= T, else a's group k
-    const auto second = [&](uint32_t k) __attribute__((always_inline)) { return PAIR && k >= T; };
+    const uint32_t T2 = SEQ ? 2 * T : T;                                                     // its steps
+    // step k of the wave: a1's group k - T for PAIR 1 steps k >= T, else group k
+    const auto second = [&](uint32_t k) __attribute__((always_inline)) { return SEQ && k >= T; };
     const auto jc = [&](uint32_t k) __attribute__((always_inline)) {  // the step's group (clamped to the last step)
         k = k < T2 ? k : T2 - 1;
         return j0 + wave + NW * (second(k) ? k - T : k);
     };
     const auto pick = [&](uint32_t k) __attribute__((always_inline)) -> const GemmArgs& { return second(k) ? a1 : a; };
 
-    floatx4 acc[RT][CT];
+    floatx4 acc[RTT][CT];
 #pragma unroll
-    for (int i = 0; i < RT; i++)
+    for (int i = 0; i < RTT; i++)
 #pragma unroll
         for (int c = 0; c < CT; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -371,13 +375,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     // base) of row tile i, so a slot's metas are one vector load, retired in order with the
     // slot's other loads (scalar loads may return out of order and would have to be waited
     // for at once), and each lane holds the meta of the tile whose raw exponents it fetches
-    constexpr int LPT = 64 / RT, RAWK = LPT / 4;
+    // (PAIR 2: lanes past LPT RT hold a1's tiles, with a1's metas and side table)
+    constexpr int LPT = 64 / RTT, RAWK = LPT / 4;
     int64_t moff = 0;  // this lane's tile's row of metas (tile-major: consecutive groups adjacent)
+    const bool lane2nd = IL && lane / LPT >= RT;
     if (DIRECT) {
-        int64_t t = (nb >> 4) + lane / LPT;
+        int64_t t = (nb >> 4) + lane / LPT - (lane2nd ? RT : 0);
         t = t < static_cast<int64_t>(a.tiles) ? t : a.tiles - 1;
         moff = 8 * t * G;
     }
+    const uint8_t* const lmeta = lane2nd ? a1.dmeta : a.dmeta;
+    const uint8_t* const lside = lane2nd ? a1.dside : a.dside;
+    const uint32_t lraw_max = lane2nd ? a1.raw_max : a.raw_max;
     // X: uniform base a.x + 64 j, lane offset of row min(16c + r, M - 1), k 16g (bytes;
     // the host keeps 2 * M * ldx below 2^32 for this kernel)
     uint32_t xoff[CT];
@@ -472,7 +481,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
             }
         }
     };
-    W16 ring[U][RT];
+    W16 ring[U][RTT];
     u32x4 xr[XNEAR ? 1 : U][CT][2];
     // direct plane: the slot's metas, and one load of raw exponents per slot: lane
     // LPT i + 4k + p holds piece p of raw row k of tile i (k < RAWK)
@@ -487,13 +496,13 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
         // not wait for the slot's W loads
         if (DIRECT)
             mr[u % (DIRECT ? U : 1)] =
-                *reinterpret_cast<const u32x2*>((s2nd ? a1.dmeta : a.dmeta) + moff + 8 * static_cast<int64_t>(j));
+                *reinterpret_cast<const u32x2*>((IL ? lmeta : s2nd ? a1.dmeta : a.dmeta) + moff + 8 * static_cast<int64_t>(j));
 #pragma unroll
-        for (int i = 0; i < RT; i++) {
-            PlaneS<SRC> pw = pl[i];
-            if (PAIR && s2nd) {
-                pw.b0 = pl1[PAIR ? i : 0].b0;
-                pw.b1 = pl1[PAIR ? i : 0].b1;
+        for (int i = 0; i < RTT; i++) {
+            PlaneS<SRC> pw = pl[i % RT];
+            if ((SEQ && s2nd) || (IL && i >= RT)) {
+                pw.b0 = pl1[PAIR ? i % RT : 0].b0;
+                pw.b1 = pl1[PAIR ? i % RT : 0].b1;
             }
             pw.load(j, ring[u][i]);
         }
@@ -507,22 +516,25 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
         // always issued, so every wait in the loop stays a counted one.
         const int k = (lane % LPT) >> 2, p4 = lane & 3;
         const uint32_t mx = mr[v].x, my = mr[v].y;
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.dmeta);
+        const uint8_t* const dm = IL ? lmeta : a.dmeta;
+        const uint8_t* const ds = IL ? lside : a.dside;
+        const uint32_t rmax = IL ? lraw_max : a.raw_max;
+        const u32x4* src = reinterpret_cast<const u32x4*>(dm);
         if (static_cast<uint32_t>(k) < static_cast<uint32_t>(__popc(mx))) {
             uint32_t ri = my + k;
-            ri = ri < a.raw_max ? ri : a.raw_max;
-            src = reinterpret_cast<const u32x4*>(a.dside + static_cast<uint64_t>(ri) * 64 + 16 * p4);
+            ri = ri < rmax ? ri : rmax;
+            src = reinterpret_cast<const u32x4*>(ds + static_cast<uint64_t>(ri) * 64 + 16 * p4);
         }
         rx[v] = *src;
     };
     // cross-wave reduction of acc into snk: red[w][i][c][q][lane]; then output element
     // o = ((tile * 16 + m_local) * 16 + n_local), consecutive threads on consecutive n of one
     // Y row. The caller has made red free (a barrier after any other use of it).
-    constexpr int TILES = RT * CT;
-    float* const redp = red + (PAIR && XT == 2 ? (NW * U * CT * 2048) / 4 : 0);  // PAIR: past the X rings
+    constexpr int TILES = RTT * CT;
+    float* const redp = red + (SEQ && XT == 2 ? (NW * U * CT * 2048) / 4 : 0);  // PAIR 1: past the X rings
     auto reduce_into = [&](const GemmArgs& ar, auto&& snk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < RT; i++)
+        for (int i = 0; i < RTT; i++)
 #pragma unroll
             for (int c = 0; c < CT; c++)
 #pragma unroll
@@ -537,6 +549,32 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
             for (int w = 0; w < NW; w++) sum += redp[((w * TILES + tile) * 4 + q) * 64 + src_lane];
             const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
             if (n < ar.N && m < ar.M) snk(o, n, m, sum);
+        }
+    };
+    // PAIR 2: both matrices' outputs of an element, a's then a1's (tile i + RT), in one thread
+    auto reduce_pair = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RTT; i++)
+#pragma unroll
+            for (int c = 0; c < CT; c++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) redp[((wave * TILES + i * CT + c) * 4 + q) * 64 + lane] = acc[i][c][q];
+        __syncthreads();
+        for (int o = threadIdx.x; o < RT * CT * 256; o += 64 * NW) {
+            const int tile = o >> 8, ml = (o >> 4) & 15, nl = o & 15;
+            const int i = tile / CT, c = tile % CT;
+            const int src_lane = (nl >> 2) * 16 + ml, q = nl & 3;
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; w++) {
+                s0 += redp[((w * TILES + tile) * 4 + q) * 64 + src_lane];
+                s1 += redp[((w * TILES + RT * CT + tile) * 4 + q) * 64 + src_lane];
+            }
+            const int64_t n = nb + 16 * i + nl, m = 16 * c + ml;
+            if (n < a.N && m < a.M) {
+                sink(o, n, m, s0);
+                sink1(o, n, m, s1);
+            }
         }
     };
     // PAIR, after a's last group: a's outputs to sink, a fresh start for a1. The X rings stay
@@ -555,7 +593,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     // raw exponents of group t + U/2, multiply, then refill the X pieces
     auto step = [&](uint32_t t, auto uc, bool refill, bool rawpf) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        const GemmArgs& a = pick(t);  // (only the consumed matrix's palette and side table)
+        const GemmArgs& a0 = pick(t);  // (only the consumed matrix's palette and side table)
         u32x4 XF[XT ? CT : 1][2];  // XT: this step's X fragments, back from the LDS tile
         if (XT == 2) {
             // the slot's X transfer was issued before its W loads, and loads retire in
@@ -583,9 +621,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
             if (!XNEAR && refill) load_x(jc(t + U), xr[XNEAR ? 0 : u]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        u32x4 A[RT][2];
+        u32x4 A[RTT][2];
 #pragma unroll
-        for (int i = 0; i < RT; i++) {
+        for (int i = 0; i < RTT; i++) {
+            const GemmArgs& a = IL && i >= RT ? a1 : a0;
             rebuild16<SRC, CONTIG>(a, ring[u][i], A[i][0], A[i][1]);
             if (DIRECT) {
                 const uint32_t mask = __builtin_amdgcn_readlane(mr[u % (DIRECT ? U : 1)].x, LPT * i);
@@ -616,7 +655,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-                for (int i = 0; i < RT; i++)
+                for (int i = 0; i < RTT; i++)
 #pragma unroll
                     for (int c = 0; c < CT; c++) acc[i][c] = mfma16(A[i][s2], xr[0][c][s2], acc[i][c]);
             if (refill || t + 1 < T2) load_x(jc(t + 1), xr[0]);  // unconditional in the steady state
@@ -638,20 +677,20 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-                for (int i = 0; i < RT; i++)
+                for (int i = 0; i < RTT; i++)
 #pragma unroll
                     for (int c = 0; c < CT; c++)
                         acc[i][c] = mfma16(A[i][s2], XT ? XF[XT ? c : 0][s2] : xr[u][c][s2], acc[i][c]);
             __builtin_amdgcn_sched_barrier(0);
             if (!XT && refill) load_x(jc(t + U), xr[u]);
         }
-        if (PAIR && t + 1 == T) mid_reduce();  // a's last group: its outputs, while a1's first are in flight
+        if (SEQ && t + 1 == T) mid_reduce();  // a's last group: its outputs, while a1's first are in flight
     };
     // The ring is filled with no conditions (slots past the wave's last group reload that
     // group): the compiler's wait counts at the loop head are the minimum over every path
     // into it, so a skipped load on any path would make it wait for nearly all loads in
     // flight, once per ring turn.
-    if (PAIR && T == 0) mid_reduce();  // (a wave with no group still takes part)
+    if (SEQ && T == 0) mid_reduce();  // (a wave with no group still takes part)
     if (T > 0) {
         [&]<int... us>(std::integer_sequence<int, us...>) {
             if constexpr (XNEAR) {
@@ -745,7 +784,10 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& a, const GemmArgs& a
     // (XT 2: every transfer has landed, those of ring slots past the wave's last group too)
     if (XT == 2) __builtin_amdgcn_s_waitcnt(0);
     if (XT) __syncthreads();
-    reduce_into(PAIR ? a1 : a, sink1);
+    if constexpr (IL)
+        reduce_pair();
+    else
+        reduce_into(SEQ ? a1 : a, sink1);
 }
 
 template <int SRC, bool CONTIG, int CT, int RT, int U, int NW, bool XNEAR, int XT>
@@ -758,27 +800,29 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny(GemmArgs a)
         else
             a.y[m * a.ldy + n] = v;
     };
-    skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT, false>(a, a, red, store, store);
+    skinny_tile<SRC, CONTIG, CT, RT, U, NW, XNEAR, XT, 0>(a, a, red, store, store);
 }
 
 // LDS of a skinny block: the cross-wave reduction, or the X tiles (aliased): XT 1, one
-// padded tile per wave; XT 2, a ring of U DMA targets per wave (PAIR: the rings and the
-// reduction side by side, as the rings stay in use across the mid-stream reduction).
-template <int CT, int RT, int U, int NW, int XT, bool PAIR = false>
+// padded tile per wave; XT 2, a ring of U DMA targets per wave (PAIR 1: the rings and the
+// reduction side by side, as the rings stay in use across the mid-stream reduction; PAIR 2:
+// the reduction covers both matrices' tiles).
+template <int CT, int RT, int U, int NW, int XT, int PAIR = 0>
 constexpr size_t skinny_lds()
 {
-    constexpr size_t red_bytes = static_cast<size_t>(NW) * RT * CT * 256 * 4;
+    constexpr size_t red_bytes = static_cast<size_t>(NW) * (PAIR == 2 ? 2 * RT : RT) * CT * 256 * 4;
     constexpr size_t xt_bytes = XT == 1 ? static_cast<size_t>(NW) * 16 * CT * 9 * 16
                               : XT == 2 ? static_cast<size_t>(NW) * U * CT * 2048
                                         : 0;
-    if (PAIR && XT == 2) return red_bytes + xt_bytes;
+    if (PAIR == 1 && XT == 2) return red_bytes + xt_bytes;
     return red_bytes > xt_bytes ? red_bytes : xt_bytes;
 }
 
 // gate and up of a SwiGLU MLP in one launch (direct planes, same X, same shape): each
-// block streams its rows of gate and then of up through one ring, keeps gate's outputs in
-// LDS, and writes g, u (fp32) and h = bf16(silu(g) * u). One ramp and one tail instead of
-// three launches (and no second ramp between the two), no separate SwiGLU pass.
+// block streams its rows of gate and up through one ring (group by group, both matrices in
+// a step, or gate's groups and then up's: PAIR 2 or 1), keeps gate's outputs in LDS, and
+// writes g, u (fp32) and h = bf16(silu(g) * u). One ramp and one tail instead of three
+// launches, no separate SwiGLU pass; with PAIR 2 each X group is fetched once for both.
 struct GateUpArgs {
     GemmArgs gate, up;
     uint16_t* h;
@@ -788,7 +832,7 @@ struct GateUpArgs {
     uint32_t zM, zN;
 };
 
-template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, int XT>
+template <bool CG, bool CU, int CT, int RT, int U, int NW, bool XNEAR, int XT, int PAIR>
 __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
 {
     static_assert(CG == CU, "one palette kind for both (the launcher takes consecutive exponents only)");
@@ -806,8 +850,8 @@ __global__ void __launch_bounds__(64 * NW) gemm_skinny_gate_up(GateUpArgs ga)
                 for (uint32_t c = 0; n + c < ga.zN; c++) row[c] = 0.f;
         }
     }
-    float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT, true>() / 4;  // RT * CT * 256 gate outputs
-    skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT, true>(
+    float* const gbuf = red + skinny_lds<CT, RT, U, NW, XT, PAIR>() / 4;  // RT * CT * 256 gate outputs
+    skinny_tile<UW_W_DIRECT, CG, CT, RT, U, NW, XNEAR, XT, PAIR>(
         ga.gate, ga.up, red,
         [&](int o, int64_t n, int64_t m, float v) {
             ga.gate.y[m * ga.gate.ldy + n] = v;
@@ -1577,24 +1621,33 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
     return launch_tiled_t<SRC, CONTIG, 256, 128>(g, s);
 }
 
-template <int CT, int RT, int U, int NW, bool XNEAR, int XT>
-hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
+template <int CT, int RT, int U, int NW, bool XNEAR, int XT, int PAIR>
+hipError_t launch_gate_up_p(const GateUpArgs& ga, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>((ga.gate.N + 16 * RT - 1) / (16 * RT)));
-    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT, true>() + static_cast<size_t>(RT) * CT * 256 * 4;
+    constexpr size_t lds = skinny_lds<CT, RT, U, NW, XT, PAIR>() + static_cast<size_t>(RT) * CT * 256 * 4;
     if constexpr (lds > 160 * 1024) {
         (void)ga;
         (void)s;
         (void)grid;
         return hipErrorNotSupported;  // (8 waves with X rings beside the reduction at M > 32)
     } else {
-        const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>);
+        const void* fn = reinterpret_cast<const void*>(&gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT, PAIR>);
         static uint64_t attr_done = 0;  // devices the LDS limit was raised on
         hipError_t e = allow_lds(fn, lds, attr_done);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT>), grid, dim3(64 * NW), lds, s, ga);
+        hipLaunchKernelGGL((gemm_skinny_gate_up<true, true, CT, RT, U, NW, XNEAR, XT, PAIR>), grid, dim3(64 * NW), lds, s, ga);
         return hipGetLastError();
     }
+}
+
+// 4 waves take group j of gate and up in one step (X fetched once for both; 2 RT row tiles
+// per slot, which fits the 512 registers of a lone wave per SIMD); 8 waves, two per SIMD
+// with half the registers each, stream gate's groups and then up's through one ring.
+template <int CT, int RT, int U, int NW, bool XNEAR, int XT>
+hipError_t launch_gate_up_ct(const GateUpArgs& ga, hipStream_t s)
+{
+    return launch_gate_up_p<CT, RT, U, NW, XNEAR, XT, NW == 4 ? 2 : 1>(ga, s);
 }
 
 template <int RT, int U, int NW, bool XNEAR = false, int XT = 0>

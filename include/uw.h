@@ -251,8 +251,10 @@ int uw_split_count(int variant, int64_t N, int64_t K, int64_t M, int32_t split_k
  * reconstructive matmul's overheads, "Bundles and results" / "Trade-offs": one launch for
  * gate and up). gate and up are two uw_gemm_args as for uw_recon_gemm, both on the
  * direct plane (src UW_W_DIRECT) with the same M (1..64), N, K and X (d_x, ldx); each
- * block streams its rows of gate and then the same rows of up through one load ring, with
- * gate's GEMM variant. Writes gate->d_y and
+ * block streams its rows of gate and the same rows of up through one load ring, with
+ * gate's GEMM variant: 4-wave variants take a K group of both matrices per step (each X
+ * group fetched once for the two), 8-wave variants all of gate's groups, then up's. A
+ * variant with 8 waves and X rings ("xd") has no fused form past M = 32. Writes gate->d_y and
  * up->d_y (fp32, exactly what uw_recon_gemm gives with that variant) and
  * d_h[M][ldh] = bf16(silu(gate) * up), the same bits as uw_swiglu on those outputs.
  * Errors: UW_EINVAL / UW_ESHAPE as for uw_recon_gemm (UW_EINVAL also when gate and up
