@@ -484,7 +484,7 @@ def test_full_size_gate():
 
 
 def test_full_size_down():
-    _full_size_case(synth.CONFIGS["down"], "down", (256, 1024, 4096))
+    _full_size_case(synth.CONFIGS["down"], "down", (1, 16, 64, 256, 1024, 4096))
 
 
 def test_full_size_70b():
