@@ -86,6 +86,8 @@ def parse(argv=None):
     p.add_argument("--plans", help="read the plans from this JSON file (written by --save-plans) instead of tuning")
     p.add_argument("--save-plans", help="write the measured plans to this JSON file")
     p.add_argument("--copy-probe", action="store_true", help="also launch a plain 256 MiB copy kernel (counter scale)")
+    p.add_argument("--schedules", action="store_true",
+                   help="also time the hard/easy stack: one stream, a decode stream, CU-split pairs, tuned end to end")
     return p.parse_args(argv)
 
 
@@ -478,6 +480,7 @@ def main():
         f"of 8 TB/s ({achieved / read_gbs:.3f} of the {read_gbs:.0f} GB/s read ceiling); launches: {op_rows}")
 
     large = None if args.no_large else large_m(uw, synth, torch, dev, stream, stack, plans, log)
+    sched = schedules(uw, synth, torch, dev, stream, stack, plans, log) if args.schedules else None
     detail = {"plans": plans_to_json(uw, plans), "launches": op_rows,
               "forward_ms": {str(M): round(fwd_ms[M], 4) for M in SMALL_MS},
               "blob_bytes_per_weight": round(2 * stack.blob_total / stack.weight_bytes, 4),
@@ -515,10 +518,91 @@ def main():
                    "layers": L, "Ms": list(SMALL_MS)},
         "roofline": roofline,
         "large_m": large,
+        "schedules": sched,
         "cpu_baseline": cpu,
         "detail": detail,
     }
     print(json.dumps(out))
+
+
+def schedules(uw, synth, torch, dev, stream, stack, plans, log, Ms=SMALL_MS, reps=5):
+    """The stack with hard layers ("Sharing the GPU between decode and compute"): every 4th layer
+    keeps only its Huffman blobs, so each of its projections needs preprocessing (full decode to
+    start with), while the others run their direct planes on the tuned plans. ms per forward at
+    each M, back to back between HIP events on the forward's stream: one stream; the decodes on a
+    second stream with 3 workspace slots (in order, then each layer's down first); the same on
+    CU-split stream pairs (decode on 32 or 64 of the CUs); then uw_mlp_stack_autotune's plan
+    (decode stream, 3 slots), against the stack with no hard layer."""
+    L = stack.L
+    hard = [l for l in range(L) if l % 4 == 3]
+    side = torch.cuda.Stream()
+    out = {"hard_layers": hard, "slots": 3}
+    for M in Ms:
+        pm = plans[M]
+        rows = []
+        for l in range(L):
+            trip = []
+            for q in range(3):
+                p = pm["down" if q == 2 else "gate"]
+                if l in hard:
+                    trip.append(uw.proj(stack.h[l][q], stack.blob[l][q], uw.PIPE_FULL))
+                else:
+                    trip.append(uw.proj(stack.h[l][q], stack.blob[l][q], p["pipeline"], d_direct=stack.plane[l][q],
+                                        variant=p["variant"], split_k=p["split_k"]))
+            rows.append(trip)
+        arr = uw.mlp_layers(rows)
+        easy = stack.layers(uw, pm)
+        full = uw.mlp_layers([[uw.proj(stack.h[l][q], stack.blob[l][q], uw.PIPE_FULL) for q in range(3)]
+                              for l in range(L)])
+        nb = max(uw.mlp_stack_workspace_ex(full, M, slots=3, down_first=df) for df in (False, True))
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        x = torch.from_numpy(synth.gen_x(stack.cfg, M, stack.K).view(np.int16)).to(dev)
+        y = torch.empty(M, stack.K, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def timed(fwd, st):
+            fwd()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for _ in range(reps):
+                fwd()
+            b.record(st)
+            torch.cuda.synchronize()
+            return round(a.elapsed_time(b) / reps, 4)
+
+        row = {"no_hard_layer": timed(lambda: uw.mlp_stack_forward(easy, M, x, y, ws, nb, stream=stream), stream),
+               "one_stream": timed(lambda: uw.mlp_stack_forward_ex(arr, M, x, y, ws, nb, stream=stream, slots=3),
+                                   stream)}
+        for df in (False, True):
+            row["decode_stream" + ("_down_first" if df else "")] = timed(
+                lambda: uw.mlp_stack_forward_ex(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3,
+                                                down_first=df), stream)
+        for cus in (32, 64):
+            g, d = uw.stream_pair_create(cus)
+            try:
+                gs = torch.cuda.ExternalStream(g)
+                row[f"cu_split_{cus}"] = timed(lambda: uw.mlp_stack_forward_ex(
+                    arr, M, x, y, ws, nb, stream=g, decode_stream=d, slots=3, down_first=True), gs)
+            finally:
+                torch.cuda.synchronize()
+                uw.stream_destroy(g)
+                uw.stream_destroy(d)
+        t0 = time.time()
+        a = uw.mlp_stack_autotune(arr, M, x, y, ws, nb, stream=stream, decode_stream=side, slots=3, reps=3, warmup=1)
+        torch.cuda.synchronize()
+        tune_s = time.time() - t0
+        df = bool(a.opts.down_first)
+        row["tuned"] = timed(lambda: uw.mlp_stack_forward_ex(arr, M, x, y, ws, nb, stream=stream, decode_stream=side,
+                                                             slots=3, down_first=df), stream)
+        row["tuned_plan"] = {cls: {r: uw.PIPELINE_NAMES[getattr(arr[l], r).pipeline] for r in ("gate", "up", "down")}
+                             for cls, l in (("easy", 0), ("hard", hard[0]))}
+        row["tuned_down_first"] = df
+        row["tune"] = {"passes": a.passes, "trials": a.trials, "seconds": round(tune_s, 1)}
+        out[str(M)] = row
+        log(f"[bench] hard/easy stack M={M} (ms per forward): {row}")
+        del ws, x, y
+    return out
 
 
 def large_m(uw, synth, torch, dev, stream, stack, plans, log):
