@@ -501,7 +501,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
     // them (valid while it fits in lmax bits). Entries are visited in a scattered order
     // (an odd multiplier permutes 0..lsize-1): entries with a common prefix read t1 at
     // strides of 2^length and would otherwise pile onto one LDS bank.
-    constexpr int kPer = 8;
+    // (10 per thread: one pass over 4096 entries with the usual 7 or 8 waves per workgroup)
+    constexpr int kPer = 10;
     for (uint32_t base = 0; base < lsize; base += kPer * nthreads) {
         uint32_t idx[kPer], vals[kPer], used[kPer], n[kPer];
 #pragma unroll
@@ -648,7 +649,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
         auto decode = [&](auto lds_tag, uint32_t S) {
             constexpr bool IN_LDS = decltype(lds_tag)::value;
             uint32_t k = 0;
-            uint64_t acc = 0;
+            // the symbol word being filled (nibbles below bit bp), stored after every entry
+            uint32_t w = 0, bp = 0;
+            uint32_t* wq = mysym;
+            const int last6 = static_cast<int>(S) - static_cast<int>(kMaxSyms);  // k <= last6: room for a whole entry
             uint32_t wn = read_word<IN_LDS>(a, win, wa, wp);  // word wp, read a refill ahead
             auto refill = [&]() {
                 const bool take = nb < 32;
@@ -657,19 +661,25 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 nb += take ? 32 : 0;
                 wn = read_word<IN_LDS>(a, win, wa, wp);
             };
+            // the next L stream bits (L <= 12: all in the buffer's high word)
+            auto peek = [&]() { return static_cast<uint32_t>(buf >> 32) >> (32 - L); };
             auto put = [&](uint32_t vals, uint32_t n) {
-                acc |= static_cast<uint64_t>(vals) << (4 * (k & 7));
-                mysym[k >> 3] = static_cast<uint32_t>(acc);
-                const uint32_t kn = k + n;
-                acc >>= ((k ^ kn) & 8) << 2;
-                k = kn;
+                const uint64_t t = static_cast<uint64_t>(vals) << bp;
+                w |= static_cast<uint32_t>(t);
+                *wq = w;
+                bp += 4 * n;
+                const bool cross = bp >= 32;  // the entry ran into the next word: its rest starts it
+                w = cross ? static_cast<uint32_t>(t >> 32) : w;
+                wq += cross ? 1 : 0;
+                bp &= 31;
+                k += n;
             };
-            while (__any(k + kMaxSyms <= S)) {
+            while (__any(static_cast<int>(k) <= last6)) {
                 refill();
 #pragma unroll
                 for (int u = 0; u < 2; u++) {
-                    uint32_t e = lut[static_cast<uint32_t>(buf >> (64 - L))];
-                    e = k + kMaxSyms <= S ? e : 0u;
+                    uint32_t e = lut[peek()];
+                    e = static_cast<int>(k) <= last6 ? e : 0u;
                     const uint32_t lt = ent_len(e);
                     buf <<= lt;
                     nb -= static_cast<int>(lt);
@@ -681,7 +691,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 refill();
 #pragma unroll
                 for (int u = 0; u < 2; u++) {
-                    const uint32_t e1 = t1[static_cast<uint32_t>(buf >> (64 - L))];
+                    const uint32_t e1 = t1[peek()];
                     const bool go = k < S;
                     const uint32_t l1 = e1 & 15u;
                     const uint32_t lt = go ? (l1 ? l1 : L) : 0u;
