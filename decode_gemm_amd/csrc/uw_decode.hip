@@ -674,32 +674,38 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 bp &= 31;
                 k += n;
             };
-            while (__any(static_cast<int>(k) <= last6)) {
-                refill();
+            // (loops test at the bottom: with the test at the top the compiler copies every
+            // loop-carried register once per iteration)
+            if (__any(static_cast<int>(k) <= last6)) {
+                do {
+                    refill();
 #pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    uint32_t e = lut[peek()];
-                    e = static_cast<int>(k) <= last6 ? e : 0u;
-                    const uint32_t lt = ent_len(e);
-                    buf <<= lt;
-                    nb -= static_cast<int>(lt);
-                    err |= e;
-                    put(e & 0xFFFFFFu, ent_n(e));
-                }
+                    for (int u = 0; u < 2; u++) {
+                        uint32_t e = lut[peek()];
+                        e = static_cast<int>(k) <= last6 ? e : 0u;
+                        const uint32_t lt = ent_len(e);
+                        buf <<= lt;
+                        nb -= static_cast<int>(lt);
+                        err |= e;
+                        put(e & 0xFFFFFFu, ent_n(e));
+                    }
+                } while (__any(static_cast<int>(k) <= last6));
             }
-            while (__any(k < S)) {
-                refill();
+            if (__any(k < S)) {
+                do {
+                    refill();
 #pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const uint32_t e1 = t1[peek()];
-                    const bool go = k < S;
-                    const uint32_t l1 = e1 & 15u;
-                    const uint32_t lt = go ? (l1 ? l1 : L) : 0u;
-                    buf <<= lt;
-                    nb -= static_cast<int>(lt);
-                    err |= go && l1 == 0 ? kEntErr : 0u;
-                    put(go ? e1 >> 4 : 0u, go ? 1u : 0u);
-                }
+                    for (int u = 0; u < 2; u++) {
+                        const uint32_t e1 = t1[peek()];
+                        const bool go = k < S;
+                        const uint32_t l1 = e1 & 15u;
+                        const uint32_t lt = go ? (l1 ? l1 : L) : 0u;
+                        buf <<= lt;
+                        nb -= static_cast<int>(lt);
+                        err |= go && l1 == 0 ? kEntErr : 0u;
+                        put(go ? e1 >> 4 : 0u, go ? 1u : 0u);
+                    }
+                } while (__any(k < S));
             }
         };
         // the task body, instantiated for each word source so that the LDS one never
