@@ -382,16 +382,21 @@ namespace lut {
 constexpr uint32_t kMaxWaves = 8;          // waves per workgroup at most
 constexpr int kWinWords = 1792;            // stream window per wave (7 KB)
 constexpr int kWinLoads = kWinWords / 256; // 16-byte loads per lane to fill it
-constexpr int kSegElems = 256;             // weights per lane per segment (four groups)
-constexpr int kSymPitch = kSegElems / 8 + 1;
 constexpr int kInfo = 128;                 // per-wave lane info: raw mask, raw-table base
-constexpr int kWaveDwords = kWinWords + 64 * kSymPitch + kInfo;
 constexpr int kLutEntries = 4096;          // multi-code table, u32 entries
 constexpr int kT1Dwords = 1024;            // single-code table, u8 entries
 constexpr uint32_t kMaxSyms = 6;
 constexpr uint32_t kMaxChunk = 2048;
 
-constexpr size_t lds_bytes(uint32_t waves) { return 4u * (kLutEntries + kT1Dwords + waves * kWaveDwords); }
+// Weights per lane per segment (a segment is decoded into the wave's symbol buffer, then written
+// out). The direct plane's write-out, the longest, is fastest in shorter alternations with the
+// decode (96 against 117 us on the gate shape); the other outputs in longer ones.
+template <int MODE>
+constexpr int seg_elems() { return MODE == DEC_DIRECT ? 128 : 256; }
+template <int MODE>
+constexpr int wave_dwords() { return kWinWords + 64 * (seg_elems<MODE>() / 8 + 1) + kInfo; }
+template <int MODE>
+constexpr size_t lds_bytes(uint32_t waves) { return 4u * (kLutEntries + kT1Dwords + waves * wave_dwords<MODE>()); }
 
 struct Args {
     const uint8_t* sm;
@@ -471,6 +476,10 @@ template <int MODE>
 __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
 {
     extern __shared__ uint32_t smem[];
+    constexpr int kSegElems = seg_elems<MODE>();  // weights per lane per segment
+    constexpr int kSG = kSegElems / 64;           // groups per segment
+    constexpr int kSymPitch = kSegElems / 8 + 1;
+    constexpr int kWaveDwords = wave_dwords<MODE>();
     uint32_t* lut = smem;
     uint8_t* t1 = reinterpret_cast<uint8_t*>(smem + kLutEntries);
     const uint32_t tid = threadIdx.x, lane = tid & 63;
@@ -717,17 +726,18 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
             start(lds_tag);
             const uint32_t segs = (a.chunk + kSegElems - 1) / kSegElems;
             for (uint32_t s = 0; s < segs; s++) {
-                const uint32_t gq = 4 * s;
-                const uint32_t nseg = ng > gq ? min(ng - gq, 4u) : 0u;
+                const uint32_t gq = kSG * s;
+                const uint32_t nseg = ng > gq ? min(ng - gq, static_cast<uint32_t>(kSG)) : 0u;
                 const uint32_t nonraw = ~(rawmask >> gq) & ((1u << nseg) - 1u);
                 const uint32_t S = 64u * __popc(nonraw);
                 // sign/mantissa bytes of this lane's write-out items, in flight during the decode
-                // (items of 16 weights: chunk l = 4 it + lane / 16, group (lane / 4) % 4, piece lane % 4)
-                constexpr int kSmItems = MODE == DEC_FULL || MODE == DEC_DIRECT ? 16 : 1;
-                constexpr int kSmEarly = kSmItems > 1 ? KSM_EARLY : 1;  // prefetched before the decode
+                // (items of 16 weights, item = 64 it + lane: chunk item / (4 kSG), group
+                // (item / 4) % kSG, piece item % 4)
+                constexpr int kSmItems = MODE == DEC_FULL || MODE == DEC_DIRECT ? 4 * kSG : 1;
+                constexpr int kSmEarly = kSmItems > 1 ? (KSM_EARLY < kSmItems ? KSM_EARLY : kSmItems) : 1;  // before the decode
                 u32x4 smv[kSmItems];
                 auto load_sm = [&](int it) {
-                    const uint32_t l = 4 * it + (lane >> 4), g = (lane >> 2) & 3;
+                    const uint32_t item = it * 64 + lane, l = item / (4 * kSG), g = (item >> 2) % kSG;
                     const uint32_t cl = min(c0 + l, a.n_chunks - 1);
                     const uint32_t el = cl * a.chunk, q = min(gq + g, (min(a.chunk, a.n_elems - el) >> 6) - 1);
                     smv[it] = *reinterpret_cast<const u32x4*>(a.sm + el + 64 * q + 16 * (lane & 3));
@@ -771,8 +781,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                 };
                 if (MODE == DEC_EXP) {
     #pragma unroll 4
-                    for (int it = 0; it < 16; it++) {
-                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                    for (int it = 0; it < 4 * kSG; it++) {
+                        const uint32_t item = it * 64 + lw, l = item / (4 * kSG), g = (item >> 2) % kSG, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t rm = info[l];
@@ -793,13 +803,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                     }
                 } else if (MODE == DEC_FULL) {
     #pragma unroll
-                    for (int it = 0; it < 16; it++) {
+                    for (int it = 0; it < 4 * kSG; it++) {
                         if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
                         if (it == kSmItems - 1 + kWindowAt) {
                             prefetch_window();
                             __builtin_amdgcn_sched_barrier(0);
                         }
-                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        const uint32_t item = it * 64 + lw, l = item / (4 * kSG), g = (item >> 2) % kSG, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t e = el + 64 * q + 16 * p;
@@ -825,8 +835,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                     }
                 } else if (MODE == DEC_IDX) {
     #pragma unroll
-                    for (int it = 0; it < 8; it++) {
-                        const uint32_t item = it * 64 + lw, l = item >> 3, g = (item >> 1) & 3, p = item & 1, q = gq + g;
+                    for (int it = 0; it < 2 * kSG; it++) {
+                        const uint32_t item = it * 64 + lw, l = item / (2 * kSG), g = (item >> 1) % kSG, p = item & 1, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t rm = info[l];
@@ -841,13 +851,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_lut_kernel(Args a)
                     // direct plane: the 16 weights of lane group p of a group, at MFMA lane
                     // 16p + (row & 15) of the row tile's block
     #pragma unroll
-                    for (int it = 0; it < 16; it++) {
+                    for (int it = 0; it < 4 * kSG; it++) {
                         if (it && (it & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound register pressure
                         if (it == kSmItems - 1 + kWindowAt) {
                             prefetch_window();
                             __builtin_amdgcn_sched_barrier(0);
                         }
-                        const uint32_t item = it * 64 + lw, l = item >> 4, g = (item >> 2) & 3, p = item & 3, q = gq + g;
+                        const uint32_t item = it * 64 + lw, l = item / (4 * kSG), g = (item >> 2) % kSG, p = item & 3, q = gq + g;
                         uint32_t el;
                         if (!item_ok(l, q, el)) continue;
                         const uint32_t fs = el + 64 * q;
@@ -941,11 +951,11 @@ hipError_t launch_lut(const lut::Args& f, uint32_t blocks, uint32_t waves, hipSt
     if (!((attr_done >> dev) & 1u)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lut::decode_lut_kernel<MODE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lut::lds_bytes(lut::kMaxWaves)));
+                                           static_cast<int>(lut::lds_bytes<MODE>(lut::kMaxWaves)));
         if (e != hipSuccess) return e;
         attr_done |= uint64_t{1} << dev;
     }
-    hipLaunchKernelGGL(lut::decode_lut_kernel<MODE>, dim3(blocks), dim3(64 * waves), lut::lds_bytes(waves), s, f);
+    hipLaunchKernelGGL(lut::decode_lut_kernel<MODE>, dim3(blocks), dim3(64 * waves), lut::lds_bytes<MODE>(waves), s, f);
     return hipGetLastError();
 }
 
