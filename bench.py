@@ -86,6 +86,7 @@ def parse(argv=None):
     p.add_argument("--plans", help="read the plans from this JSON file (written by --save-plans) instead of tuning")
     p.add_argument("--save-plans", help="write the measured plans to this JSON file")
     p.add_argument("--copy-probe", action="store_true", help="also launch a plain 256 MiB copy kernel (counter scale)")
+    p.add_argument("--no-70b", action="store_true", help="skip the 70B-shaped layer")
     p.add_argument("--schedules", action="store_true",
                    help="also time the hard/easy stack: one stream, a decode stream, CU-split pairs, tuned end to end")
     return p.parse_args(argv)
@@ -147,20 +148,20 @@ def gate_up_bytes(hg, hu, M):
 
 # ---------------------------------------------------------------- the stack
 class Stack:
-    """The 32-layer stack on the device: per (layer, role) the header, the blob and the
-    direct plane made from it at load."""
+    """MLP layers on the device (the 32-layer stack, or the one 70B-shaped layer): per (layer,
+    role) the header, the blob and the direct plane made from it at load."""
 
-    def __init__(self, uw, synth, torch, dev, log):
+    def __init__(self, uw, synth, torch, dev, log, cfg_name="stack"):
         import concurrent.futures as cf
 
-        self.cfg = cfg = synth.CONFIGS["stack"]
+        self.cfg = cfg = synth.CONFIGS[cfg_name]
         self.L = cfg.layers
-        sig = synth.gen_stack_sigmas(cfg)
+        sig = synth.gen_stack_sigmas(cfg) if cfg.layers > 1 else None
         t0 = time.time()
 
         def make(i):
             layer, q = divmod(i, 3)
-            return uw.encode(synth.gen_weight(cfg, ROLES[q], layer, sigma=float(sig[layer])))
+            return uw.encode(synth.gen_weight(cfg, ROLES[q], layer, sigma=None if sig is None else float(sig[layer])))
 
         self.h = [[None] * 3 for _ in range(self.L)]
         self.blob = [[None] * 3 for _ in range(self.L)]
@@ -182,7 +183,7 @@ class Stack:
         self.macs = sum(h.N * h.K for row in self.h for h in row)
         blob_total = sum(sum(r) for r in self.blob_bytes)
         plane_total = sum(uw.direct_plane_bytes(h) for row in self.h for h in row)
-        log(f"[bench] stack: {3 * self.L} matrices encoded and prepared in {time.time() - t0:.1f}s; "
+        log(f"[bench] {cfg.name}: {3 * self.L} matrices encoded and prepared in {time.time() - t0:.1f}s; "
             f"Huffman {blob_total / 1e9:.2f} GB ({blob_total / self.weight_bytes * 2:.3f} B/w), direct planes "
             f"{plane_total / 1e9:.2f} GB ({plane_total / self.weight_bytes * 2:.3f} B/w), bf16 {self.weight_bytes / 1e9:.2f} GB")
         self.blob_total, self.plane_total = blob_total, plane_total
@@ -481,6 +482,7 @@ def main():
 
     large = None if args.no_large else large_m(uw, synth, torch, dev, stream, stack, plans, log)
     sched = schedules(uw, synth, torch, dev, stream, stack, plans, log) if args.schedules else None
+    l70 = None if args.no_70b else layer_70b(uw, synth, torch, dev, stream, log)
     detail = {"plans": plans_to_json(uw, plans), "launches": op_rows,
               "forward_ms": {str(M): round(fwd_ms[M], 4) for M in SMALL_MS},
               "blob_bytes_per_weight": round(2 * stack.blob_total / stack.weight_bytes, 4),
@@ -519,10 +521,56 @@ def main():
         "roofline": roofline,
         "large_m": large,
         "schedules": sched,
+        "layer_70b": l70,
         "cpu_baseline": cpu,
         "detail": detail,
     }
     print(json.dumps(out))
+
+
+def layer_70b(uw, synth, torch, dev, stream, log, reps=10):
+    """The 70B-shaped MLP layer (gate and up 28672x8192, down 8192x28672; Student-t(4) weights
+    with 1% of 64-weight rows holding an outlier exponent) at M in {1, 64, 512, 2048}: plans
+    chosen as for the stack (uw_autotune per projection, the fused gate/up launch timed itself
+    at M <= 64), then the layer's forward launched back to back between HIP events:
+    uncompressed-equivalent GB/s at M <= 64, TFLOP/s and the bf16-peak fraction above."""
+    st = Stack(uw, synth, torch, dev, log, "70b")
+    Ms = st.cfg.Ms
+    plans = tune_plans(uw, synth, torch, dev, st, Ms, log)
+    pj = plans_to_json(uw, plans)
+    out = {"workload": "70B-shaped SwiGLU MLP layer: gate/up 28672x8192, down 8192x28672 bf16 Student-t(4)*0.01, "
+                       "1% of 64-weight rows with an outlier exponent",
+           "n_raw": [int(h.n_raw) for h in st.h[0]]}
+    for M in Ms:
+        arr = st.layers(uw, plans[M])
+        nb = uw.mlp_stack_workspace(arr, M)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        x = torch.from_numpy(synth.gen_x(st.cfg, M, st.K).view(np.int16)).to(dev)
+        y = torch.empty(M, st.K, dtype=torch.float32, device=dev)
+        uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        row = {"forward_ms": round(ms, 4), "plans": pj[str(M)]}
+        if M <= 64:
+            row["uncompressed_GBs"] = round(st.weight_bytes / (ms * 1e-3) / 1e9, 1)
+            res = st.plane_total + 2 * M * st.K + 4 * M * st.K
+            row["hbm_frac"] = round(res / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            tf = 2.0 * M * st.macs / (ms * 1e-3) / 1e12
+            row["tflops"] = round(tf, 1)
+            row["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        out[str(M)] = row
+        log(f"[bench] 70B layer M={M}: {row}")
+        del ws, x, y
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def schedules(uw, synth, torch, dev, stream, stack, plans, log, Ms=SMALL_MS, reps=5):
