@@ -1412,9 +1412,156 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
             store_out(a, m0 + (TM * wm + c) * 16 + (lane & 15), n0 + (TN * wn + i) * 16 + 4 * (lane >> 4), acc[i][c]);
 }
 
+// ------------------------------------------------------------------------- dma
+// Plain bf16 GEMM for large M (the GEMM half of the full-decode and expand pipelines):
+// 256 x 256 output tile of 8 waves (4 x 2, 64 x 128 each), both operands sent from global
+// memory straight into LDS with global_load_lds_dwordx4, so no VGPR holds them on the way
+// and no LDS store instruction is issued. K advances BK (64 or 32) per step through NST
+// LDS stages (2 x 64 KB, or 4 x 32 KB: transfers three steps ahead).
+//
+// LDS layout of one operand in one stage: row rho (0..255) of the tile at RB rho (RB = 2 BK
+// bytes), its 16-byte chunk c (k 8c .. 8c+7 of the step) at slot c ^ f(rho), with
+// f(rho) = (rho / (256 / RB)) mod (BK / 8): rows that share LDS banks get different slots.
+// A transfer covers 1 KB: lane l lands at 16 l, i.e. row RPI i + l / CPR, slot l mod CPR
+// (RPI rows of CPR chunks per transfer), so it fetches chunk (l mod CPR) ^ f(rho); the
+// lanes of a row still read the row's whole segment. A fragment read (lane 16 g + r: row
+// 16 t + r, chunk 4 h + g) then hits 16 distinct 16-byte bank groups in every 16 lanes.
+template <int NWV, int BK, int NST>
+__global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
+{
+    constexpr int BN = 256, BM = 256;
+    constexpr int WGN = NWV / 2;       // waves along N
+    constexpr int TN = BN / 16 / WGN;  // 16-row W tiles per wave
+    constexpr int TM = 8;              // 16-row X tiles per wave
+    constexpr int RB = 2 * BK;         // bytes of one row of a stage
+    constexpr int CPR = BK / 8;        // 16-byte chunks per row
+    constexpr int RPI = 1024 / RB;     // rows per transfer
+    constexpr int BANKROWS = 256 / RB; // rows per 256-byte bank period
+    constexpr int OPB = 256 * RB;      // one operand, one stage
+    constexpr int STAGE = 2 * OPB;
+    constexpr int NLD = 256 / RPI / NWV;  // transfers per wave per operand per step
+    constexpr int H = BK / 32;            // MFMA k-halves per step
+    static_assert(NST * STAGE <= 160 * 1024 && NLD >= 1, "stage shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const uint32_t tiles_n = static_cast<uint32_t>((a.N + BN - 1) / BN);
+    const uint32_t tiles_m = static_cast<uint32_t>((a.M + BM - 1) / BM);
+    uint32_t tn, tm;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_n, tiles_m, tn, tm);
+    const int64_t n0 = static_cast<int64_t>(tn) * BN, m0 = static_cast<int64_t>(tm) * BM;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave >> 1, wm = wave & 1;
+    const uint32_t G = static_cast<uint32_t>(a.K >> 6);
+    uint32_t j0, j1;
+    k_slice(a, G, j0, j1);
+    // steps of BK over this K slice
+    const uint32_t s0 = j0 * (64 / BK), s1 = j1 * (64 / BK);
+
+    // per-lane byte offsets of this wave's transfers (rows past N or M read the last row;
+    // the host keeps every offset below 2^32)
+    uint32_t woff[NLD], xoff[NLD];
+#pragma unroll
+    for (int q = 0; q < NLD; q++) {
+        const int rho = RPI * (NLD * wave + q) + lane / CPR;
+        const int kap = (lane % CPR) ^ ((rho / BANKROWS) % CPR);
+        const int64_t n = n0 + rho < a.N ? n0 + rho : a.N - 1;
+        const int64_t m = m0 + rho < a.M ? m0 + rho : a.M - 1;
+        woff[q] = static_cast<uint32_t>(2 * n * a.K + 16 * kap);
+        xoff[q] = static_cast<uint32_t>(2 * m * a.ldx + 16 * kap);
+    }
+    const uint32_t lds0 = lds_offset(lds);
+    const uint8_t* const wbase = static_cast<const uint8_t*>(a.wplane);
+    const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(a.x);
+    auto issue = [&](uint32_t st_k, int st) {
+        const uint8_t* wb = wbase + RB * static_cast<int64_t>(st_k);
+        const uint8_t* xb = xbase + RB * static_cast<int64_t>(st_k);
+        const uint32_t dst = lds0 + st * STAGE + 1024 * NLD * wave;
+#pragma unroll
+        for (int q = 0; q < NLD; q++) {
+            dma16(wb, woff[q], dst + 1024 * q);
+            dma16(xb, xoff[q], dst + OPB + 1024 * q);
+        }
+    };
+    // fragment slot of this lane for k-half h
+    int foff[H];
+#pragma unroll
+    for (int h = 0; h < H; h++) foff[h] = RB * r + 16 * ((4 * h + g) ^ ((r / BANKROWS) % CPR));
+
+    floatx4 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int c = 0; c < TM; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // X fragments of a k-half are held for the whole half; W fragments are read one 16-row
+    // tile ahead of their MFMAs, so few registers hold operands
+    auto bfrags = [&](const uint8_t* S, int fo, u32x4 (&bf)[TM]) {
+#pragma unroll
+        for (int c = 0; c < TM; c++)
+            bf[c] = *reinterpret_cast<const u32x4*>(S + OPB + 16 * RB * (TM * wm + c) + fo);
+    };
+    auto afrag = [&](const uint8_t* S, int fo, int i) {
+        return *reinterpret_cast<const u32x4*>(S + 16 * RB * (TN * wn + i) + fo);
+    };
+
+    // transfers of the first NST - 1 steps in flight
+#pragma unroll
+    for (int p = 0; p < NST - 1; p++)
+        if (s0 + p < s1) issue(s0 + p, p);
+    for (uint32_t sk = s0; sk < s1; sk++) {
+        const int st = (sk - s0) % NST;
+        // this wave's transfers into stage st have landed (the NST - 2 younger steps' may
+        // still be in flight); after the barrier everyone's have, and every wave is done
+        // reading the stage the step before used, which the transfer below refills
+        if (NST > 2 && sk + NST - 2 < s1) {
+            constexpr int younger = (NST > 2 ? NST - 2 : 0) * 2 * NLD;
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(younger) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        const uint8_t* S = lds + st * STAGE;
+        u32x4 bf0[TM], bf1[TM];
+        bfrags(S, foff[0], bf0);
+        u32x4 an = afrag(S, foff[0], 0);
+        if (sk + NST - 1 < s1) issue(sk + NST - 1, (st + NST - 1) % NST);
+#pragma unroll
+        for (int i = 0; i < TN; i++) {
+            const u32x4 ac = an;
+            if (i + 1 < TN) an = afrag(S, foff[0], i + 1);
+            else if (H > 1) an = afrag(S, foff[H - 1], 0);
+            if (H > 1 && i == TN / 2) bfrags(S, foff[H - 1], bf1);
+#pragma unroll
+            for (int c = 0; c < TM; c++) acc[i][c] = mfma16(ac, bf0[c], acc[i][c]);
+        }
+        if (H > 1) {
+#pragma unroll
+            for (int i = 0; i < TN; i++) {
+                const u32x4 ac = an;
+                if (i + 1 < TN) an = afrag(S, foff[H - 1], i + 1);
+#pragma unroll
+                for (int c = 0; c < TM; c++) acc[i][c] = mfma16(ac, bf1[c], acc[i][c]);
+            }
+        }
+    }
+
+    static_assert(BM / 2 * BN * 4 <= NST * STAGE, "split-K epilogue half tile must fit the LDS");
+    if (gridDim.y > 1) {  // one of several K slices
+        add_tile<BN, BM, TN, TM, 64 * NWV>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
+                                           static_cast<int>(threadIdx.x));
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int c = 0; c < TM; c++)
+            store_out(a, m0 + (TM * wm + c) * 16 + (lane & 15), n0 + (TN * wn + i) * 16 + 4 * (lane >> 4), acc[i][c]);
+}
+
 struct Variant {
     const char* name;
-    int kind;  // 0 skinny, 1 tiled, 2 wide
+    int kind;  // 0 skinny, 1 tiled, 2 wide, 3 dma (bf16 W, both operands by LDS DMA)
     int rt, nw, u;
     int bn, bm;
     int xnear;  // skinny: X one group ahead in one register set instead of with the ring
@@ -1436,6 +1583,7 @@ const Variant kVariants[] = {
     {"skinny rt4 u2 w4 ks", 0, 4, 4, 2, 0, 0, 0, 0, 1}, {"skinny rt4 u2 w4 xt ks", 0, 4, 4, 2, 0, 0, 0, 1, 1},
     {"skinny rt4 u2 w8 xd", 0, 4, 8, 2, 0, 0, 0, 2},    {"skinny rt4 u2 w4 xd", 0, 4, 4, 2, 0, 0, 0, 2},
     {"skinny rt4 u2 w8 xd ks", 0, 4, 8, 2, 0, 0, 0, 2, 1},
+    {"dma 256x256", 3, 0, 8, 2, 256, 256},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1491,6 +1639,7 @@ struct SliceModel {
 };
 constexpr SliceModel kTiledModel = {2, 3.2, 1.66};  // 128 x 128 tile, 4 waves
 constexpr SliceModel kWideModel = {1, 22.0, 2.07};   // 256 x 256 tile, 8 waves
+constexpr SliceModel kDmaModel = {1, 22.0, 1.75};    // 256 x 256 tile, operands by LDS DMA
 constexpr double kAtomUs = 3.3e-6;
 
 struct SlicePlan {
@@ -1542,6 +1691,19 @@ hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
+template <int BK, int NST>
+hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s)
+{
+    constexpr size_t lds = NST * (256 + 256) * BK * 2;
+    static uint64_t attr_done = 0;  // devices the LDS limit was raised on
+    const void* fn = reinterpret_cast<const void*>(&gemm_dma<8, BK, NST>);
+    hipError_t e = allow_lds(fn, lds, attr_done);
+    if (e != hipSuccess) return e;
+    const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
+    e = launch_sliced(fn, g, tiles, 512, lds, s);
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
 template <int SRC, bool CONTIG>
 hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
 {
@@ -1582,7 +1744,7 @@ uint32_t resolve_split(const Variant& v, int64_t N, int64_t K, int64_t M, int32_
     else if (v.kind == 1)
         ks = v.bn == 128 && v.bm == 128 ? plan_slices(kTiledModel, N, K, M, 128, 128).ks : 1;
     else
-        ks = plan_slices(kWideModel, N, K, M, 256, 256).ks;
+        ks = plan_slices(v.kind == 3 ? kDmaModel : kWideModel, N, K, M, 256, 256).ks;
     ks = ks < 1 ? 1 : ks > G ? G : ks;
     const uint32_t kg = (G + ks - 1) / ks;
     return (G + kg - 1) / kg;
@@ -1592,6 +1754,10 @@ template <int SRC, bool CONTIG>
 hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
+    if (v.kind == 3) {
+        if constexpr (SRC == UW_W_BF16) return launch_dma_t<64, 2>(g, s);
+        return hipErrorNotSupported;  // (rejected before: bf16 weights only)
+    }
     // (a "ks" variant is its neighbour's kernel with a K split chosen for it; the split is
     // in g.kgroups, set by the caller)
     if (v.kind == 0) {
@@ -1730,8 +1896,6 @@ uw_status launch_gate_up_gemm(const uw_gemm_args* gate, const uw_gemm_args* up, 
 
 int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
 {
-    (void)K;
-    (void)src;
     if (M <= 64) {
         // the most rows per workgroup (X reused across more weight rows) that still gives
         // ~200 workgroups of 16 * rt rows
@@ -1740,8 +1904,13 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
         if (tiles >= 2 * 200) return 3;                // rt2 u4 w4
         return M > 16 ? 2 : 1;                // rt1 u4 w4 / rt1 u4 w8
     }
-    // the 128 x 128 or the 256 x 256 kernel, each with its best K split
+    // the 128 x 128 or the 256 x 256 kernel, each with its best K split (for bf16 weights
+    // the 256 x 256 tile fed by LDS DMA, the last variant)
     const double t_tiled = plan_slices(kTiledModel, N, K, M, 128, 128).us;
+    if (src == UW_W_BF16 && 2 * N * K < (int64_t{1} << 32) && 2 * M * K < (int64_t{1} << 32)) {
+        const double t_dma = plan_slices(kDmaModel, N, K, M, 256, 256).us;
+        return t_dma < t_tiled ? kNumVariants - 1 : 6;
+    }
     const double t_wide = plan_slices(kWideModel, N, K, M, 256, 256).us;
     return t_wide < t_tiled ? 9 : 6;
 }
@@ -1765,6 +1934,8 @@ uw_status make_args(const uw_gemm_args* p, GemmArgs& g, bool& contig, int& v)
     if (p->split_k < 0 || p->split_k > h->K / 64) return fail(UW_EINVAL, "split_k %d outside 0..K/64", p->split_k);
     if (kVariants[v].kind == 0 && 2 * p->M * p->ldx + 32 * h->K >= (int64_t{1} << 32))
         return fail(UW_EUNSUPPORTED, "variant %d addresses X and W with 32-bit offsets: ldx or K too large", v);
+    if (kVariants[v].kind == 3 && (2 * p->M * p->ldx >= (int64_t{1} << 32) || 2 * h->N * h->K >= (int64_t{1} << 32)))
+        return fail(UW_EUNSUPPORTED, "variant %d addresses X and W with 32-bit offsets: X or W too large", v);
     std::memset(&g, 0, sizeof g);
     g.x = p->d_x;
     g.wplane = p->d_wplane;
@@ -1908,6 +2079,7 @@ int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t sr
     // a "ks" variant exists only where it cuts K (elsewhere it would be its unsplit neighbour)
     if (v.kind == 0 && v.ks && uw::skinny_slices(N, K, v.rt) < 2) return 0;
     if (v.kind == 0 && v.xt == 2 && src != UW_W_DIRECT) return 0;  // X by LDS DMA: built for direct planes only
+    if (v.kind == 3) return src == UW_W_BF16 && M >= 1 && 2 * N * K < (int64_t{1} << 32) && 2 * M * K < (int64_t{1} << 32);
     if (v.kind == 0) return M >= 1 && M <= (v.rt == 2 && v.nw == 8 && !v.xnear ? 32 : 64);  // rt2 w8 spills beyond 32 rows of X
     return M >= 1;
 }

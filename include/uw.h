@@ -269,10 +269,12 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
 /* Kernel variants of uw_recon_gemm (tile shape per CU and pipelining depth, "How the
  * reconstructive matmul works": wider tiles for large batches, deeper buffers for small
  * ones). uw_variant_count() variants exist; uw_variant_name() describes one;
- * uw_variant_supports() says whether a variant accepts (N, K, M, src). Every variant
- * takes every src, so the plain bf16 GEMM of the full-decode pipeline ("Four ways to use
- * compressed weights": the decoded weights go to a standard matrix multiply) is the same
- * kernel family on the UW_W_BF16 loader. */
+ * uw_variant_supports() says whether a variant accepts (N, K, M, src). The variants take
+ * every src with two exceptions, so the plain bf16 GEMM of the full-decode pipeline ("Four
+ * ways to use compressed weights": the decoded weights go to a standard matrix multiply) is
+ * the same kernel family on the UW_W_BF16 loader: the skinny "... xd" variants (X by LDS DMA)
+ * take direct planes only, and "dma 256x256" (both operands sent from memory straight into
+ * LDS, no rebuild step) takes UW_W_BF16 only, with X and W each under 4 GiB. */
 int uw_variant_count(void);
 const char* uw_variant_name(int variant);
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
