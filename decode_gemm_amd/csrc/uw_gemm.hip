@@ -1416,32 +1416,28 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
 // Plain bf16 GEMM for large M (the GEMM half of the full-decode and expand pipelines):
 // 256 x 256 output tile of 8 waves (4 x 2, 64 x 128 each), both operands sent from global
 // memory straight into LDS with global_load_lds_dwordx4, so no VGPR holds them on the way
-// and no LDS store instruction is issued. K advances BK (64 or 32) per step through NST
-// LDS stages (2 x 64 KB, or 4 x 32 KB: transfers three steps ahead).
+// and no LDS store instruction is issued. K advances 64 per step through two 64 KB stages.
 //
-// LDS layout of one operand in one stage: row rho (0..255) of the tile at RB rho (RB = 2 BK
-// bytes), its 16-byte chunk c (k 8c .. 8c+7 of the step) at slot c ^ f(rho), with
-// f(rho) = (rho / (256 / RB)) mod (BK / 8): rows that share LDS banks get different slots.
-// A transfer covers 1 KB: lane l lands at 16 l, i.e. row RPI i + l / CPR, slot l mod CPR
-// (RPI rows of CPR chunks per transfer), so it fetches chunk (l mod CPR) ^ f(rho); the
-// lanes of a row still read the row's whole segment. A fragment read (lane 16 g + r: row
-// 16 t + r, chunk 4 h + g) then hits 16 distinct 16-byte bank groups in every 16 lanes.
-template <int NWV, int BK, int NST>
-__global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
+// LDS layout of one operand in one stage: row rho (0..255) of the tile at 128 rho, its
+// 16-byte chunk c (k 8c .. 8c+7 of the step) at slot c ^ ((rho >> 1) & 7): the two rows
+// that share a 256-byte bank period, and the rows of other periods, get different slots.
+// A transfer covers 1 KB: lane l lands at 16 l, i.e. row 8 i + l / 8, slot l mod 8, so it
+// fetches chunk (l mod 8) ^ ((rho >> 1) & 7) of that row; the eight lanes of a row still
+// read its whole 128-byte segment. A fragment read (lane 16 g + r: row 16 t + r, chunk
+// 4 h + g) hits 16 distinct 16-byte bank groups in every 16 lanes.
+//
+// One barrier per step, placed where every fragment of the step is already in registers:
+// after it, the stage the step used takes the transfers of the step after next, the X
+// fragments of the next step's first k-half are read, and the step's second k-half is
+// multiplied from registers meanwhile, so the matrix cores do not wait for LDS reads at
+// the start of a step.
+__global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
 {
-    constexpr int BN = 256, BM = 256;
-    constexpr int WGN = NWV / 2;       // waves along N
-    constexpr int TN = BN / 16 / WGN;  // 16-row W tiles per wave
-    constexpr int TM = 8;              // 16-row X tiles per wave
-    constexpr int RB = 2 * BK;         // bytes of one row of a stage
-    constexpr int CPR = BK / 8;        // 16-byte chunks per row
-    constexpr int RPI = 1024 / RB;     // rows per transfer
-    constexpr int BANKROWS = 256 / RB; // rows per 256-byte bank period
-    constexpr int OPB = 256 * RB;      // one operand, one stage
+    constexpr int BN = 256, BM = 256, NWV = 8;
+    constexpr int TN = 4, TM = 8;   // 16-row W and X tiles per wave (waves 4 along N, 2 along M)
+    constexpr int OPB = 256 * 128;  // one operand, one stage
     constexpr int STAGE = 2 * OPB;
-    constexpr int NLD = 256 / RPI / NWV;  // transfers per wave per operand per step
-    constexpr int H = BK / 32;            // MFMA k-halves per step
-    static_assert(NST * STAGE <= 160 * 1024 && NLD >= 1, "stage shape");
+    constexpr int NLD = 32 / NWV;   // transfers per wave per operand per step
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t tiles_n = static_cast<uint32_t>((a.N + BN - 1) / BN);
@@ -1455,16 +1451,14 @@ __global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
     const uint32_t G = static_cast<uint32_t>(a.K >> 6);
     uint32_t j0, j1;
     k_slice(a, G, j0, j1);
-    // steps of BK over this K slice
-    const uint32_t s0 = j0 * (64 / BK), s1 = j1 * (64 / BK);
 
     // per-lane byte offsets of this wave's transfers (rows past N or M read the last row;
     // the host keeps every offset below 2^32)
     uint32_t woff[NLD], xoff[NLD];
 #pragma unroll
     for (int q = 0; q < NLD; q++) {
-        const int rho = RPI * (NLD * wave + q) + lane / CPR;
-        const int kap = (lane % CPR) ^ ((rho / BANKROWS) % CPR);
+        const int rho = 8 * (NLD * wave + q) + (lane >> 3);
+        const int kap = (lane & 7) ^ ((rho >> 1) & 7);
         const int64_t n = n0 + rho < a.N ? n0 + rho : a.N - 1;
         const int64_t m = m0 + rho < a.M ? m0 + rho : a.M - 1;
         woff[q] = static_cast<uint32_t>(2 * n * a.K + 16 * kap);
@@ -1473,9 +1467,9 @@ __global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
     const uint32_t lds0 = lds_offset(lds);
     const uint8_t* const wbase = static_cast<const uint8_t*>(a.wplane);
     const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(a.x);
-    auto issue = [&](uint32_t st_k, int st) {
-        const uint8_t* wb = wbase + RB * static_cast<int64_t>(st_k);
-        const uint8_t* xb = xbase + RB * static_cast<int64_t>(st_k);
+    auto issue = [&](uint32_t j, int st) {
+        const uint8_t* wb = wbase + 128 * static_cast<int64_t>(j);
+        const uint8_t* xb = xbase + 128 * static_cast<int64_t>(j);
         const uint32_t dst = lds0 + st * STAGE + 1024 * NLD * wave;
 #pragma unroll
         for (int q = 0; q < NLD; q++) {
@@ -1483,10 +1477,17 @@ __global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
             dma16(xb, xoff[q], dst + OPB + 1024 * q);
         }
     };
-    // fragment slot of this lane for k-half h
-    int foff[H];
+    // fragment slots of this lane for the two k-halves
+    const int foff0 = 128 * r + 16 * ((0 + g) ^ ((r >> 1) & 7));
+    const int foff1 = 128 * r + 16 * ((4 + g) ^ ((r >> 1) & 7));
+    auto bfrags = [&](const uint8_t* S, int fo, u32x4 (&bf)[TM]) {
 #pragma unroll
-    for (int h = 0; h < H; h++) foff[h] = RB * r + 16 * ((4 * h + g) ^ ((r / BANKROWS) % CPR));
+        for (int c = 0; c < TM; c++)
+            bf[c] = *reinterpret_cast<const u32x4*>(S + OPB + 2048 * (TM * wm + c) + fo);
+    };
+    auto afrag = [&](const uint8_t* S, int fo, int i) {
+        return *reinterpret_cast<const u32x4*>(S + 2048 * (TN * wn + i) + fo);
+    };
 
     floatx4 acc[TN][TM];
 #pragma unroll
@@ -1494,59 +1495,50 @@ __global__ void __launch_bounds__(64 * NWV) gemm_dma(GemmArgs a)
 #pragma unroll
         for (int c = 0; c < TM; c++) acc[i][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // X fragments of a k-half are held for the whole half; W fragments are read one 16-row
-    // tile ahead of their MFMAs, so few registers hold operands
-    auto bfrags = [&](const uint8_t* S, int fo, u32x4 (&bf)[TM]) {
-#pragma unroll
-        for (int c = 0; c < TM; c++)
-            bf[c] = *reinterpret_cast<const u32x4*>(S + OPB + 16 * RB * (TM * wm + c) + fo);
-    };
-    auto afrag = [&](const uint8_t* S, int fo, int i) {
-        return *reinterpret_cast<const u32x4*>(S + 16 * RB * (TN * wn + i) + fo);
-    };
-
-    // transfers of the first NST - 1 steps in flight
-#pragma unroll
-    for (int p = 0; p < NST - 1; p++)
-        if (s0 + p < s1) issue(s0 + p, p);
-    for (uint32_t sk = s0; sk < s1; sk++) {
-        const int st = (sk - s0) % NST;
-        // this wave's transfers into stage st have landed (the NST - 2 younger steps' may
-        // still be in flight); after the barrier everyone's have, and every wave is done
-        // reading the stage the step before used, which the transfer below refills
-        if (NST > 2 && sk + NST - 2 < s1) {
-            constexpr int younger = (NST > 2 ? NST - 2 : 0) * 2 * NLD;
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(younger) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+    u32x4 bf0[TM], an;
+    if (j0 < j1) {
+        issue(j0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if (j0 + 1 < j1) issue(j0 + 1, 1);
+        bfrags(lds, foff0, bf0);
+        an = afrag(lds, foff0, 0);
+    }
+    for (uint32_t j = j0; j < j1; j++) {
+        const int st = (j - j0) & 1;
         const uint8_t* S = lds + st * STAGE;
-        u32x4 bf0[TM], bf1[TM];
-        bfrags(S, foff[0], bf0);
-        u32x4 an = afrag(S, foff[0], 0);
-        if (sk + NST - 1 < s1) issue(sk + NST - 1, (st + NST - 1) % NST);
+        // first k-half from the X fragments already in registers; the rest of the step's
+        // fragments are read meanwhile (W one tile ahead of its MFMAs)
+        u32x4 a1[TN], bf1[TM];
 #pragma unroll
         for (int i = 0; i < TN; i++) {
             const u32x4 ac = an;
-            if (i + 1 < TN) an = afrag(S, foff[0], i + 1);
-            else if (H > 1) an = afrag(S, foff[H - 1], 0);
-            if (H > 1 && i == TN / 2) bfrags(S, foff[H - 1], bf1);
+            if (i + 1 < TN) an = afrag(S, foff0, i + 1);
+            a1[i] = afrag(S, foff1, i);
+            if (i == 0) bfrags(S, foff1, bf1);
 #pragma unroll
             for (int c = 0; c < TM; c++) acc[i][c] = mfma16(ac, bf0[c], acc[i][c]);
         }
-        if (H > 1) {
+        // every wave holds all of this step's fragments and (after the wait) its transfers
+        // of the next step have landed: after the barrier this stage takes the step after
+        // next, and the next step's first X fragments are read. (Unconditional, also in
+        // the last step: behind a branch the compiler would make the second k-half's
+        // MFMAs wait for those reads. The scheduling barriers keep the second k-half's
+        // MFMAs after the barrier and the reads, where they hide the reads' latency.)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 2 < j1) issue(j + 2, st);
+        bfrags(lds + (st ^ 1) * STAGE, foff0, bf0);
+        an = afrag(lds + (st ^ 1) * STAGE, foff0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < TN; i++) {
-                const u32x4 ac = an;
-                if (i + 1 < TN) an = afrag(S, foff[H - 1], i + 1);
+        for (int i = 0; i < TN; i++)
 #pragma unroll
-                for (int c = 0; c < TM; c++) acc[i][c] = mfma16(ac, bf1[c], acc[i][c]);
-            }
-        }
+            for (int c = 0; c < TM; c++) acc[i][c] = mfma16(a1[i], bf1[c], acc[i][c]);
     }
 
-    static_assert(BM / 2 * BN * 4 <= NST * STAGE, "split-K epilogue half tile must fit the LDS");
+    static_assert(BM / 2 * BN * 4 <= 2 * STAGE, "split-K epilogue half tile must fit the LDS");
     if (gridDim.y > 1) {  // one of several K slices
         add_tile<BN, BM, TN, TM, 64 * NWV>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
                                            static_cast<int>(threadIdx.x));
@@ -1691,12 +1683,11 @@ hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
-template <int BK, int NST>
-hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s)
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s)
 {
-    constexpr size_t lds = NST * (256 + 256) * BK * 2;
+    constexpr size_t lds = 2 * (256 + 256) * 64 * 2;
     static uint64_t attr_done = 0;  // devices the LDS limit was raised on
-    const void* fn = reinterpret_cast<const void*>(&gemm_dma<8, BK, NST>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_dma);
     hipError_t e = allow_lds(fn, lds, attr_done);
     if (e != hipSuccess) return e;
     const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
@@ -1755,7 +1746,7 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
     if (v.kind == 3) {
-        if constexpr (SRC == UW_W_BF16) return launch_dma_t<64, 2>(g, s);
+        if constexpr (SRC == UW_W_BF16) return launch_dma(g, s);
         return hipErrorNotSupported;  // (rejected before: bf16 weights only)
     }
     // (a "ks" variant is its neighbour's kernel with a K split chosen for it; the split is
