@@ -194,6 +194,21 @@ def test_variants_table():
     assert not uw.variant_supports(0, 4096, 100, 1, uw.W_IDX)
 
 
+def test_dma_variant_takes_bf16_weights_within_32_bit_offsets():
+    """The LDS-DMA 256x256 kernel streams bf16 operands only (no rebuild step), and it
+    addresses X and W with 32-bit offsets: it reports no support for the compressed planes
+    or for an operand of 4 GiB or more."""
+    names = [uw.variant_name(v) for v in range(uw.variant_count())]
+    v = names.index("dma 256x256")
+    assert uw.variant_supports(v, 14336, 4096, 4096, uw.W_BF16)
+    assert uw.variant_supports(v, 4096, 14336, 1, uw.W_BF16)
+    for src in (uw.W_EXP, uw.W_IDX, uw.W_DIRECT):
+        assert not uw.variant_supports(v, 14336, 4096, 4096, src)
+    assert not uw.variant_supports(v, 1 << 18, 8192, 64, uw.W_BF16)   # W: 4 GiB of bf16
+    assert not uw.variant_supports(v, 8192, 8192, 1 << 18, uw.W_BF16)  # X: 4 GiB of bf16
+    assert not uw.variant_supports(v, 4096, 4096, 0, uw.W_BF16)
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     """Importing the binding before PyTorch must not load a second HIP runtime: libuw and
     the tensors it is given have to share PyTorch's (a second runtime finds no device)."""
