@@ -1431,13 +1431,17 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
 // fragments of the next step's first k-half are read, and the step's second k-half is
 // multiplied from registers meanwhile, so the matrix cores do not wait for LDS reads at
 // the start of a step.
+template <int BM, int NST>
 __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
 {
-    constexpr int BN = 256, BM = 256, NWV = 8;
-    constexpr int TN = 4, TM = 8;   // 16-row W and X tiles per wave (waves 4 along N, 2 along M)
-    constexpr int OPB = 256 * 128;  // one operand, one stage
-    constexpr int STAGE = 2 * OPB;
-    constexpr int NLD = 32 / NWV;   // transfers per wave per operand per step
+    constexpr int BN = 256, NWV = 8;
+    constexpr int TN = 4, TM = BM / 32;  // 16-row W and X tiles per wave (waves 4 along N, 2 along M)
+    constexpr int OPB = BN * 128;        // W of one stage
+    constexpr int OPX = BM * 128;        // X of one stage
+    constexpr int STAGE = OPB + OPX;
+    constexpr int NLD = BN / 8 / NWV;    // W transfers per wave per step
+    constexpr int NLX = BM / 8 / NWV;    // X transfers per wave per step
+    static_assert(NST >= 2 && NST * STAGE <= 160 * 1024 && NLX >= 1, "stage shape");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t tiles_n = static_cast<uint32_t>((a.N + BN - 1) / BN);
@@ -1454,14 +1458,19 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
 
     // per-lane byte offsets of this wave's transfers (rows past N or M read the last row;
     // the host keeps every offset below 2^32)
-    uint32_t woff[NLD], xoff[NLD];
+    uint32_t woff[NLD], xoff[NLX];
 #pragma unroll
     for (int q = 0; q < NLD; q++) {
         const int rho = 8 * (NLD * wave + q) + (lane >> 3);
         const int kap = (lane & 7) ^ ((rho >> 1) & 7);
         const int64_t n = n0 + rho < a.N ? n0 + rho : a.N - 1;
-        const int64_t m = m0 + rho < a.M ? m0 + rho : a.M - 1;
         woff[q] = static_cast<uint32_t>(2 * n * a.K + 16 * kap);
+    }
+#pragma unroll
+    for (int q = 0; q < NLX; q++) {
+        const int rho = 8 * (NLX * wave + q) + (lane >> 3);
+        const int kap = (lane & 7) ^ ((rho >> 1) & 7);
+        const int64_t m = m0 + rho < a.M ? m0 + rho : a.M - 1;
         xoff[q] = static_cast<uint32_t>(2 * m * a.ldx + 16 * kap);
     }
     const uint32_t lds0 = lds_offset(lds);
@@ -1470,12 +1479,11 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
     auto issue = [&](uint32_t j, int st) {
         const uint8_t* wb = wbase + 128 * static_cast<int64_t>(j);
         const uint8_t* xb = xbase + 128 * static_cast<int64_t>(j);
-        const uint32_t dst = lds0 + st * STAGE + 1024 * NLD * wave;
+        const uint32_t dst = lds0 + st * STAGE;
 #pragma unroll
-        for (int q = 0; q < NLD; q++) {
-            dma16(wb, woff[q], dst + 1024 * q);
-            dma16(xb, xoff[q], dst + OPB + 1024 * q);
-        }
+        for (int q = 0; q < NLD; q++) dma16(wb, woff[q], dst + 1024 * (NLD * wave + q));
+#pragma unroll
+        for (int q = 0; q < NLX; q++) dma16(xb, xoff[q], dst + OPB + 1024 * (NLX * wave + q));
     };
     // fragment slots of this lane for the two k-halves
     const int foff0 = 128 * r + 16 * ((0 + g) ^ ((r >> 1) & 7));
@@ -1500,12 +1508,14 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
         issue(j0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j0 + 1 < j1) issue(j0 + 1, 1);
+#pragma unroll
+        for (int p = 1; p < NST; p++)
+            if (j0 + p < j1) issue(j0 + p, p);
         bfrags(lds, foff0, bf0);
         an = afrag(lds, foff0, 0);
     }
     for (uint32_t j = j0; j < j1; j++) {
-        const int st = (j - j0) & 1;
+        const int st = (j - j0) % NST, sn = (st + 1) % NST;
         const uint8_t* S = lds + st * STAGE;
         // first k-half from the X fragments already in registers; the rest of the step's
         // fragments are read meanwhile (W one tile ahead of its MFMAs)
@@ -1526,11 +1536,17 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
         // MFMAs wait for those reads. The scheduling barriers keep the second k-half's
         // MFMAs after the barrier and the reads, where they hide the reads' latency.)
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // (with NST stages the NST - 2 steps after the next may still be in flight)
+        if (NST > 2 && j + NST - 1 < j1) {
+            constexpr int younger = (NST > 2 ? NST - 2 : 0) * (NLD + NLX);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(younger) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         __syncthreads();
-        if (j + 2 < j1) issue(j + 2, st);
-        bfrags(lds + (st ^ 1) * STAGE, foff0, bf0);
-        an = afrag(lds + (st ^ 1) * STAGE, foff0, 0);
+        if (j + NST < j1) issue(j + NST, st);
+        bfrags(lds + sn * STAGE, foff0, bf0);
+        an = afrag(lds + sn * STAGE, foff0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TN; i++)
@@ -1538,7 +1554,7 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
             for (int c = 0; c < TM; c++) acc[i][c] = mfma16(a1[i], bf1[c], acc[i][c]);
     }
 
-    static_assert(BM / 2 * BN * 4 <= 2 * STAGE, "split-K epilogue half tile must fit the LDS");
+    static_assert(BM / 2 * BN * 4 <= NST * STAGE, "split-K epilogue half tile must fit the LDS");
     if (gridDim.y > 1) {  // one of several K slices
         add_tile<BN, BM, TN, TM, 64 * NWV>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
                                            static_cast<int>(threadIdx.x));
@@ -1575,7 +1591,7 @@ const Variant kVariants[] = {
     {"skinny rt4 u2 w4 ks", 0, 4, 4, 2, 0, 0, 0, 0, 1}, {"skinny rt4 u2 w4 xt ks", 0, 4, 4, 2, 0, 0, 0, 1, 1},
     {"skinny rt4 u2 w8 xd", 0, 4, 8, 2, 0, 0, 0, 2},    {"skinny rt4 u2 w4 xd", 0, 4, 4, 2, 0, 0, 0, 2},
     {"skinny rt4 u2 w8 xd ks", 0, 4, 8, 2, 0, 0, 0, 2, 1},
-    {"dma 256x256", 3, 0, 8, 2, 256, 256},
+    {"dma 256x256", 3, 0, 8, 2, 256, 256},              {"dma 256x128 s3", 3, 0, 8, 3, 256, 128},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1683,14 +1699,15 @@ hipError_t launch_tiled_t(const GemmArgs& g, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
+template <int BM, int NST>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s)
 {
-    constexpr size_t lds = 2 * (256 + 256) * 64 * 2;
+    constexpr size_t lds = NST * (256 + BM) * 128;
     static uint64_t attr_done = 0;  // devices the LDS limit was raised on
-    const void* fn = reinterpret_cast<const void*>(&gemm_dma);
+    const void* fn = reinterpret_cast<const void*>(&gemm_dma<BM, NST>);
     hipError_t e = allow_lds(fn, lds, attr_done);
     if (e != hipSuccess) return e;
-    const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + 255) / 256));
+    const uint32_t tiles = static_cast<uint32_t>(((g.N + 255) / 256) * ((g.M + BM - 1) / BM));
     e = launch_sliced(fn, g, tiles, 512, lds, s);
     return e != hipSuccess ? e : hipGetLastError();
 }
@@ -1735,7 +1752,7 @@ uint32_t resolve_split(const Variant& v, int64_t N, int64_t K, int64_t M, int32_
     else if (v.kind == 1)
         ks = v.bn == 128 && v.bm == 128 ? plan_slices(kTiledModel, N, K, M, 128, 128).ks : 1;
     else
-        ks = plan_slices(v.kind == 3 ? kDmaModel : kWideModel, N, K, M, 256, 256).ks;
+        ks = plan_slices(v.kind == 3 ? kDmaModel : kWideModel, N, K, M, 256, v.kind == 3 ? v.bm : 256).ks;
     ks = ks < 1 ? 1 : ks > G ? G : ks;
     const uint32_t kg = (G + ks - 1) / ks;
     return (G + kg - 1) / kg;
@@ -1746,7 +1763,7 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
     if (v.kind == 3) {
-        if constexpr (SRC == UW_W_BF16) return launch_dma(g, s);
+        if constexpr (SRC == UW_W_BF16) return v.bm == 128 ? launch_dma<128, 3>(g, s) : launch_dma<256, 2>(g, s);
         return hipErrorNotSupported;  // (rejected before: bf16 weights only)
     }
     // (a "ks" variant is its neighbour's kernel with a K split chosen for it; the split is
@@ -1900,7 +1917,10 @@ int default_variant(int64_t N, int64_t K, int64_t M, int32_t src)
     const double t_tiled = plan_slices(kTiledModel, N, K, M, 128, 128).us;
     if (src == UW_W_BF16 && 2 * N * K < (int64_t{1} << 32) && 2 * M * K < (int64_t{1} << 32)) {
         const double t_dma = plan_slices(kDmaModel, N, K, M, 256, 256).us;
-        return t_dma < t_tiled ? kNumVariants - 1 : 6;
+        int dma = 9;  // the 256 x 256 DMA variant
+        for (int v = 0; v < kNumVariants; v++)
+            if (kVariants[v].kind == 3 && kVariants[v].bm == 256) dma = v;
+        return t_dma < t_tiled ? dma : 6;
     }
     const double t_wide = plan_slices(kWideModel, N, K, M, 256, 256).us;
     return t_wide < t_tiled ? 9 : 6;

@@ -273,8 +273,9 @@ uw_status uw_recon_gemm_gate_up(const uw_gemm_args* gate, const uw_gemm_args* up
  * every src with two exceptions, so the plain bf16 GEMM of the full-decode pipeline ("Four
  * ways to use compressed weights": the decoded weights go to a standard matrix multiply) is
  * the same kernel family on the UW_W_BF16 loader: the skinny "... xd" variants (X by LDS DMA)
- * take direct planes only, and "dma 256x256" (both operands sent from memory straight into
- * LDS, no rebuild step) takes UW_W_BF16 only, with X and W each under 4 GiB. */
+ * take direct planes only, and the "dma ..." variants (both operands sent from memory straight
+ * into LDS, no rebuild step: a 256x256 tile through two stages, or 256x128 through three) take
+ * UW_W_BF16 only, with X and W each under 4 GiB. */
 int uw_variant_count(void);
 const char* uw_variant_name(int variant);
 int uw_variant_supports(int variant, int64_t N, int64_t K, int64_t M, int32_t src);
