@@ -55,6 +55,8 @@ struct GemmArgs {
     const uint8_t* dside;  // direct plane: raw exponents, 64 bytes per raw (row, group)
     uint32_t tiles;        // direct plane: ceil(N / 16)
     uint32_t kgroups;      // K split: 64-groups per K slice (blockIdx.y), partial sums added into a zeroed Y; 0 = all
+    uint16_t* hout;        // SwiGLU epilogue (one K slice only): Y holds the gate projection's output and is
+    int64_t ldh;           // only read; the tile's result u goes out as hout[m][n] = bf16(silu(Y[m][n]) u)
 };
 
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c)
@@ -965,6 +967,52 @@ __device__ __forceinline__ void add_tile(const GemmArgs& a, float* ep, const flo
     }
 }
 
+// SwiGLU epilogue of a BN x BM tile (one K slice, a.hout set): the tile holds the up
+// projection's outputs u, Y the gate's; hout[m][n] = bf16(silu(Y[m][n]) u[m][n]). As in
+// add_tile, one m half at a time goes through LDS, so that a wave reads one whole Y row
+// segment (BN floats) per load instruction instead of 16 rows of an MFMA fragment.
+template <int BN, int BM, int TN, int TM, int NT>
+__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, float* ep, const floatx4 (&acc)[TN][TM], int64_t n0,
+                                            int64_t m0, int wn, int wm, int lane, int tid)
+{
+    constexpr int HR = BM / 2, Q = BN / 4;
+    static_assert(BN % 64 == 0 && TM * 16 == HR, "tile shape");
+    const bool vec = (a.ldy & 3) == 0 && (a.ldh & 3) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        __syncthreads();
+        if (wm == h) {
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+#pragma unroll
+                for (int c = 0; c < TM; c++) {
+                    const int nn = (wn * TN + i) * 16 + 4 * (lane >> 4), mm = c * 16 + (lane & 15);
+                    *reinterpret_cast<floatx4*>(ep + mm * BN + (nn ^ ((mm & 15) << 2))) = acc[i][c];
+                }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int e = tid; e < HR * Q; e += NT) {
+            const int mm = e / Q, nn = 4 * (e % Q);
+            const int64_t m = m0 + h * HR + mm, n = n0 + nn;
+            if (m >= a.M || n >= a.N) continue;
+            const floatx4 u4 = *reinterpret_cast<const floatx4*>(ep + mm * BN + (nn ^ ((mm & 15) << 2)));
+            const float* gp = a.y + m * a.ldy + n;
+            uint16_t* hp = a.hout + m * a.ldh + n;
+            if (vec && n + 3 < a.N) {
+                const floatx4 g4 = *reinterpret_cast<const floatx4*>(gp);
+                uint32_t o[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) o[q] = f32_to_bf16_rne(silu_mul(g4[q], u4[q]));
+                *reinterpret_cast<uint2*>(hp) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            } else {
+                for (int q = 0; q < 4; q++)
+                    if (n + q < a.N) hp[q] = static_cast<uint16_t>(f32_to_bf16_rne(silu_mul(gp[q], u4[q])));
+            }
+        }
+    }
+}
+
 // Y[0, M) x [0, N) = 0: rows m = blockIdx.y + k gridDim.y, four columns per thread (one
 // 16-byte store when ldy keeps the rows 16-byte aligned).
 __global__ void __launch_bounds__(256) zero_rows(float* y, int64_t ldy, int64_t M, int64_t N)
@@ -1200,6 +1248,10 @@ __global__ void __launch_bounds__(256) gemm_tiled(GemmArgs a)
         add_tile<BN, BM, C::TN, C::TM, 256>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane, tid);
         return;
     }
+    if (a.hout) {
+        swiglu_tile<BN, BM, C::TN, C::TM, 256>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane, tid);
+        return;
+    }
     // lane holds D[4*(lane/16) + q][lane%16] = Y^T: 4 consecutive n of one Y row
 #pragma unroll
     for (int i = 0; i < C::TN; i++)
@@ -1404,6 +1456,11 @@ __global__ void __launch_bounds__(512) gemm_wide(GemmArgs a)
                                       static_cast<int>(threadIdx.x));
         return;
     }
+    if (a.hout) {
+        swiglu_tile<BN, BM, TN, TM, 512>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
+                                         static_cast<int>(threadIdx.x));
+        return;
+    }
     // lane holds D[4*(lane/16) + q][lane%16] = Y^T: 4 consecutive n of one Y row
 #pragma unroll
     for (int i = 0; i < TN; i++)
@@ -1558,6 +1615,11 @@ __global__ void __launch_bounds__(512) gemm_dma(GemmArgs a)
     if (gridDim.y > 1) {  // one of several K slices
         add_tile<BN, BM, TN, TM, 64 * NWV>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
                                            static_cast<int>(threadIdx.x));
+        return;
+    }
+    if (a.hout) {
+        swiglu_tile<BN, BM, TN, TM, 64 * NWV>(a, reinterpret_cast<float*>(lds), acc, n0, m0, wn, wm, lane,
+                                              static_cast<int>(threadIdx.x));
         return;
     }
 #pragma unroll
@@ -2021,7 +2083,9 @@ uw_status launch_expand_direct(const uw_header* h, const uint8_t* d_direct, uint
     return UW_OK;
 }
 
-uw_status launch_gemm(const uw_gemm_args* p, void* stream, bool y_zeroed)
+namespace {
+
+uw_status gemm_launch(const uw_gemm_args* p, void* stream, bool y_zeroed, uint16_t* hout, int64_t ldh)
 {
     clear_error();
     if (!p || !p->h) return fail(UW_EINVAL, "NULL argument");
@@ -2035,6 +2099,13 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream, bool y_zeroed)
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const Variant& var = kVariants[v];
+    if (hout) {
+        // the tiled, wide and dma kernels end in store_out; a K split adds partial sums instead
+        if (var.kind == 0 || g.kgroups) return fail(UW_EUNSUPPORTED, "no SwiGLU epilogue for this variant or K split");
+        if (ldh < g.N || !aligned(hout, 8)) return fail(UW_EINVAL, "h: ldh must be >= N and h 8-byte aligned");
+        g.hout = hout;
+        g.ldh = ldh;
+    }
     // K split: Y is zeroed first (a kernel, not a memset, so the launch can be captured in
     // a graph) and every slice adds its part with fp32 atomics
     if (g.kgroups && !y_zeroed) {
@@ -2049,6 +2120,18 @@ uw_status launch_gemm(const uw_gemm_args* p, void* stream, bool y_zeroed)
     }
     if (e != hipSuccess) return fail(UW_EHIP, "GEMM launch failed: %s", hipGetErrorString(e));
     return UW_OK;
+}
+
+}  // namespace
+
+uw_status launch_gemm(const uw_gemm_args* p, void* stream, bool y_zeroed)
+{
+    return gemm_launch(p, stream, y_zeroed, nullptr, 0);
+}
+
+uw_status launch_gemm_swiglu(const uw_gemm_args* p, uint16_t* h, int64_t ldh, void* stream)
+{
+    return gemm_launch(p, stream, false, h, ldh);
 }
 
 }  // namespace uw

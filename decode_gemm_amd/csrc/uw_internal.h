@@ -55,6 +55,12 @@ uw_status launch_decode(const uw_header* h, const void* d_blob, void* d_out, int
                         void* stream);
 // y_zeroed: the caller has already cleared Y (a K-split launch then skips its own clearing)
 uw_status launch_gemm(const uw_gemm_args* a, void* stream, bool y_zeroed = false);
+// The up projection's GEMM with the SwiGLU in its epilogue: a->d_y holds the gate
+// projection's fp32 output (read only, leading dimension a->ldy) and the launch writes
+// h[m][n] = bf16(silu(gate) up) (leading dimension ldh, 8-byte aligned), the same bits as
+// the GEMM into Y followed by the separate activation kernel. UW_EUNSUPPORTED when the
+// variant (skinny) or a K split leaves no such epilogue; the caller then runs the two steps.
+uw_status launch_gemm_swiglu(const uw_gemm_args* a, uint16_t* h, int64_t ldh, void* stream);
 // An fp32 buffer Y[M][ld] (first N columns) that a fused gate/up launch clears on the way, for
 // the K-split launch that follows it on the same stream (16-byte aligned, ld a multiple of 4).
 struct ZeroTarget {

@@ -425,6 +425,33 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     return launch_gemm(&g, stream, y_zeroed);
 }
 
+// The up projection's GEMM with the SwiGLU in its epilogue (h = bf16(silu(g) u), g the gate's
+// output, u never stored); where the variant or a K split leaves no such epilogue, the GEMM
+// into u and the separate activation kernel.
+uw_status up_proj_swiglu(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, const float* g,
+                         float* u, uint16_t* h, int64_t ldf, void* stream)
+{
+    uw_gemm_args a;
+    std::memset(&a, 0, sizeof a);
+    a.M = M;
+    a.d_x = x;
+    a.ldx = ldx;
+    a.h = p.h;
+    a.d_blob = p.d_blob;
+    a.d_y = const_cast<float*>(g);
+    a.ldy = ldf;
+    a.variant = p.variant;
+    a.split_k = p.split_k;
+    a.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
+          : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
+    a.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
+    uw_status st = launch_gemm_swiglu(&a, h, ldf, stream);
+    if (st != UW_EUNSUPPORTED) return st;
+    clear_error();
+    if ((st = gemm_proj(p, slot, M, x, ldx, u, ldf, stream)) != UW_OK) return st;
+    return uw_swiglu(g, u, M * p.h->N, h, stream);
+}
+
 // gate, up and SwiGLU of a layer in one launch when both projections are direct planes
 // and the fused form applies; UW_EUNSUPPORTED otherwise (the caller runs them one by one).
 uw_status gate_up_fused(const uw_proj& gp, const uw_proj& up, int64_t M, const uint16_t* x, int64_t ldx, float* g,
@@ -558,8 +585,7 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
         if (r != UW_EUNSUPPORTED) return r;
         clear_error();
         if ((r = gemm_proj(L.gate, nullptr, M, d_x, lay.K, g, lay.Nff, s)) != UW_OK) return r;
-        if ((r = gemm_proj(L.up, nullptr, M, d_x, lay.K, u, lay.Nff, s)) != UW_OK) return r;
-        return uw_swiglu(g, u, mf, h, s);
+        return up_proj_swiglu(L.up, nullptr, M, d_x, lay.K, g, u, h, lay.Nff, s);
     };
 
     if (!decode_stream) {
@@ -574,15 +600,10 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
             if (both_direct(L, M)) {
                 st = direct_pair(L, stream, split_down ? &clear_y : nullptr, &cleared);
             } else {
-                for (int r = 0; r < 2 && st == UW_OK; r++) {
-                    const uint16_t* x;
-                    int64_t ldx, ldy;
-                    float* y;
-                    gemm_io(r, x, ldx, y, ldy);
-                    if ((st = decode_proj(role_of(L, r), slot(0), stream)) == UW_OK)
-                        st = gemm_proj(role_of(L, r), slot(0), M, x, ldx, y, ldy, stream);
-                }
-                if (st == UW_OK) st = uw_swiglu(g, u, mf, h, stream);
+                if ((st = decode_proj(L.gate, slot(0), stream)) == UW_OK)
+                    st = gemm_proj(L.gate, slot(0), M, d_x, lay.K, g, lay.Nff, stream);
+                if (st == UW_OK && (st = decode_proj(L.up, slot(0), stream)) == UW_OK)
+                    st = up_proj_swiglu(L.up, slot(0), M, d_x, lay.K, g, u, h, lay.Nff, stream);
             }
             if (st != UW_OK) break;
             if ((st = decode_proj(L.down, slot(0), stream)) != UW_OK) break;
@@ -617,6 +638,7 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
         release();
         return fail(UW_EHIP, "stream ordering failed");
     }
+    std::vector<char> swiglu_done(n_layers, 0);  // the layer's up GEMM ran the SwiGLU in its epilogue
     for (const Action& a : plan) {
         const uw_mlp_layer& L = layers[a.layer];
         if (a.kind == Action::DECODE) {
@@ -629,17 +651,22 @@ uw_status stack_forward(const uw_mlp_layer* layers, int n_layers, int64_t M, con
             int64_t ldx, ldy;
             float* y;
             gemm_io(a.role, x, ldx, y, ldy);
+            auto run = [&](const void* sl) -> uw_status {
+                if (a.role != 1) return gemm_proj(role_of(L, a.role), sl, M, x, ldx, y, ldy, ms);
+                swiglu_done[a.layer] = 1;  // h is written either way: by the epilogue or the activation kernel
+                return up_proj_swiglu(L.up, sl, M, d_x, lay.K, g, u, h, lay.Nff, ms);
+            };
             if (a.q < 0) {
-                if ((st = gemm_proj(role_of(L, a.role), nullptr, M, x, ldx, y, ldy, ms)) != UW_OK) break;
+                if ((st = run(nullptr)) != UW_OK) break;
                 continue;
             }
             const int s = a.q % slots;
             if (hipStreamWaitEvent(ms, decoded[s], 0) != hipSuccess) { st = fail(UW_EHIP, "wait failed"); break; }
-            if ((st = gemm_proj(role_of(L, a.role), slot(s), M, x, ldx, y, ldy, ms)) != UW_OK) break;
+            if ((st = run(slot(s))) != UW_OK) break;
             if (hipEventRecord(freed[s], ms) != hipSuccess) { st = fail(UW_EHIP, "event record failed"); break; }
         } else if (a.kind == Action::FUSED) {
             if ((st = direct_pair(L, ms)) != UW_OK) break;
-        } else {
+        } else if (!swiglu_done[a.layer]) {
             if ((st = uw_swiglu(g, u, mf, h, ms)) != UW_OK) break;
         }
     }

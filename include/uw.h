@@ -477,9 +477,14 @@ uw_status uw_swiglu(const float* d_g, const float* d_u, int64_t n, uint16_t* d_h
  * their own priorities). All layers must have the same shapes: gate and up N_ff x K, down
  * N_out x N_ff. Buffers are the caller's; nothing is allocated on the device.
  *
+ * Where the up projection runs a tiled, wide or dma variant in one K slice, the SwiGLU is
+ * computed in that GEMM's epilogue (from g and the tile's up outputs, the same bits as
+ * uw_swiglu) and u is not stored; elsewhere the up GEMM writes u and uw_swiglu follows.
+ *
  * Workspace, uw_mlp_stack_workspace: g and u (fp32 M x N_ff), h (bf16 M x N_ff) and one
  * decode slot (two when two_slots != 0) of the largest plane the layers' pipelines decode,
- * each part 256-byte aligned.
+ * each part 256-byte aligned. After the call g and h hold the last layer's values, and u
+ * too unless that layer's up GEMM took the SwiGLU epilogue.
  * Errors: UW_EINVAL (NULL pointers, bad pipeline, direct plane missing), UW_ESHAPE
  * (shapes differ or do not chain), UW_ENOSPACE (workspace too small), UW_EHIP.
  */

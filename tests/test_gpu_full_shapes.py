@@ -6,10 +6,11 @@
   of Y against the fp64 oracle (1e-3 * sum|x w|), and no unwritten output.
 - The whole 32-layer uw_mlp_stack_forward at M = 64 (the plans the bench measures there:
   fused gate/up, down with a K split) and at M = 1024 (every pipeline, layers cycling
-  through them): the layer run last is checked teacher-forced (its g and u against the
-  oracle on X, h within one bf16 ulp of the oracle's SwiGLU of the GPU's g and u, Y
-  against the oracle on the GPU's h), with the layer order rotated so that several
-  layers, one of each pipeline, are the last one.
+  through them; the SwiGLU in the up GEMM's epilogue): the layer run last is checked
+  teacher-forced (its g against the oracle on X, h against the SwiGLU of the GPU's g and
+  the oracle's u within the GEMM tolerance and one bf16 rounding, Y against the oracle on
+  the GPU's h), with the layer order rotated so that several layers, one of each
+  pipeline, are the last one.
 """
 import concurrent.futures as cf
 import os
@@ -129,22 +130,29 @@ class _Stack:
 
 
 def _check_last(st, last, x, y, ws, M, rng, what):
-    """Teacher-forced check of the layer run last: g, u, h are left in the workspace."""
+    """Teacher-forced check of the layer run last: g and h are left in the workspace (u
+    only where the up GEMM ran without the SwiGLU epilogue, so it is not read here)."""
     torch = torch_cuda()
     F, K = st.h[(0, 0)].N, st.h[(0, 0)].K
     a256 = lambda v: (v + 255) // 256 * 256
     g = ws[: 4 * M * F].view(torch.float32).reshape(M, F)
-    u = ws[a256(4 * M * F): a256(4 * M * F) + 4 * M * F].view(torch.float32).reshape(M, F)
     ho = 2 * a256(4 * M * F)
     hg = ws[ho: ho + 2 * M * F].view(torch.int16).reshape(M, F)
     mi, fi = rng.integers(0, M, 4096), rng.integers(0, F, 4096)
-    for name, got, q in (("gate", g, 0), ("up", u, 1)):
-        yr, ar = oracle.gemm_pairs(x, _weight(last, name), mi, fi)
-        check_gemm(_sample(got, mi, fi), yr, ar, f"{what}: layer {last} {name}")
-    gs, us = _sample(g, mi, fi), _sample(u, mi, fi)
+    yr, ar = oracle.gemm_pairs(x, _weight(last, "gate"), mi, fi)
+    gs = _sample(g, mi, fi)
+    check_gemm(gs, yr, ar, f"{what}: layer {last} gate")
+    # h = bf16(silu(g) u) with the GPU's g and u within 1e-3 sum|x w| of the oracle's u:
+    # |h - silu(g) u_oracle| <= |silu(g)| 1e-3 sum|x w| + the bf16 rounding of h (2^-8 |h|,
+    # which also covers the fp32 arithmetic of silu)
+    ur, ua = oracle.gemm_pairs(x, _weight(last, "up"), mi, fi)
     hs = _sample(hg, mi, fi).view(np.uint16)
-    href = oracle.swiglu(gs, us)
-    assert (np.abs(hs.astype(np.int32) - href.astype(np.int32)) <= 1).all(), f"{what}: layer {last} SwiGLU"
+    hv = (hs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g64 = gs.astype(np.float64)
+    sg = g64 / (1.0 + np.exp(-g64))
+    err = np.abs(hv - sg * ur)
+    bound = np.abs(sg) * 1e-3 * ua + 2.0 ** -8 * np.abs(hv) + 1e-30
+    assert (err <= bound).all(), f"{what}: layer {last} up + SwiGLU, worst {float(np.max(err - bound))}"
     hh = host(hg).view(np.uint16)
     ni = rng.integers(0, K, 4096)
     yr, ar = oracle.gemm_pairs(hh, _weight(last, "down"), mi, ni)

@@ -670,6 +670,73 @@ def test_mlp_stack_forward_one_and_two_streams():
     check_gemm(y, yr, ar, "stack last layer down")
 
 
+def test_stack_up_gemm_swiglu_epilogue_matches_two_steps():
+    """Past M = 64 the stack forward runs the SwiGLU in the up projection's GEMM epilogue
+    (tiled, wide and dma variants, one K slice; u is never stored): g, h and Y equal, bit for
+    bit, the up GEMM into u followed by uw_swiglu and then down, on one stream and with a
+    decode stream. An up projection cut into two K slices takes the two steps. Ragged M
+    and N_ff (130 rows, 576 = 2 x 256 + 64 columns), and h checked against the oracle's
+    SwiGLU of the two-step g and u."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(97)
+    K, F, M = 256, 576, 130
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    d_x = dev(x)
+    mats = [Mat(synth.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * 0.05), 256)
+            for shape in ((F, K), (F, K), (K, F))]
+    planes = [m.decode("direct")[0] for m in mats]
+    names = [uw.variant_name(v) for v in range(uw.variant_count())]
+    vdown = names.index("tiled 128x128")
+    side = torch.cuda.Stream()
+    for pipe, vname, up_split in ((uw.PIPE_DIRECT, "tiled 128x128", 1), (uw.PIPE_DIRECT, "tiled 256x128", 1),
+                                  (uw.PIPE_DIRECT, "wide 256x256", 1), (uw.PIPE_EXP, "tiled 128x64", 1),
+                                  (uw.PIPE_TRANSCODE, "wide 256x256", 1), (uw.PIPE_FULL, "dma 256x256", 1),
+                                  (uw.PIPE_EXPAND, "dma 256x128 s3", 1), (uw.PIPE_DIRECT, "wide 256x256", 2)):
+        v = names.index(vname)
+        what = f"{uw.PIPELINE_NAMES[pipe]} / {vname} / up split {up_split}"
+        log(f"  up GEMM + SwiGLU: {what}")
+        d = lambda q: planes[q] if pipe in (uw.PIPE_DIRECT, uw.PIPE_EXPAND) else None
+        # two steps: gate, up into u, uw_swiglu, down
+        nws = max(uw.workspace_bytes(m.h, pipe) for m in mats[:2])
+        wsr = empty_u8(max(nws, 256))
+        g_ref, u_ref, y_ref = empty_f32(M, F), empty_f32(M, F), empty_f32(M, K)
+        h_ref = empty_u16(M * F)
+        for q, out, ks in ((0, g_ref, 1), (1, u_ref, up_split)):
+            uw.run_pipeline(pipe, mats[q].h, mats[q].d_blob, d_x, out, M, d_direct=d(q), d_ws=wsr, ws_bytes=nws,
+                            variant=v, split_k=ks)
+        uw.swiglu(g_ref, u_ref, h_ref, M * F)
+        uw.run_pipeline(uw.PIPE_DIRECT, mats[2].h, mats[2].d_blob, h_ref, y_ref, M, d_direct=planes[2],
+                        variant=vdown, split_k=1)
+        _sync()
+        gr, ur, hr, yr = host(g_ref), host(u_ref), host(h_ref, np.uint16).reshape(M, F), host(y_ref)
+        assert (np.abs(hr.astype(np.int32) - oracle.swiglu(gr, ur).reshape(M, F).astype(np.int32)) <= 1).all(), what
+        arr = uw.mlp_layers([(uw.proj(mats[0].h, mats[0].d_blob, pipe, d_direct=d(0), variant=v, split_k=1),
+                              uw.proj(mats[1].h, mats[1].d_blob, pipe, d_direct=d(1), variant=v, split_k=up_split),
+                              uw.proj(mats[2].h, mats[2].d_blob, uw.PIPE_DIRECT, d_direct=planes[2], variant=vdown,
+                                      split_k=1))])
+        for two in (False, True):
+            nb = uw.mlp_stack_workspace(arr, M, two_slots=two)
+            ws = empty_u8(nb)
+            ws.fill_(0xFF)
+            y = empty_f32(M, K)
+            y.fill_(float("nan"))
+            uw.mlp_stack_forward(arr, M, d_x, y, ws, nb, decode_stream=side if two else None)
+            _sync()
+            wsb = host(ws)
+            a256 = lambda n: (n + 255) // 256 * 256
+            g = wsb[: 4 * M * F].view(np.float32).reshape(M, F)
+            u = wsb[a256(4 * M * F): a256(4 * M * F) + 4 * M * F].view(np.float32).reshape(M, F)
+            ho = 2 * a256(4 * M * F)
+            hg = wsb[ho: ho + 2 * M * F].view(np.uint16).reshape(M, F)
+            assert np.array_equal(g, gr), f"{what}, decode stream {two}: g"
+            assert np.array_equal(hg, hr), f"{what}, decode stream {two}: h"
+            assert np.array_equal(host(y), yr), f"{what}, decode stream {two}: Y"
+            if up_split == 1:
+                assert np.isnan(u).all(), f"{what}: u was stored although the epilogue took the SwiGLU"
+            else:
+                assert np.array_equal(u, ur), f"{what}: u of the two-step path"
+
+
 def _hard_easy_stack(rng, K, F, hard_pipes):
     """A stack whose layers alternate easy (three projections with direct planes, run on
     them) and hard (Huffman blobs only; decode-first pipelines from hard_pipes in turn).
