@@ -1774,6 +1774,34 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
+// The 256 x 256 DMA GEMM in whole rounds of the CUs. When its tiles leave a last round that
+// only part of the CUs would run (the gate shape at M = 4096: 896 tiles = 3.5 rounds of 256),
+// the column blocks of that round go to a second launch of the 256 x 128 kernel, whose
+// half-height tiles finish a round in a little over half the time. Both launches sum every
+// output over K in the same order, so Y is the same as from one launch.
+hipError_t launch_dma_rounds(const GemmArgs& g, hipStream_t s)
+{
+    const int64_t tn = (g.N + 255) / 256, tm = (g.M + 255) / 256, cus = cu_count();
+    if (g.kgroups == 0 && tn * tm > cus && (tn * tm) % cus != 0) {
+        int64_t nm = tn * tm / cus * cus / tm;  // column blocks of the first launch: whole rounds
+        while (nm > 0 && (nm * tm) % cus != 0) nm--;
+        const int64_t n0 = nm * 256;
+        if (nm > 0 && n0 < g.N && (tn - nm) * ((g.M + 127) / 128) <= cus) {
+            GemmArgs a = g;
+            a.N = n0;
+            hipError_t e = launch_dma<256, 2>(a, s);
+            if (e != hipSuccess) return e;
+            GemmArgs b = g;
+            b.N = g.N - n0;
+            b.wplane = static_cast<const uint8_t*>(g.wplane) + 2 * n0 * g.K;
+            b.y = g.y + n0;
+            b.hout = g.hout ? g.hout + n0 : nullptr;
+            return launch_dma<128, 3>(b, s);
+        }
+    }
+    return launch_dma<256, 2>(g, s);
+}
+
 template <int SRC, bool CONTIG>
 hipError_t launch_wide_t(const GemmArgs& g, hipStream_t s)
 {
@@ -1825,7 +1853,7 @@ hipError_t launch_src(const GemmArgs& g, const Variant& v, hipStream_t s)
 {
     if (v.kind == 2) return launch_wide_t<SRC, CONTIG>(g, s);
     if (v.kind == 3) {
-        if constexpr (SRC == UW_W_BF16) return v.bm == 128 ? launch_dma<128, 3>(g, s) : launch_dma<256, 2>(g, s);
+        if constexpr (SRC == UW_W_BF16) return v.bm == 128 ? launch_dma<128, 3>(g, s) : launch_dma_rounds(g, s);
         return hipErrorNotSupported;  // (rejected before: bf16 weights only)
     }
     // (a "ks" variant is its neighbour's kernel with a K split chosen for it; the split is

@@ -10,7 +10,8 @@
   teacher-forced (its g against the oracle on X, h against the SwiGLU of the GPU's g and
   the oracle's u within the GEMM tolerance and one bf16 rounding, Y against the oracle on
   the GPU's h), with the layer order rotated so that several layers, one of each
-  pipeline, are the last one.
+  pipeline, are the last one; and one layer at M = 4096 on expand + the 256x256 DMA GEMM
+  (three whole rounds of the CUs and a 256x128 tail per launch).
 """
 import concurrent.futures as cf
 import os
@@ -93,6 +94,20 @@ def test_stack_shapes_large_m_every_loader_variant_and_split(role):
                     uw.recon_gemm(h, d_blob, src, plane, d_x, y, M, variant=v, split_k=ks)
                     check_gemm(_sample(y, mi, ni), y_ref, a_ref, what)
                     assert _all_finite(y), f"{what}: unwritten outputs"
+        if role == "gate" and M == 4096:
+            # 896 tiles of 256 x 256 are 3.5 rounds of 256 CUs: the DMA launch runs three whole
+            # rounds and its last column blocks as 256 x 128 tiles. Every output is summed over K
+            # in the same order as by the 256 x 128 variant alone, so the two agree bit for bit.
+            names = [uw.variant_name(v) for v in range(uw.variant_count())]
+            y2 = empty_f32(M, N)
+            y2.fill_(float("nan"))
+            y.fill_(float("nan"))
+            uw.recon_gemm(h, d_blob, uw.W_BF16, planes[uw.W_BF16], d_x, y, M, variant=names.index("dma 256x256"),
+                          split_k=1)
+            uw.recon_gemm(h, d_blob, uw.W_BF16, planes[uw.W_BF16], d_x, y2, M,
+                          variant=names.index("dma 256x128 s3"), split_k=1)
+            assert torch_cuda().equal(y, y2), "dma 256x256 in whole rounds differs from dma 256x128 s3"
+            del y2
         del d_x, y
 
 
@@ -165,7 +180,7 @@ def test_stack_32_layers_forward_teacher_forced():
     L = CFG.layers
     rng = np.random.default_rng(7)
     torch = torch_cuda()
-    xs = synth.gen_x(CFG, 1024, st.h[(0, 0)].K)
+    xs = synth.gen_x(CFG, 4096, st.h[(0, 0)].K)
     # M = 64: the plans the bench measures there (fused gate/up; down with four K slices)
     xt, ks4 = _variant("skinny rt4 u2 w4 xt"), _variant("skinny rt4 u2 w4 xt ks")
     plan64 = lambda l, q: (uw.PIPE_DIRECT, ks4, 4) if q == 2 else (uw.PIPE_DIRECT, xt, 0)
@@ -180,12 +195,17 @@ def test_stack_32_layers_forward_teacher_forced():
             return p, wide, 4 if q == 2 else 1
         return p, -1, 0
 
-    for M, plan_of, lasts in ((64, plan64, (L - 1, 0, 13)), (1024, plan1024, (L - 1, 0, 1, 2, 3, 4))):
+    # M = 4096, one layer: expand + the 256 x 256 DMA GEMM (gate and up: three whole rounds of
+    # 256 CUs and a 256 x 128 tail, the SwiGLU in up's epilogue through both launches)
+    dma = _variant("dma 256x256")
+    plan4096 = lambda l, q: (uw.PIPE_EXPAND, dma, 1)
+    for M, plan_of, lasts in ((64, plan64, (L - 1, 0, 13)), (1024, plan1024, (L - 1, 0, 1, 2, 3, 4)),
+                              (4096, plan4096, (5,))):
         x = xs[:M]
         d_x = dev(x)
         y = empty_f32(M, st.h[(0, 2)].N)
         for last in lasts:
-            order = [l for l in range(L) if l != last] + [last]
+            order = [l for l in range(L) if l != last] + [last] if M < 4096 else [last]
             arr = st.arr(order, plan_of)
             nb = uw.mlp_stack_workspace(arr, M)
             ws = empty_u8(nb)
