@@ -252,8 +252,9 @@ def tune_plans(uw, synth, torch, dev, stack, Ms, log):
     pipeline, variant and K split; up runs on gate's plan (same shape and statistics). For
     M <= 64 the stack forward runs gate, up and the SwiGLU as one launch, so gate's plan is
     that launch's: direct planes, the variant under which the fused launch itself runs
-    fastest (one K slice)."""
-    plans = {}
+    fastest (one K slice). Past M = 64, where a pick runs with preprocessing (expand,
+    decode), the best plan without it is tuned too and the stack forward chooses."""
+    plans, alts = {}, {}
     stream = torch.cuda.current_stream()
     for M in Ms:
         plans[M] = {}
@@ -276,8 +277,55 @@ def tune_plans(uw, synth, torch, dev, stack, Ms, log):
             plans[M][role] = {"pipeline": pl.pipeline, "variant": pl.variant, "split_k": pl.split_k, "t_ms": pl.t_ms}
             log(f"[bench] plan M={M} {role}: {uw.PIPELINE_NAMES[pl.pipeline]} / {uw.variant_name(pl.variant)} / "
                 f"split {pl.split_k}: {pl.t_ms * 1e3:.1f} us ({time.time() - t0:.1f}s)")
+            if M > 64 and pl.pipeline != uw.PIPE_DIRECT:
+                # the best plan without preprocessing too: launch by launch the two can be within
+                # noise of each other while the forward, where each expand precedes its GEMM,
+                # is not; the forward decides between them below
+                pd = uw.autotune(h0, stack.blob[0][q], x, y, [M], d_ws=ws, ws_bytes=ws.numel(), reps=reps, warmup=1,
+                                 trials=trials, rot=stack.rot(uw, q), pipeline_mask=1 << uw.PIPE_DIRECT)[0]
+                alts.setdefault(M, {})[role] = {"pipeline": pd.pipeline, "variant": pd.variant, "split_k": pd.split_k,
+                                                "t_ms": pd.t_ms}
             del x, y, ws
+        if M in alts:
+            plans[M] = fastest_forward(uw, synth, torch, dev, stack, M, plans[M], alts[M], log)
     return plans
+
+
+def fastest_forward(uw, synth, torch, dev, stack, M, best, alts, log):
+    """Among the per-launch picks and the same with any role on its best plan without
+    preprocessing, the plans whose whole stack forward at M (one stream) is fastest."""
+    cands = [best]
+    for roles in (("gate",), ("down",), ("gate", "down")):
+        if all(r in alts for r in roles):
+            c = dict(best)
+            for r in roles:
+                c[r] = alts[r]
+            cands.append(c)
+    x = torch.from_numpy(synth.gen_x(stack.cfg, M, stack.K).view(np.int16)).to(dev)
+    y = torch.empty(M, stack.K, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    times = []
+    for c in cands:
+        arr = stack.layers(uw, c)
+        nb = uw.mlp_stack_workspace(arr, M)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(2):
+            uw.mlp_stack_forward(arr, M, x, y, ws, nb, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 2)
+        del ws
+    i = min(range(len(cands)), key=lambda k: times[k])
+    desc = lambda c: ", ".join(f"{r} {uw.PIPELINE_NAMES[c[r]['pipeline']]} / {uw.variant_name(c[r]['variant'])}"
+                               for r in ("gate", "down"))
+    log(f"[bench] plans M={M} by forward: " + "; ".join(f"{desc(c)}: {t:.3f} ms" for c, t in zip(cands, times))
+        + f" -> {desc(cands[i])}")
+    del x, y
+    return cands[i]
 
 
 def plans_to_json(uw, plans):
