@@ -404,9 +404,9 @@ uw_status decode_proj(const uw_proj& p, void* slot, void* stream)
     }
 }
 
-// The GEMM of a projection whose plane is ready (in `slot`, or the direct plane).
-uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
-                    void* stream, bool y_zeroed = false)
+// GEMM arguments of a projection whose plane is ready (in `slot`, or the direct plane).
+uw_gemm_args proj_args(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, float* y,
+                       int64_t ldy)
 {
     uw_gemm_args g;
     std::memset(&g, 0, sizeof g);
@@ -422,6 +422,14 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
     g.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
           : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
     g.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
+    return g;
+}
+
+// The GEMM of a projection whose plane is ready.
+uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
+                    void* stream, bool y_zeroed = false)
+{
+    const uw_gemm_args g = proj_args(p, slot, M, x, ldx, y, ldy);
     return launch_gemm(&g, stream, y_zeroed);
 }
 
@@ -431,20 +439,7 @@ uw_status gemm_proj(const uw_proj& p, const void* slot, int64_t M, const uint16_
 uw_status up_proj_swiglu(const uw_proj& p, const void* slot, int64_t M, const uint16_t* x, int64_t ldx, const float* g,
                          float* u, uint16_t* h, int64_t ldf, void* stream)
 {
-    uw_gemm_args a;
-    std::memset(&a, 0, sizeof a);
-    a.M = M;
-    a.d_x = x;
-    a.ldx = ldx;
-    a.h = p.h;
-    a.d_blob = p.d_blob;
-    a.d_y = const_cast<float*>(g);
-    a.ldy = ldf;
-    a.variant = p.variant;
-    a.split_k = p.split_k;
-    a.src = p.pipeline == UW_PIPE_FULL || p.pipeline == UW_PIPE_EXPAND ? UW_W_BF16 : p.pipeline == UW_PIPE_EXP ? UW_W_EXP
-          : p.pipeline == UW_PIPE_TRANSCODE ? UW_W_IDX : UW_W_DIRECT;
-    a.d_wplane = p.pipeline == UW_PIPE_DIRECT ? static_cast<const void*>(p.d_direct) : slot;
+    const uw_gemm_args a = proj_args(p, slot, M, x, ldx, const_cast<float*>(g), ldf);  // Y = g, read only
     uw_status st = launch_gemm_swiglu(&a, h, ldf, stream);
     if (st != UW_EUNSUPPORTED) return st;
     clear_error();
