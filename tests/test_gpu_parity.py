@@ -350,6 +350,39 @@ def test_gemm_parity_ragged(N, K):
                 check_gemm(_run_gemm(m, planes, src, x, v), y_ref, a_ref, f"N={N} K={K} M={M} src={src} v={v}")
 
 
+def test_dma_whole_rounds_ragged_tail():
+    """The 256x256 DMA launch in whole rounds of the CUs with a 256x128 tail launch, on ragged
+    N and M: N = 4296 (17 column blocks, the last 200 rows wide), M = 4046 (16 row blocks, the
+    last 206 rows) make 272 tiles; with 256 CUs the first 16 column blocks fill one round and
+    the last one goes out as 32 tiles of 256x128. Y matches the oracle on a sample, every
+    output is written, and the 256x128 variant alone gives the same bits."""
+    torch = torch_cuda()
+    N, K, M = 4296, 256, 4046
+    cfg = synth.Config("rounds", 11, (("w", N, K),), 0.02, "normal", 0.001, 0.0, 12, (1,))
+    w = synth.gen_weight(cfg, "w")
+    m = Mat(w, 256)
+    plane = dev(w)
+    x = synth.gen_x(cfg, M, K)
+    d_x = dev(x)
+    names = [uw.variant_name(v) for v in range(uw.variant_count())]
+    ys = []
+    for vname in ("dma 256x256", "dma 256x128 s3"):
+        y = empty_f32(M, N)
+        y.fill_(float("nan"))
+        log(f"  {vname} N={N} K={K} M={M}")
+        uw.recon_gemm(m.h, m.d_blob, uw.W_BF16, plane, d_x, y, M, variant=names.index(vname), split_k=1)
+        _sync()
+        assert bool(torch.isfinite(y).all().item()), f"{vname}: unwritten outputs"
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1]), "whole rounds + tail differ from the 256x128 variant"
+    rng = np.random.default_rng(5)
+    mi, ni = rng.integers(0, M, 4096), rng.integers(0, N, 4096)
+    mi[:8], ni[:8] = M - 1, N - 1 - np.arange(8)  # the ragged corner of the tail launch
+    yr, ar = oracle.gemm_pairs(x, w, mi, ni)
+    yg = ys[0][torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    check_gemm(yg, yr, ar, "dma whole rounds, ragged")
+
+
 def test_gemm_padded_leading_dimensions():
     """X and Y as rows of wider buffers (ldx > K, ldy > N): every loader and variant reads
     only the first K of each X row (the rest holds NaN, which would poison any output it
